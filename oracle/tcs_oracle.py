@@ -1,0 +1,465 @@
+"""Plain, slow, fp64 oracle of the trie_tree label-scoring path.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It shares
+no code with the HIP library and imports nothing from it.
+
+Sources (cited by page title and section):
+  [CT] "To Classify, Try a Trie Tree" (Quail blog): section 3.1 (the label trie,
+       root = the ANSWER: token), section 3.2 (trie_tree: label probability is the
+       product of its token probabilities; normalisation over labels; the rule for
+       a label that is a prefix of another; every node attends only to the prompt
+       and to the nodes on its own path), section 4.1 (full-vocabulary output head).
+  [EX] Quail documentation, "Execution", section "Label scoring" (worked example:
+       refund 0.8 x 0.6 = 0.48 against praise 0.3).
+  [QI] "Building an Ultra-High Throughput AI-SQL Engine", section 3.2.4 (partial
+       attention results merged by their log-sum-exp / online softmax).
+  [TA] "Trie Automata for Constrained Decoding over Large Finite Sets",
+       Proposition 1 (the trie is the minimal automaton: one state per distinct
+       prefix).
+
+Readings taken where the pages leave a step open (each is also listed with its
+reason in the design notes):
+  R1  every label is scored over its full root-to-leaf token path;
+  R2  every internal trie node (a node with children) runs the model;
+  R3  a prefix label ending at an internal node gets log(1 - sum of its children's
+      probabilities) -- the section 3.2 prefix rule generalised to several children;
+  R4  a node attends to the document keys and to its ancestors *and itself*;
+  R5  no positional encoding; one attention layer: pre-RMSNorm, GQA (query head h
+      reads KV head h // (Hq/Hkv)), scale 1/sqrt(hd), output projection, residual,
+      final RMSNorm (gain 1, eps 1e-6), then the LM head;
+  R6  bf16 workloads round to bf16 (nearest-even) exactly where a bf16 tensor is
+      stored: the normalised node input a, the node q/k/v, the attention output O
+      and the final hidden state h.  The residual sum y is not rounded;
+  R7  the fp8 head holds E4M3FN codes with one fp32 scale per vocabulary row; the
+      scale multiplies the dot product;
+  R8  argmax ties go to the lowest label id.
+
+Parity status: every function below is pinned by the non-GPU oracle tests
+(library routines, closed forms, the worked example, brute-force scoring).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "TCS_OK", "TCS_EINVAL", "TCS_EDUPLICATE", "TrieError", "Trie", "build_trie",
+    "round_bf16", "decode_bf16", "decode_e4m3", "rmsnorm", "OracleModel",
+    "node_layer", "doc_kv_from_tokens", "tree_attention", "hidden_states",
+    "lm_head_lse", "head_logits_at", "edge_logprobs", "log1mexp", "path_log_likelihoods",
+    "label_softmax", "classify", "bruteforce_ll",
+]
+
+TCS_OK = 0
+TCS_EINVAL = -1
+TCS_EDUPLICATE = -2
+
+
+class TrieError(ValueError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+# =========================================================================== trie ([CT] 3.1)
+
+@dataclass
+class Trie:
+    n_nodes: int
+    n_int: int
+    n_labels: int
+    max_depth: int
+    parent: np.ndarray        # [N]   parent node id, -1 at the root
+    token: np.ndarray         # [N]   token id of the node (root: root_token)
+    depth: np.ndarray         # [N]
+    child_begin: np.ndarray   # [N]   first child id, 0 when the node has no child
+    child_count: np.ndarray   # [N]
+    node_label: np.ndarray    # [N]   label ending at the node, -1 if none
+    label_node: np.ndarray    # [M]
+    qrow: np.ndarray          # [N]   query row of an internal node, -1 for a leaf
+    qnode: np.ndarray         # [N_int] node id of each query row
+    qparent: np.ndarray       # [N_int] query row of the parent, -1 for the root
+    level_offsets: np.ndarray  # [max_depth + 2]
+    e_tok: np.ndarray         # [N-1] edges sorted by (token, parent query row)
+    e_qrow: np.ndarray        # [N-1]
+    e_child: np.ndarray       # [N-1]
+
+
+def build_trie(labels, root_token: int, V: int) -> Trie:
+    """Token trie of the labels ([CT] 3.1): each label is a root-to-node path.
+
+    Insert the labels in input order into a dict of children, then number the
+    nodes breadth-first with each node's children visited in ascending token id.
+    That numbering is the rank of (depth, token path compared lexicographically).
+    """
+    M = len(labels)
+    if M < 1:
+        raise TrieError(TCS_EINVAL, "need at least one label")
+    if not (0 <= root_token < V):
+        raise TrieError(TCS_EINVAL, "root token out of range")
+    root = {"children": {}, "label": -1}
+    for m, lab in enumerate(labels):
+        if len(lab) == 0:
+            raise TrieError(TCS_EINVAL, f"label {m} is empty")
+        node = root
+        for t in lab:
+            t = int(t)
+            if not (0 <= t < V):
+                raise TrieError(TCS_EINVAL, f"label {m} has token {t} outside [0, {V})")
+            node = node["children"].setdefault(t, {"children": {}, "label": -1})
+        if node["label"] >= 0:
+            raise TrieError(TCS_EDUPLICATE, f"label {m} duplicates label {node['label']}")
+        node["label"] = m
+
+    # breadth-first numbering, children in ascending token order
+    order = [(root, -1, int(root_token), 0)]
+    head = 0
+    while head < len(order):
+        node, _, _, dep = order[head]
+        for t in sorted(node["children"]):
+            order.append((node["children"][t], head, t, dep + 1))
+        head += 1
+    N = len(order)
+    parent = np.array([p for (_, p, _, _) in order], dtype=np.int32)
+    token = np.array([t for (_, _, t, _) in order], dtype=np.int32)
+    depth = np.array([d for (_, _, _, d) in order], dtype=np.int32)
+    child_count = np.array([len(n["children"]) for (n, _, _, _) in order], dtype=np.int32)
+    child_begin = np.zeros(N, dtype=np.int32)
+    for u in range(N - 1, 0, -1):      # smallest child id of each parent
+        child_begin[parent[u]] = u
+    node_label = np.array([n["label"] for (n, _, _, _) in order], dtype=np.int32)
+    label_node = np.full(M, -1, dtype=np.int32)
+    for u in range(N):
+        if node_label[u] >= 0:
+            label_node[node_label[u]] = u
+    internal = child_count > 0
+    qnode = np.nonzero(internal)[0].astype(np.int32)
+    qrow = np.full(N, -1, dtype=np.int32)
+    qrow[qnode] = np.arange(len(qnode), dtype=np.int32)
+    qparent = np.array([qrow[parent[u]] if u > 0 else -1 for u in qnode], dtype=np.int32)
+    D = int(depth.max())
+    level_offsets = np.searchsorted(depth, np.arange(D + 2), side="left").astype(np.int32)
+    children = np.arange(1, N)
+    e_q = qrow[parent[children]]
+    e_t = token[children]
+    perm = np.lexsort((e_q, e_t))
+    return Trie(
+        n_nodes=N, n_int=len(qnode), n_labels=M, max_depth=D, parent=parent, token=token,
+        depth=depth, child_begin=child_begin, child_count=child_count, node_label=node_label,
+        label_node=label_node, qrow=qrow, qnode=qnode, qparent=qparent,
+        level_offsets=level_offsets, e_tok=e_t[perm].astype(np.int32),
+        e_qrow=e_q[perm].astype(np.int32), e_child=children[perm].astype(np.int32))
+
+
+def _path_rows(trie: Trie, r: int):
+    """Query rows from the root down to row r (ancestors and r itself)."""
+    rows = []
+    while r >= 0:
+        rows.append(r)
+        r = int(trie.qparent[r])
+    return rows[::-1]
+
+
+def _path_nodes(trie: Trie, u: int):
+    """Node ids from the root's first child down to node u (root excluded)."""
+    nodes = []
+    while u > 0:
+        nodes.append(u)
+        u = int(trie.parent[u])
+    return nodes[::-1]
+
+
+# =========================================================================== number formats
+
+def round_bf16(x):
+    """Round fp64 values to the nearest bf16 value (ties to even), returned as fp64.
+
+    bf16 keeps 8 significant bits and fp32's exponent range; below 2^-126 the
+    quantum is fixed at 2^-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, -133)
+    r = np.ldexp(np.round(np.ldexp(x, -q)), q)
+    return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x), r)
+
+
+def decode_bf16(bits):
+    """bf16 bit patterns (uint16) -> fp64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3(codes):
+    """OCP E4M3FN bytes -> fp64: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+
+    Exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def rmsnorm(x, eps: float = 1e-6):
+    """x / sqrt(mean(x^2) + eps) over the last axis, gain 1 (reading R5)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+# =========================================================================== model
+
+class OracleModel:
+    """fp64 copies of the stored weights plus the rounding rule of the workload."""
+
+    def __init__(self, inp: dict):
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.bf16 = cfg.dtype == "bf16"
+        dec = decode_bf16 if self.bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+        self.E = dec(inp["E"])
+        self.Wq = dec(inp["Wq"])
+        self.Wk = dec(inp["Wk"])
+        self.Wv = dec(inp["Wv"])
+        self.Wo = dec(inp["Wo"])
+        if cfg.head == "fp8":
+            self.W = decode_e4m3(inp["W"])
+            self.W_scale = np.asarray(inp["W_scale"], dtype=np.float64)
+        else:
+            self.W = dec(inp["W"])
+            self.W_scale = None
+        self.Hq, self.Hkv, self.hd = cfg.Hq, cfg.Hkv, cfg.hd
+        self.scale = 1.0 / np.sqrt(cfg.hd)
+
+    def rnd(self, x):
+        return round_bf16(x) if self.bf16 else np.asarray(x, dtype=np.float64)
+
+
+def node_layer(model: OracleModel, tokens):
+    """Input block for a set of tokens (R5, R6).
+
+    x = E[token]; a = RMSNorm(x) (stored: rounded); q, k, v = a Wq^T, a Wk^T, a Wv^T
+    (stored: rounded).  Returns x [n, d], q [n, Hq, hd], k, v [n, Hkv, hd].
+    """
+    x = model.E[np.asarray(tokens)]
+    a = model.rnd(rmsnorm(x))
+    n = x.shape[0]
+    q = model.rnd(a @ model.Wq.T).reshape(n, model.Hq, model.hd)
+    k = model.rnd(a @ model.Wk.T).reshape(n, model.Hkv, model.hd)
+    v = model.rnd(a @ model.Wv.T).reshape(n, model.Hkv, model.hd)
+    return x, q, k, v
+
+
+def doc_kv_from_tokens(model: OracleModel, doc_tokens):
+    """Document keys/values of a token-id document: the node_layer k and v of each token."""
+    _, _, k, v = node_layer(model, doc_tokens)
+    return k, v
+
+
+def tree_attention(qn, kn, vn, trie: Trie, Kd, Vd, doc_offsets, scale, docs=None, rows=None):
+    """Ancestor-masked tree attention ([CT] 3.2 custom attention kernel; R4, R5).
+
+    For document b, query row r (an internal node u) and query head h, the keys are
+    the document's keys K_d[b, 0..L_b-1] followed by the keys of the nodes on the
+    root-to-u path (u included); scores q.k * scale, softmax, weighted sum of values.
+    Returns O[len(docs), len(rows), Hq, hd] in fp64 (unrounded).
+    """
+    Hq, Hkv = qn.shape[1], kn.shape[1]
+    group = Hq // Hkv
+    kv_of_head = np.arange(Hq) // group
+    docs = range(len(doc_offsets) - 1) if docs is None else docs
+    rows = range(trie.n_int) if rows is None else rows
+    out = np.zeros((len(docs), len(rows), Hq, qn.shape[2]))
+    for bi, b in enumerate(docs):
+        Kb = np.asarray(Kd[doc_offsets[b]:doc_offsets[b + 1]], dtype=np.float64)
+        Vb = np.asarray(Vd[doc_offsets[b]:doc_offsets[b + 1]], dtype=np.float64)
+        for ri, r in enumerate(rows):
+            path = _path_rows(trie, r)
+            keys = np.concatenate([Kb, kn[path]], axis=0)[:, kv_of_head, :]   # [nk, Hq, hd]
+            vals = np.concatenate([Vb, vn[path]], axis=0)[:, kv_of_head, :]
+            s = np.einsum("hd,khd->hk", qn[r], keys) * scale
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            out[bi, ri] = np.einsum("hk,khd->hd", p, vals)
+    return out
+
+
+def hidden_states(model: OracleModel, x_nodes, O):
+    """y = x + concat_h(O_h) Wo^T (not rounded); h = RMSNorm(y) (stored: rounded).
+
+    O: [..., Hq, hd] already rounded to its storage type; x_nodes broadcasts over
+    the leading document axis.
+    """
+    Of = O.reshape(O.shape[:-2] + (-1,))
+    y = x_nodes + Of @ model.Wo.T
+    return model.rnd(rmsnorm(y))
+
+
+def head_logits_at(model: OracleModel, h, cols=None):
+    """Logits h W^T for all vocabulary rows (or the listed ones); fp8 heads scale
+    each dot product by the row's scale (R7)."""
+    W = model.W if cols is None else model.W[cols]
+    z = h @ W.T
+    if model.W_scale is not None:
+        z = z * (model.W_scale if cols is None else model.W_scale[cols])
+    return z
+
+
+def lm_head_lse(model: OracleModel, h, chunk: int = 512):
+    """Full-vocabulary log-sum-exp per hidden state ([CT] 4.1: all vocab rows are
+    needed to turn scores into probabilities).  h: [R, d] -> lse [R]."""
+    h = np.asarray(h, dtype=np.float64)
+    lse = np.empty(h.shape[0])
+    for r0 in range(0, h.shape[0], chunk):
+        z = head_logits_at(model, h[r0:r0 + chunk])
+        m = z.max(axis=1)
+        lse[r0:r0 + chunk] = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return lse
+
+
+def edge_logprobs(model: OracleModel, trie: Trie, h, lse):
+    """Token log-probability of every trie edge, per document.
+
+    h: [B, N_int, d], lse: [B, N_int].  For the edge parent(c) -> c,
+    lp[b, c] = logit[b, qrow(parent c), token c] - lse[b, qrow(parent c)];
+    lp[b, root] = 0.  Returns lp [B, N].
+    """
+    B = h.shape[0]
+    lp = np.zeros((B, trie.n_nodes))
+    for c in range(1, trie.n_nodes):
+        r = trie.qrow[trie.parent[c]]
+        z = head_logits_at(model, h[:, r, :], cols=[trie.token[c]])[:, 0]
+        lp[:, c] = z - lse[:, r]
+    return lp
+
+
+def log1mexp(x):
+    """log(1 - e^x) for x <= 0, split at -ln 2 (Maechler's log1mexp); -inf for x >= 0."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out = np.where(x > -np.log(2.0), np.log(-np.expm1(np.minimum(x, 0.0))),
+                       np.log1p(-np.exp(np.minimum(x, 0.0))))
+    return np.where(x >= 0.0, -np.inf, out)
+
+
+def path_log_likelihoods(trie: Trie, lp):
+    """Per-label log score ([CT] 3.2; R1, R3).
+
+    LL[b, m] = sum of lp over the path root -> label_node[m]; a label ending at an
+    internal node adds log(1 - sum_{children c} e^{lp[b, c]}) -- the probability
+    of not continuing with any child.  lp: [B, N] -> LL [B, M].
+    """
+    lp = np.asarray(lp, dtype=np.float64)
+    B = lp.shape[0]
+    LL = np.zeros((B, trie.n_labels))
+    for m in range(trie.n_labels):
+        u = int(trie.label_node[m])
+        LL[:, m] = lp[:, _path_nodes(trie, u)].sum(axis=1)
+        if trie.child_count[u] > 0:
+            cs = np.arange(trie.child_begin[u], trie.child_begin[u] + trie.child_count[u])
+            z = lp[:, cs]
+            mx = z.max(axis=1)
+            lse_c = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
+            LL[:, m] += log1mexp(lse_c)
+    return LL
+
+
+def label_softmax(LL):
+    """P(m) = score(m) / sum of scores ([CT] 3.2 normalisation), computed as a
+    softmax of the log scores; label = argmax, lowest id on ties (R8)."""
+    LL = np.asarray(LL, dtype=np.float64)
+    mx = LL.max(axis=1, keepdims=True)
+    e = np.exp(LL - mx)
+    P = e / e.sum(axis=1, keepdims=True)
+    return P, np.argmax(LL, axis=1).astype(np.int32)
+
+
+# =========================================================================== whole path
+
+def classify(inp: dict, docs=None, model: OracleModel | None = None, trie: Trie | None = None):
+    """The whole trie_tree pass for the listed documents (all by default).
+
+    Returns a dict with trie, node q/k/v, O (rounded), h, lse, lp, ll, prob, label.
+    """
+    model = model or OracleModel(inp)
+    trie = trie or build_trie(inp["labels"], inp["root_token"], inp["cfg"].V)
+    offs = inp["doc_offsets"]
+    docs = list(range(len(offs) - 1)) if docs is None else list(docs)
+    x, qn, kn, vn = node_layer(model, trie.token[trie.qnode])
+    if inp["cfg"].doc_mode == "tokens":
+        Kd, Vd = doc_kv_from_tokens(model, inp["doc_tokens"])
+    else:
+        dec = decode_bf16 if model.bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+        Kd, Vd = dec(inp["Kd"]), dec(inp["Vd"])
+    O = model.rnd(tree_attention(qn, kn, vn, trie, Kd, Vd, offs, model.scale, docs=docs))
+    h = hidden_states(model, x[None], O)
+    B, n_int, d = h.shape
+    lse = lm_head_lse(model, h.reshape(-1, d)).reshape(B, n_int)
+    lp = edge_logprobs(model, trie, h, lse)
+    ll = path_log_likelihoods(trie, lp)
+    prob, label = label_softmax(ll)
+    return dict(trie=trie, x=x, qn=qn, kn=kn, vn=vn, Kd=Kd, Vd=Vd, O=O, h=h, lse=lse, lp=lp,
+                ll=ll, prob=prob, label=label, docs=docs)
+
+
+def bruteforce_ll(inp: dict, doc: int, label_ids=None, model: OracleModel | None = None):
+    """Score labels one at a time by running the whole sequence causally.
+
+    The direct definition of [CT] 3.2: P(m) = prod_k P(x_k | prompt, x_<k).  For
+    label m with tokens t_1..t_k the sequence is [root, t_1, ..., t_k]; position j
+    attends to every document key and to sequence positions 0..j (a causal mask);
+    log P(t_{j+1}) = logit_j[t_{j+1}] - logsumexp(logit_j).  When other labels
+    continue label m, the log-probability of not taking any of their next tokens
+    is added ([CT] 3.2 prefix rule).  No trie is built.
+    """
+    model = model or OracleModel(inp)
+    labels = [list(map(int, l)) for l in inp["labels"]]
+    root = int(inp["root_token"])
+    offs = inp["doc_offsets"]
+    if inp["cfg"].doc_mode == "tokens":
+        Kb, Vb = doc_kv_from_tokens(model, inp["doc_tokens"][offs[doc]:offs[doc + 1]])
+    else:
+        dec = decode_bf16 if model.bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+        Kb = dec(inp["Kd"][offs[doc]:offs[doc + 1]])
+        Vb = dec(inp["Vd"][offs[doc]:offs[doc + 1]])
+    L = Kb.shape[0]
+    group = model.Hq // model.Hkv
+    label_ids = range(len(labels)) if label_ids is None else label_ids
+    out = []
+    for m in label_ids:
+        seq = [root] + labels[m]
+        n = len(seq)
+        x, q, k, v = node_layer(model, seq)
+        keys = np.concatenate([Kb, k], axis=0)            # [L + n, Hkv, hd]
+        vals = np.concatenate([Vb, v], axis=0)
+        allowed = np.zeros((n, L + n), dtype=bool)
+        allowed[:, :L] = True
+        for j in range(n):
+            allowed[j, L:L + j + 1] = True
+        O = np.zeros((n, model.Hq, model.hd))
+        for h in range(model.Hq):
+            g = h // group
+            s = (q[:, h, :] @ keys[:, g, :].T) * model.scale
+            s = np.where(allowed, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            O[:, h, :] = p @ vals[:, g, :]
+        hid = model.rnd(rmsnorm(x + model.rnd(O).reshape(n, -1) @ model.Wo.T))
+        z = head_logits_at(model, hid)
+        mx = z.max(axis=1)
+        lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
+        ll = sum(z[j, seq[j + 1]] - lse[j] for j in range(n - 1))
+        cont = sorted({l[len(labels[m])] for l in labels
+                       if len(l) > len(labels[m]) and l[:len(labels[m])] == labels[m]})
+        if cont:
+            pstop = 1.0 - np.exp(z[n - 1, cont] - lse[n - 1]).sum()
+            ll += np.log(pstop) if pstop > 0 else -np.inf
+        out.append(ll)
+    return np.array(out)
