@@ -1,0 +1,258 @@
+/*
+ * tcs.h -- C ABI of libtcs, the gfx950 (MI355X) trie_tree label scorer.
+ *
+ * The library scores every label of a token trie for a batch of documents in one
+ * pass, the trie_tree method of "To Classify, Try a Trie Tree" (Quail blog),
+ * section 3.2:
+ *   - every internal trie node is one answer position; its query attends to the
+ *     document's keys/values and to the nodes on its own root-to-node path
+ *     (section 3.2, "Custom attention kernel");
+ *   - the node's hidden state goes through the full-vocabulary output head, whose
+ *     log-sum-exp turns each child edge's logit into a token log-probability
+ *     (section 4.1: probabilities need every vocabulary row);
+ *   - a label's log score is the sum of the token log-probs on its path; a label
+ *     that ends where other labels continue also gets log(1 - P(continue))
+ *     (section 3.2, prefix rule); scores are normalised over the labels and the
+ *     best label is returned (section 3.2 normalisation, section 2: AI.CLASSIFY
+ *     always returns one of the labels; probabilities sum to 1).
+ *
+ * Conventions for every entry point:
+ *   - Ownership: all buffers belong to the caller.  Device entry points take
+ *     device pointers, enqueue work on `stream` and return without waiting; the
+ *     library never allocates, frees or retains memory.  Scratch memory comes in
+ *     through a caller-sized workspace (see the *_workspace_bytes functions).
+ *   - Layouts are row-major and densely packed unless a stride is given.
+ *     bf16 tensors are 16-bit bfloat16 bit patterns; fp8 tensors are OCP E4M3FN
+ *     bytes.  Weight matrices use the [out_features, in_features] layout, so every
+ *     projection is y = x W^T.
+ *   - Status: 0 on success or a negative TCS_E* code; tcs_last_error() then
+ *     returns a message for the calling thread.  Device-side faults surface when
+ *     the caller synchronises the stream.  Outputs are undefined after an error.
+ *   - The library runs on gfx950 only.
+ */
+#ifndef TCS_H_
+#define TCS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TCS_OK            0
+#define TCS_EINVAL       -1  /* null pointer, bad dimension, token outside [0,V), empty label, M < 1 */
+#define TCS_EDUPLICATE   -2  /* two labels with the same token sequence */
+#define TCS_ECAPACITY    -3  /* output arrays too small; the required sizes are reported */
+#define TCS_EUNSUPPORTED -4  /* head_dim, width or dtype combination this build does not run */
+#define TCS_EHIP         -5  /* a HIP launch or runtime call failed (message has the HIP string) */
+#define TCS_ENOTIMPL     -6
+
+typedef enum {
+  TCS_F32 = 0,       /* IEEE fp32 */
+  TCS_BF16 = 1,      /* bfloat16 bit patterns */
+  TCS_FP8_E4M3 = 2   /* OCP E4M3FN bytes, with one fp32 scale per row */
+} tcs_dtype;
+
+/* hipStream_t without including HIP headers; NULL is the default stream. */
+typedef void* tcs_stream;
+
+/* ------------------------------------------------------------------ trie ---- */
+
+/*
+ * Canonical token trie (section 3.1: labels are token paths from the root, the
+ * root is the ANSWER: token; labels with a common start share nodes).
+ *
+ * Node ids are the rank of (depth, token path compared lexicographically by token
+ * id): breadth-first order with children in ascending token id, root = 0.  The
+ * number of nodes is the number of distinct non-empty label prefixes plus one,
+ * the state count of the minimal automaton ("Trie Automata for Constrained
+ * Decoding over Large Finite Sets", Proposition 1).  A node with children is
+ * internal and owns one query row; rows follow node-id order.  Edges (one per
+ * non-root node) are listed sorted by (token, parent row).
+ *
+ * Every array pointer is caller-owned host memory of the capacity stated.
+ */
+typedef struct {
+  /* capacities, set by the caller */
+  int32_t cap_nodes;     /* entries in each per-node array, in qnode/qparent, and in each
+                            edge array (edges need cap_nodes - 1) */
+  int32_t cap_levels;    /* entries in level_offsets (needs max_depth + 2) */
+  /* sizes, set by tcs_trie_build (also on TCS_ECAPACITY) */
+  int32_t n_nodes, n_int, n_labels, max_depth;
+  /* per node [cap_nodes] */
+  int32_t* parent;       /* parent id, -1 at the root */
+  int32_t* token;        /* token id; the root holds root_token */
+  int32_t* depth;
+  int32_t* child_begin;  /* id of the first child, 0 for a leaf */
+  int32_t* child_count;
+  int32_t* node_label;   /* label ending at the node, -1 if none */
+  int32_t* qrow;         /* query row of an internal node, -1 for a leaf */
+  /* per query row [cap_nodes] (n_int used) */
+  int32_t* qnode;        /* node id of the row */
+  int32_t* qparent;      /* row of the parent node, -1 for the root */
+  /* per label [M] */
+  int32_t* label_node;
+  /* per level [cap_levels] */
+  int32_t* level_offsets; /* first node of each depth, then n_nodes */
+  /* per edge [cap_nodes] (n_nodes - 1 used), sorted by (e_tok, e_qrow) */
+  int32_t* e_tok;
+  int32_t* e_qrow;       /* query row of the edge's parent */
+  int32_t* e_child;      /* node id of the edge's child */
+} tcs_trie;
+
+/*
+ * Build the trie of M labels given as CSR: label m is label_tokens[label_offsets[m]
+ * .. label_offsets[m+1]).  Labels keep their input order as label ids.
+ * Errors: TCS_EINVAL (M < 1, an empty label, a token or root_token outside [0,V)),
+ * TCS_EDUPLICATE (two equal labels), TCS_ECAPACITY (out->n_nodes / max_depth hold
+ * the sizes needed).  Host only; no GPU needed.
+ */
+int tcs_trie_build(const int32_t* label_offsets, const int32_t* label_tokens, int32_t M,
+                   int32_t root_token, int32_t V, tcs_trie* out);
+
+/* Device copy of the trie arrays needed by the kernels (all device pointers). */
+typedef struct {
+  int32_t n_nodes, n_int, n_labels, max_depth;
+  const int32_t* parent;       /* [n_nodes] */
+  const int32_t* token;        /* [n_nodes] */
+  const int32_t* child_begin;  /* [n_nodes] */
+  const int32_t* child_count;  /* [n_nodes] */
+  const int32_t* qnode;        /* [n_int] */
+  const int32_t* qparent;      /* [n_int] */
+  const int32_t* label_node;   /* [n_labels] */
+  const int32_t* e_tok;        /* [n_nodes-1] sorted */
+  const int32_t* e_qrow;       /* [n_nodes-1] */
+  const int32_t* e_child;      /* [n_nodes-1] */
+} tcs_trie_dev;
+
+/* --------------------------------------------------------- tree attention ---- */
+
+/*
+ * Ancestor-masked tree attention (section 3.2, "Custom attention kernel": all
+ * answer nodes of a document in one request, each attending only to the prompt and
+ * to the nodes on its own path).
+ *
+ * For document b, query row r (internal node u) and query head h, the keys are
+ * the document's keys Kd[doc_offsets[b] .. doc_offsets[b+1]) followed by the node
+ * keys of every row on the root-to-u path, u included (walk qparent from r).  KV
+ * head of query head h is h / (Hq/Hkv).  Output is softmax(q.k * scale) . v.
+ *
+ *   dtype       TCS_F32 or TCS_BF16: storage of Qn/Kn/Vn/Kd/Vd/O; math in fp32.
+ *   Qn          [n_int, Hq, hd]     node queries (shared by every document)
+ *   Kn, Vn      [n_int, Hkv, hd]    node keys / values
+ *   Kd, Vd      [sum L_b, Hkv, hd]  document keys / values, documents back to back
+ *   doc_offsets [B+1] device        prefix sums of document lengths (L_b may be 0)
+ *   qparent     [n_int] device      tcs_trie.qparent
+ *   O           [B, n_int, Hq, hd]  output, rounded to dtype
+ *   ws          workspace of tcs_tree_attn_workspace_bytes(n_int, Hq, hd) bytes
+ * hd must be 64 or 128 and Hq a multiple of Hkv (else TCS_EUNSUPPORTED / TCS_EINVAL).
+ */
+size_t tcs_tree_attn_workspace_bytes(int32_t n_int, int32_t Hq, int32_t hd);
+int tcs_tree_attn(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, int32_t Hq,
+                  int32_t Hkv, int32_t hd, const void* Qn, const void* Kn, const void* Vn,
+                  const void* Kd, const void* Vd, const int32_t* doc_offsets,
+                  const int32_t* qparent, float scale, void* O, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------- LM head ---- */
+
+/*
+ * Full-vocabulary output head with the log-sum-exp and the child-token gather
+ * fused in (section 4.1: F_head = 2 d V per answer position; the [rows x V] logits
+ * are never stored).
+ *
+ * Rows: r = b * n_int + q for document b and query row q (R = B * n_int rows).
+ *   logit[r, v] = h[r] . W[v]            (times w_scale[v] for an fp8 head)
+ *   lse[r]      = log sum_v exp(logit[r, v])
+ *   lp[b, c]    = logit[b*n_int + e_qrow, e_tok] - lse[b*n_int + e_qrow] for every
+ *                 edge (e_tok, e_qrow, e_child = c); lp[b, 0] = 0 for the root.
+ *
+ *   h_dtype     TCS_F32 or TCS_BF16: storage of h.
+ *   w_dtype     h_dtype, or TCS_FP8_E4M3 (with h_dtype TCS_BF16) plus w_scale [V] fp32.
+ *   h           [R, d];  W [V, d]
+ *   edges       trie->e_tok / e_qrow / e_child, sorted by token
+ *   lse         [R] fp32 out;  lp [B, n_nodes] fp32 out
+ *   ws          workspace of tcs_lmhead_workspace_bytes(...) bytes
+ * bf16 heads need d % 64 == 0.
+ */
+size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, int32_t rows, int32_t V);
+int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
+                          int32_t n_int, int32_t n_nodes, int32_t d, int32_t V, const void* h,
+                          const void* W, const float* w_scale, const int32_t* e_tok,
+                          const int32_t* e_qrow, const int32_t* e_child, float* lse, float* lp,
+                          void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------ path sums ---- */
+
+/*
+ * Per-label log score, label softmax and argmax (section 3.2).
+ *   ll[b, m]  = sum of lp[b, .] over the path root -> label_node[m], plus
+ *               log(1 - sum_{children c} exp(lp[b, c])) when label_node[m] has
+ *               children (accumulated in fp64; -inf if the children take all mass)
+ *   prob[b,.] = softmax over m of ll[b, .]            (optional: prob may be NULL)
+ *   label[b]  = argmax_m ll[b, m], lowest label id among equal maxima
+ * lp is [B, n_nodes] fp32 with lp[b, 0] = 0; ll and prob are [B, M] fp32.
+ */
+int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie, const float* lp,
+                         float* ll, float* prob, int32_t* label);
+
+/* ------------------------------------------------------------- classify ---- */
+
+/*
+ * Model of one answer position: a single attention layer and the output head.
+ *   x = E[token]; a = RMSNorm(x); q,k,v = a Wq^T, a Wk^T, a Wv^T   (no positions)
+ *   o = tree attention (above);  y = x + o Wo^T;  h = RMSNorm(y);  head(h)
+ * RMSNorm has gain 1 and epsilon `eps`.  In bf16 models a, q, k, v, o and h are
+ * stored (rounded to nearest-even) in bf16; y stays fp32.
+ */
+typedef struct {
+  tcs_dtype dtype;       /* TCS_F32 or TCS_BF16: E, Wq, Wk, Wv, Wo and activations */
+  tcs_dtype head_dtype;  /* dtype, or TCS_FP8_E4M3 (bf16 models) */
+  int32_t d, Hq, Hkv, hd, V;
+  float eps;
+  const void* E;         /* [V, d] token embeddings */
+  const void* Wq;        /* [Hq*hd, d] */
+  const void* Wk;        /* [Hkv*hd, d] */
+  const void* Wv;        /* [Hkv*hd, d] */
+  const void* Wo;        /* [d, Hq*hd] */
+  const void* W;         /* [V, d] output head */
+  const float* W_scale;  /* [V] for an fp8 head, else NULL */
+} tcs_model;
+
+/*
+ * A batch of documents: either their precomputed keys/values (Kd, Vd) or their
+ * token ids (doc_tokens), in which case the library computes each token's k and v
+ * with the model's input block.
+ */
+typedef struct {
+  int32_t B;
+  int32_t total_tokens;          /* doc_offsets[B] */
+  const int32_t* doc_offsets;    /* [B+1] device */
+  const void* Kd;                /* [total_tokens, Hkv, hd] model dtype, or NULL */
+  const void* Vd;
+  const int32_t* doc_tokens;     /* [total_tokens] device, used when Kd is NULL */
+} tcs_docs;
+
+/*
+ * The whole trie_tree pass on one stream: node input block, tree attention,
+ * output projection + residual + RMSNorm, output head with LSE and gather, path
+ * sums, label softmax and argmax.
+ *   label [B] int32 out; prob [B, M] fp32 out or NULL; ll [B, M] fp32 out or NULL.
+ *   ws    workspace of tcs_classify_workspace_bytes(model, trie, docs) bytes.
+ */
+size_t tcs_classify_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
+                                    const tcs_docs* docs);
+int tcs_classify(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* trie,
+                 const tcs_docs* docs, int32_t* label, float* prob, float* ll, void* ws,
+                 size_t ws_bytes);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* tcs_last_error(void);
+
+/* Library version string. */
+const char* tcs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TCS_H_ */

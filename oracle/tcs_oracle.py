@@ -49,7 +49,7 @@ __all__ = [
     "round_bf16", "decode_bf16", "decode_e4m3", "rmsnorm", "OracleModel",
     "node_layer", "doc_kv_from_tokens", "tree_attention", "hidden_states",
     "lm_head_lse", "head_logits_at", "edge_logprobs", "log1mexp", "path_log_likelihoods",
-    "label_softmax", "classify", "bruteforce_ll",
+    "label_softmax", "classify", "bruteforce_ll", "label_ll_on_paths",
 ]
 
 TCS_OK = 0
@@ -392,12 +392,17 @@ def classify(inp: dict, docs=None, model: OracleModel | None = None, trie: Trie 
     offs = inp["doc_offsets"]
     docs = list(range(len(offs) - 1)) if docs is None else list(docs)
     x, qn, kn, vn = node_layer(model, trie.token[trie.qnode])
+    # keys/values of the listed documents only, back to back
     if inp["cfg"].doc_mode == "tokens":
-        Kd, Vd = doc_kv_from_tokens(model, inp["doc_tokens"])
+        toks = np.concatenate([inp["doc_tokens"][offs[b]:offs[b + 1]] for b in docs])
+        Kd, Vd = doc_kv_from_tokens(model, toks)
     else:
         dec = decode_bf16 if model.bf16 else (lambda a: np.asarray(a, dtype=np.float64))
-        Kd, Vd = dec(inp["Kd"]), dec(inp["Vd"])
-    O = model.rnd(tree_attention(qn, kn, vn, trie, Kd, Vd, offs, model.scale, docs=docs))
+        Kd = dec(np.concatenate([inp["Kd"][offs[b]:offs[b + 1]] for b in docs]))
+        Vd = dec(np.concatenate([inp["Vd"][offs[b]:offs[b + 1]] for b in docs]))
+    sub = np.zeros(len(docs) + 1, dtype=np.int64)
+    sub[1:] = np.cumsum([offs[b + 1] - offs[b] for b in docs])
+    O = model.rnd(tree_attention(qn, kn, vn, trie, Kd, Vd, sub, model.scale))
     h = hidden_states(model, x[None], O)
     B, n_int, d = h.shape
     lse = lm_head_lse(model, h.reshape(-1, d)).reshape(B, n_int)
@@ -463,3 +468,63 @@ def bruteforce_ll(inp: dict, doc: int, label_ids=None, model: OracleModel | None
             ll += np.log(pstop) if pstop > 0 else -np.inf
         out.append(ll)
     return np.array(out)
+
+
+class _Rows:
+    """Row view of a compact array: row r of the full index space -> compact[idx[r]]."""
+
+    def __init__(self, compact, idx, n_rows):
+        self.compact, self.idx = compact, idx
+        self.shape = (n_rows,) + compact.shape[1:]
+
+    def __getitem__(self, r):
+        if isinstance(r, (list, tuple, np.ndarray)):
+            return self.compact[[self.idx[int(x)] for x in r]]
+        return self.compact[self.idx[int(r)]]
+
+
+def label_ll_on_paths(inp: dict, doc: int, label_ids, model: OracleModel | None = None,
+                      trie: Trie | None = None):
+    """LL of the listed labels for one document, computed from the query rows on
+    their paths only (the same steps as `classify`, restricted to those rows).
+
+    Lets a large trie be checked on sampled labels without scoring every row.
+    """
+    model = model or OracleModel(inp)
+    trie = trie or build_trie(inp["labels"], inp["root_token"], inp["cfg"].V)
+    need_rows, need_edges = set(), set()
+    for m in label_ids:
+        u = int(trie.label_node[m])
+        v = u
+        while v > 0:
+            need_edges.add(v)
+            need_rows.add(int(trie.qrow[trie.parent[v]]))
+            v = int(trie.parent[v])
+        if trie.child_count[u] > 0:
+            need_rows.add(int(trie.qrow[u]))
+            need_edges.update(range(trie.child_begin[u], trie.child_begin[u] + trie.child_count[u]))
+    rows = sorted(need_rows)
+    idx = {r: i for i, r in enumerate(rows)}
+    x, q, k, v = node_layer(model, trie.token[trie.qnode[rows]])
+    offs = inp["doc_offsets"]
+    if inp["cfg"].doc_mode == "tokens":
+        Kd, Vd = doc_kv_from_tokens(model, inp["doc_tokens"])
+    else:
+        Kd = decode_bf16(inp["Kd"][offs[doc]:offs[doc + 1]]) if model.bf16 else \
+            np.asarray(inp["Kd"][offs[doc]:offs[doc + 1]], dtype=np.float64)
+        Vd = decode_bf16(inp["Vd"][offs[doc]:offs[doc + 1]]) if model.bf16 else \
+            np.asarray(inp["Vd"][offs[doc]:offs[doc + 1]], dtype=np.float64)
+        offs = np.zeros(doc + 2, dtype=np.int64)   # only document `doc` is visited
+        offs[doc + 1] = Kd.shape[0]
+    n = trie.n_int
+    O = model.rnd(tree_attention(_Rows(q, idx, n), _Rows(k, idx, n), _Rows(v, idx, n), trie, Kd, Vd,
+                                 offs, model.scale, docs=[doc], rows=rows))
+    h = hidden_states(model, x[None], O)[0]
+    lse = lm_head_lse(model, h)
+    lp = np.zeros((1, trie.n_nodes))
+    for c in need_edges:
+        i = idx[int(trie.qrow[trie.parent[c]])]
+        lp[0, c] = head_logits_at(model, h[i:i + 1], cols=[trie.token[c]])[0, 0] - lse[i]
+    with np.errstate(all="ignore"):
+        ll = path_log_likelihoods(trie, lp)[0]
+    return ll[list(label_ids)], dict(rows=rows, lse=lse, h=h)

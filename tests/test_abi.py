@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host trie builder matches the oracle bit for bit."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle as O
+import trie_constrained_scoring_amd as tcs
+from synth import config, labels_to_csr, make_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tcs.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tcs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = tcs.lib()
+    names = declared_functions()
+    assert "tcs_classify" in names and "tcs_trie_build" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert "gfx950" in tcs.version()
+
+
+ARRAYS = ["parent", "token", "depth", "child_begin", "child_count", "node_label", "label_node",
+          "qrow", "qnode", "qparent", "level_offsets", "e_tok", "e_qrow", "e_child"]
+
+
+def assert_same_trie(t, o):
+    assert (t.n_nodes, t.n_int, t.n_labels, t.max_depth) == (o.n_nodes, o.n_int, o.n_labels, o.max_depth)
+    for n in ARRAYS:
+        np.testing.assert_array_equal(t.arrays[n], getattr(o, n), err_msg=n)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_trie_build_matches_oracle_on_configs(cid):
+    inp = make_inputs(config(cid), weights=False) if cid != 5 else make_inputs(
+        config(5, B=1, L=1), weights=False)
+    V = config(cid).V
+    t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], V)
+    assert_same_trie(t, O.build_trie(inp["labels"], inp["root_token"], V))
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.lists(st.integers(0, 6), min_size=1, max_size=7), min_size=1, max_size=30),
+       st.integers(0, 9))
+def test_trie_build_matches_oracle_random(raw, root):
+    V = 10
+    try:
+        o = O.build_trie(raw, root, V)
+    except O.TrieError as e:
+        offs, toks = labels_to_csr(raw)
+        with pytest.raises(tcs.TcsError) as ei:
+            tcs.trie_build(offs, toks, root, V)
+        assert ei.value.code == e.code
+        return
+    offs, toks = labels_to_csr(raw)
+    assert_same_trie(tcs.trie_build(offs, toks, root, V), o)
+
+
+def test_trie_build_errors():
+    def code(labels, root=0, V=10, offs=None, toks=None):
+        if offs is None:
+            offs, toks = labels_to_csr(labels)
+        with pytest.raises(tcs.TcsError) as e:
+            tcs.trie_build(offs, toks, root, V)
+        return e.value.code
+    assert code([[1, 2], [1, 2]]) == tcs.TCS_EDUPLICATE
+    assert code([[1, 12]]) == tcs.TCS_EINVAL
+    assert code([[1, -1]]) == tcs.TCS_EINVAL
+    assert code([[1]], root=10) == tcs.TCS_EINVAL
+    assert code(None, offs=np.array([0, 1, 1], np.int32), toks=np.array([3], np.int32)) == tcs.TCS_EINVAL
+    assert code(None, offs=np.array([0], np.int32), toks=np.zeros(0, np.int32)) == tcs.TCS_EINVAL
+
+
+def test_trie_build_capacity_report():
+    lib = tcs.lib()
+    offs, toks = labels_to_csr([[1, 2, 3], [1, 4], [5]])
+    bufs = [np.zeros(3, np.int32) for _ in range(14)]
+    t = tcs.tcs_trie(cap_nodes=3, cap_levels=2)
+    for n, b in zip([f for f, _ in tcs.tcs_trie._fields_[6:]], bufs):
+        setattr(t, n, b.ctypes.data_as(tcs.P32))
+    rc = lib.tcs_trie_build(offs.ctypes.data_as(tcs.P32), toks.ctypes.data_as(tcs.P32), 3, 0, 8, C.byref(t))
+    assert rc == tcs.TCS_ECAPACITY
+    assert t.n_nodes == 6 and t.max_depth == 3 and t.n_int == 3
+
+
+def test_null_pointer_errors_without_gpu():
+    lib = tcs.lib()
+    assert lib.tcs_trie_build(None, None, 1, 0, 10, None) == tcs.TCS_EINVAL
+    assert b"null" in lib.tcs_last_error()
+    assert lib.tcs_tree_attn(None, tcs.TCS_BF16, 1, 1, 4, 2, 96, *([None] * 7), 1.0, None, None, 0) == \
+        tcs.TCS_EUNSUPPORTED
+    assert lib.tcs_tree_attn(None, tcs.TCS_BF16, 1, 1, 4, 3, 128, *([None] * 7), 1.0, None, None, 0) == \
+        tcs.TCS_EINVAL
+    assert lib.tcs_lmhead_lse_gather(None, tcs.TCS_BF16, tcs.TCS_F32, 1, 1, 2, 64, 10, *([None] * 9), 0) == \
+        tcs.TCS_EUNSUPPORTED
+    assert lib.tcs_lmhead_lse_gather(None, tcs.TCS_BF16, tcs.TCS_BF16, 1, 1, 2, 100, 10, *([None] * 9), 0) == \
+        tcs.TCS_EUNSUPPORTED
+    assert lib.tcs_path_sum_softmax(None, 1, None, None, None, None, None) == tcs.TCS_EINVAL
+    assert lib.tcs_classify(None, None, None, None, None, None, None, None, 0) == tcs.TCS_EINVAL

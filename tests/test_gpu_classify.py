@@ -1,0 +1,104 @@
+"""End-to-end parity of tcs_classify against the oracle on all five workloads,
+at full size (sampled documents or labels where the oracle would take too long)
+and on small shapes with ragged documents and prefix labels."""
+import numpy as np
+import pytest
+
+import oracle as O
+import trie_constrained_scoring_amd as tcs
+from synth import config, make_inputs
+from tests.gpu_util import LL_TOL, check_labels, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def run_gpu(cfg, inp):
+    torch = _torch()
+    t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(t)
+    model = tcs.Model(cfg, inp)
+    docs = tcs.Docs(cfg, inp)
+    label, prob, ll = tcs.classify(model, td, docs)
+    torch.cuda.synchronize()
+    out = label.cpu().numpy(), prob.cpu().numpy(), ll.cpu().numpy()
+    del model, docs
+    torch.cuda.empty_cache()
+    return out
+
+
+SMALL = {
+    "tiny-f32": config(1),
+    "tiny-f32-ragged": config(1, doc_lens=(1, 32, 7, 0, 19)),
+    "running-bf16-small": config(2, V=3000, d=256, B=6, L=100, doc_lens=(100, 1, 257, 0, 64, 130)),
+    "zipf-bf16-small": config(3, V=4096, d=128, Hq=8, Hkv=2, B=3, L=50,
+                              trie=("zipf", 40, 2, 9, 1.2)),
+    "prefix-bf16-small": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=64, B=5, L=40,
+                                trie=("explicit", [[3], [3, 4], [3, 4, 5], [3, 6], [9, 9, 9], [9, 9], [1]])),
+    "fp8-small": config(5, V=2500, d=192, Hq=4, Hkv=1, B=4, L=300),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_classify_small_vs_oracle(dev, name):
+    cfg = SMALL[name]
+    inp = make_inputs(cfg, seed=101)
+    label, prob, ll = run_gpu(cfg, inp)
+    o = O.classify(inp)
+    check_labels(ll, prob, label, o["ll"], o["prob"], o["label"], f"classify[{name}]")
+
+
+@pytest.fixture(scope="module")
+def cfg2():
+    cfg = config(2)
+    return cfg, make_inputs(cfg)
+
+
+@pytest.fixture(scope="module")
+def cfg5():
+    cfg = config(5)
+    return cfg, make_inputs(cfg)
+
+
+@pytest.mark.parametrize("which", ["cfg2", "cfg5"])
+def test_classify_full_size_sampled_docs(dev, which, request):
+    """Running-example trie at full size: every label of sampled documents."""
+    cfg, inp = request.getfixturevalue(which)
+    label, prob, ll = run_gpu(cfg, inp)
+    docs = [0, 1, cfg.B // 2, cfg.B - 1]
+    o = O.classify(inp, docs=docs)
+    check_labels(ll[docs], prob[docs], label[docs], o["ll"], o["prob"], o["label"],
+                 f"classify[config {cfg.id} full, docs {docs}]")
+    np.testing.assert_allclose(prob.sum(axis=1), 1.0, atol=1e-4)
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_classify_full_size_sampled_labels(dev, cid):
+    """Large tries at full size: sampled (document, label) log-likelihoods from the
+    oracle's path-restricted pass; probabilities and labels by their properties."""
+    cfg = config(cid)
+    inp = make_inputs(cfg)
+    label, prob, ll = run_gpu(cfg, inp)
+    M = len(inp["labels"])
+    rng = np.random.default_rng(cid)
+    model = O.OracleModel(inp)
+    trie = O.build_trie(inp["labels"], inp["root_token"], cfg.V)
+    worst = 0.0
+    for b in (0, cfg.B - 1):
+        ids = sorted(set(rng.choice(M, 6, replace=False).tolist() + [int(label[b])]))
+        o_ll, _ = O.label_ll_on_paths(inp, b, ids, model=model, trie=trie)
+        err = np.abs(ll[b, ids] - o_ll).max()
+        worst = max(worst, err)
+        assert err <= LL_TOL, (b, ids, ll[b, ids], o_ll)
+    say(f"classify[config {cid} full]: sampled max |dll| {worst:.2e}")
+    # properties that hold at any size
+    ll64 = ll.astype(np.float64)
+    p_ref = np.exp(ll64 - ll64.max(axis=1, keepdims=True))
+    p_ref /= p_ref.sum(axis=1, keepdims=True)
+    assert np.abs(prob - p_ref).max() < 1e-4
+    np.testing.assert_allclose(prob.sum(axis=1), 1.0, atol=1e-4)
+    assert np.array_equal(label, np.argmax(ll, axis=1))

@@ -1,0 +1,444 @@
+// Ancestor-masked tree attention.
+//
+// "To Classify, Try a Trie Tree", section 3.2 ("Custom attention kernel"): all
+// answer nodes of a document go in one request and each node attends only to the
+// prompt and to the nodes on its own path.  The scores of a node against its own
+// path do not depend on the document, so they are reduced once per trie to a
+// softmax partial (max, sum, weighted value sum) per (node, head).  The document
+// part is a dense attention of every node query against the document's keys; its
+// online-softmax state is merged with the path partial by log-sum-exp at the end,
+// the same combine that "Building an Ultra-High Throughput AI-SQL Engine"
+// (section 3.2.4) applies to its two attention calls for joins.
+#include <cstdio>
+
+#include "tcs_device.h"
+#include "tcs_internal.h"
+
+namespace tcs {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- fp32 path
+// One wave per (document, query row, head): keys are the document's keys, then
+// the path from the row up to the root.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_simt_kernel(
+    int B, int n_int, int Hq, int Hkv, const T* __restrict__ Qn, const T* __restrict__ Kn,
+    const T* __restrict__ Vn, const T* __restrict__ Kd, const T* __restrict__ Vd,
+    const int32_t* __restrict__ doc_offsets, const int32_t* __restrict__ qparent, float scale,
+    T* __restrict__ O) {
+  constexpr int E = HD / 64;
+  const int lane = threadIdx.x & 63;
+  const long gw = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gw >= long(B) * n_int * Hq) return;
+  const int h = int(gw % Hq);
+  const int r = int((gw / Hq) % n_int);
+  const int b = int(gw / (long(Hq) * n_int));
+  const int g = h / (Hq / Hkv);
+  float q[E], o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    q[e] = to_f32(Qn[((size_t)r * Hq + h) * HD + lane * E + e]);
+    o[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  auto visit = [&](const T* k, const T* v) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s = fmaf(q[e], to_f32(k[lane * E + e]), s);
+    s = wave_sum(s) * scale;
+    const float mn = fmaxf(m, s);
+    const float c = __expf(m - mn), p = __expf(s - mn);
+    l = l * c + p;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = o[e] * c + p * to_f32(v[lane * E + e]);
+    m = mn;
+  };
+  for (int j = doc_offsets[b]; j < doc_offsets[b + 1]; ++j)
+    visit(Kd + ((size_t)j * Hkv + g) * HD, Vd + ((size_t)j * Hkv + g) * HD);
+  for (int w = r, steps = 0; w >= 0 && steps <= r; w = qparent[w], ++steps)
+    visit(Kn + ((size_t)w * Hkv + g) * HD, Vn + ((size_t)w * Hkv + g) * HD);
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    O[(((size_t)b * n_int + r) * Hq + h) * HD + lane * E + e] = from_f32<T>(o[e] * inv);
+}
+
+// ---------------------------------------------------------------- path partial
+// One wave per (query row, head): softmax partial over the row's own path.
+// anc_ml[(r*Hq + h)] = (max score, sum exp), anc_o = unnormalised value sum (fp32).
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void anc_attn_kernel(int n_int, int Hq, int Hkv,
+                                                       const T* __restrict__ Qn,
+                                                       const T* __restrict__ Kn,
+                                                       const T* __restrict__ Vn,
+                                                       const int32_t* __restrict__ qparent,
+                                                       float scale, float2* __restrict__ anc_ml,
+                                                       float* __restrict__ anc_o) {
+  constexpr int E = HD / 64;
+  const int lane = threadIdx.x & 63;
+  const long gw = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gw >= long(n_int) * Hq) return;
+  const int h = int(gw % Hq), r = int(gw / Hq);
+  const int g = h / (Hq / Hkv);
+  float q[E], o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    q[e] = to_f32(Qn[((size_t)r * Hq + h) * HD + lane * E + e]);
+    o[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int w = r, steps = 0; w >= 0 && steps <= r; w = qparent[w], ++steps) {
+    const T* k = Kn + ((size_t)w * Hkv + g) * HD;
+    const T* v = Vn + ((size_t)w * Hkv + g) * HD;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s = fmaf(q[e], to_f32(k[lane * E + e]), s);
+    s = wave_sum(s) * scale;
+    const float mn = fmaxf(m, s);
+    const float c = __expf(m - mn), p = __expf(s - mn);
+    l = l * c + p;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = o[e] * c + p * to_f32(v[lane * E + e]);
+    m = mn;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) anc_o[(size_t)gw * HD + lane * E + e] = o[e];
+  if (lane == 0) anc_ml[gw] = float2{m, l};
+}
+
+// ---------------------------------------------------------------- document part (MFMA)
+//
+// Workgroup: one document b, one KV head g, and 32*WR query rows of that head
+// (row j = node * G + hh, G = Hq/Hkv query heads per KV head).  4 waves laid out
+// WR (row blocks of 32) x WK (key tiles of 32).  Each iteration stages WK*32 keys
+// into LDS: keys in their natural [key][hd] layout, values transposed to
+// [hd][key] so both MFMA operands read 8 consecutive contraction elements.
+//
+// Per wave, with v_mfma_f32_32x32x16_bf16:
+//   S^T[key][row] = K . Q^T  (A = K from LDS, B = Q^T from registers)
+//     -> lane l holds row l%32 and keys 8j + 4(l/32) + i, so the softmax row
+//        statistics stay in the lane (plus its partner lane l^32);
+//   O^T[hd][row] += V^T . P^T (A = V^T from LDS, B = P^T straight from the S^T
+//     registers, with the same key order on both operands).
+template <int HD, int WR, int WK>
+__global__ __launch_bounds__(256) void doc_attn_mfma_kernel(
+    int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn, const uint16_t* __restrict__ Kd,
+    const uint16_t* __restrict__ Vd, const int32_t* __restrict__ doc_offsets,
+    const float2* __restrict__ anc_ml, const float* __restrict__ anc_o, float scale,
+    uint16_t* __restrict__ O) {
+  static_assert(WR * WK == 4, "4 waves");
+  constexpr int KT = 32 * WK;        // keys per stage
+  constexpr int LDK = HD + 8;        // sK row (bf16)
+  constexpr int LDV = KT + 8;        // sVt row (bf16)
+  constexpr int STAGE = KT * LDK + HD * LDV;
+  constexpr int K_CH = KT * (HD / 8) / 256;              // K chunks per thread
+  constexpr int V_GROUPS = (KT / 4) * (HD / 8);          // 4 keys x 8 hd groups
+  constexpr int V_GR = (V_GROUPS + 255) / 256;
+  constexpr int NBLK = HD / 32;      // O^T blocks
+  constexpr int KSTEPS = HD / 16;
+  static_assert(K_CH * 256 == KT * (HD / 8), "K staging");
+  constexpr int MERGE_FLOATS = WR * WK * 32 * (HD + 1) + WR * WK * 32 * 2;
+  constexpr int LDS_BYTES = (2 * STAGE * 2 > MERGE_FLOATS * 4) ? 2 * STAGE * 2 : MERGE_FLOATS * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LDS_BYTES];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+
+  const int G = Hq / Hkv;
+  const int rows_total = n_int * G;
+  const int n_rb = (rows_total + 32 * WR - 1) / (32 * WR);
+  const int rb = blockIdx.x % n_rb;
+  const int g = (blockIdx.x / n_rb) % Hkv;
+  const int b = blockIdx.x / (n_rb * Hkv);
+  const int j0 = rb * 32 * WR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / WK, wk = wave % WK;
+  const int doc0 = doc_offsets[b];
+  const int L = doc_offsets[b + 1] - doc0;
+
+  // Q^T fragments for this wave's 32 rows (lane: row l%32, hd 16*ks + 8*(l/32) ..)
+  bf16x8 qf[KSTEPS];
+  {
+    const int j = j0 + wr * 32 + (lane & 31);
+    const bool ok = j < rows_total;
+    const int r = ok ? j / G : 0, h = g * G + (ok ? j % G : 0);
+    const uint16_t* qp = Qn + ((size_t)r * Hq + h) * HD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : uint4{0, 0, 0, 0};
+      qf[ks] = *reinterpret_cast<bf16x8*>(&v);
+    }
+  }
+
+  uint4 rk[K_CH];
+  uint4 rv[V_GR][4];
+  auto load_stage = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < K_CH; ++i) {
+      const int c = tid + i * 256;
+      const int kk = c / (HD / 8), hc = c % (HD / 8);
+      const int key = key0 + kk;
+      rk[i] = key < L ? *reinterpret_cast<const uint4*>(Kd + ((size_t)(doc0 + key) * Hkv + g) * HD + hc * 8)
+                      : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < V_GR; ++i) {
+      const int gi = tid + i * 256;
+      const int kg = gi / (HD / 8), hc = gi % (HD / 8);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int key = key0 + kg * 4 + t;
+        rv[i][t] = (gi < V_GROUPS && key < L)
+                       ? *reinterpret_cast<const uint4*>(Vd + ((size_t)(doc0 + key) * Hkv + g) * HD + hc * 8)
+                       : uint4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    uint16_t* sK = lds + buf * STAGE;
+    uint16_t* sV = sK + KT * LDK;
+#pragma unroll
+    for (int i = 0; i < K_CH; ++i) {
+      const int c = tid + i * 256;
+      const int kk = c / (HD / 8), hc = c % (HD / 8);
+      *reinterpret_cast<uint4*>(sK + kk * LDK + hc * 8) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V_GR; ++i) {
+      const int gi = tid + i * 256;
+      if (gi >= V_GROUPS) continue;
+      const int kg = gi / (HD / 8), hc = gi % (HD / 8);
+      const uint32_t w[4][4] = {{rv[i][0].x, rv[i][0].y, rv[i][0].z, rv[i][0].w},
+                                {rv[i][1].x, rv[i][1].y, rv[i][1].z, rv[i][1].w},
+                                {rv[i][2].x, rv[i][2].y, rv[i][2].z, rv[i][2].w},
+                                {rv[i][3].x, rv[i][3].y, rv[i][3].z, rv[i][3].w}};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t k0 = (w[0][e >> 1] >> sh) & 0xFFFFu, k1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t k2 = (w[2][e >> 1] >> sh) & 0xFFFFu, k3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(sV + (hc * 8 + e) * LDV + kg * 4) = uint2{k0 | (k1 << 16), k2 | (k3 << 16)};
+      }
+    }
+  };
+
+  f32x16 acc[NBLK];
+#pragma unroll
+  for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  float m = -INFINITY, lsum = 0.f;   // base-2 running max; this lane's share of the sum
+  const float qk = scale * LOG2E;
+
+  const int n_it = (L + KT - 1) / KT;
+  if (n_it > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < n_it) load_stage((it + 1) * KT);
+    const uint16_t* sK = lds + cur * STAGE;
+    const uint16_t* sV = sK + KT * LDK;
+    // S^T = K Q^T for this wave's 32 keys
+    f32x16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    const uint16_t* kp = sK + (wk * 32 + (lane & 31)) * LDK + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+    // online softmax (base 2); keys past the document end are masked
+    const int kbase = it * KT + wk * 32;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kbase + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      s[e] = key < L ? s[e] * qk : -INFINITY;
+      tmax = fmaxf(tmax, s[e]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);
+    const float c = mn == -INFINITY ? 1.f : exp2f(m - mn);
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = mn == -INFINITY ? 0.f : exp2f(s[e] - mn);
+      lsum = lsum * (e == 0 ? c : 1.f) + p[e];
+    }
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] *= c;
+    // P^T fragments: keys {8j + 4(l/32) + i}; step 0 takes j = 0,1, step 1 j = 2,3.
+    // P is split into a bf16 high part and a bf16 remainder (two MFMAs), which
+    // keeps the weights to ~2^-17 relative error instead of bf16's 2^-9.
+    bf16x8 ph[2], pl[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const float a = p[8 * st + 2 * q2], c2 = p[8 * st + 2 * q2 + 1];
+        const uint16_t ah = f32_to_bf16(a), ch = f32_to_bf16(c2);
+        const uint16_t al = f32_to_bf16(a - bf16_to_f32(ah)), cl = f32_to_bf16(c2 - bf16_to_f32(ch));
+        wh[q2] = uint32_t(ah) | (uint32_t(ch) << 16);
+        wl[q2] = uint32_t(al) | (uint32_t(cl) << 16);
+      }
+      uint4 uh{wh[0], wh[1], wh[2], wh[3]}, ul{wl[0], wl[1], wl[2], wl[3]};
+      ph[st] = *reinterpret_cast<bf16x8*>(&uh);
+      pl[st] = *reinterpret_cast<bf16x8*>(&ul);
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      const uint16_t* vp = sV + (blk * 32 + (lane & 31)) * LDV + wk * 32 + 4 * (lane >> 5);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp + 16 * st);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16 * st + 8);
+        uint4 u{lo.x, lo.y, hi.x, hi.y};
+        const bf16x8 vf = *reinterpret_cast<bf16x8*>(&u);
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[st], acc[blk], 0, 0, 0);
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[st], acc[blk], 0, 0, 0);
+      }
+    }
+    if (it + 1 < n_it) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // merge the WK key slices of each row block and the row's path partial
+  float* so = reinterpret_cast<float*>(lds_raw);            // [WR*WK][32][HD+1]
+  float* sml = so + WR * WK * 32 * (HD + 1);                 // [WR*WK][32][2]
+  lsum += __shfl_xor(lsum, 32, 64);
+  {
+    float* base = so + (size_t)wave * 32 * (HD + 1);
+    const int row = lane & 31;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int hd = blk * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        base[row * (HD + 1) + hd] = acc[blk][e];
+      }
+    if (lane < 32) {
+      sml[(wave * 32 + row) * 2 + 0] = m;
+      sml[(wave * 32 + row) * 2 + 1] = lsum;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < WR * 32 * HD; idx += 256) {
+    const int rw = idx / HD, hd = idx % HD;      // rw: row within the workgroup
+    const int wrr = rw / 32, row = rw % 32;
+    const int j = j0 + rw;
+    if (j >= rows_total) continue;
+    const int r = j / G, h = g * G + j % G;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < WK; ++k) M = fmaxf(M, sml[((wrr * WK + k) * 32 + row) * 2]);
+    float Ls = 0.f, Os = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < WK; ++k) {
+        const int wv = wrr * WK + k;
+        const float f = exp2f(sml[(wv * 32 + row) * 2] - M);
+        Ls += f * sml[(wv * 32 + row) * 2 + 1];
+        Os += f * so[((size_t)wv * 32 + row) * (HD + 1) + hd];
+      }
+    }
+    const float2 a = anc_ml[(size_t)r * Hq + h];
+    const float ma = a.x * LOG2E;
+    const float Mt = fmaxf(M, ma);
+    const float fd = M == -INFINITY ? 0.f : exp2f(M - Mt);
+    const float fa = exp2f(ma - Mt);
+    const float num = Os * fd + anc_o[((size_t)r * Hq + h) * HD + hd] * fa;
+    const float den = Ls * fd + a.y * fa;
+    O[(((size_t)b * n_int + r) * Hq + h) * HD + hd] = f32_to_bf16(num / den);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32_t Hkv, int32_t hd,
+                    const void* Qn, const void* Kn, const void* Vn, const int32_t* qparent,
+                    float scale, float* anc_ml, float* anc_o) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long waves = long(n_int) * Hq;
+  if (waves == 0) return TCS_OK;
+  const int grid = int((waves + 3) / 4);
+  float2* ml = reinterpret_cast<float2*>(anc_ml);
+#define TCS_ANC(T, HDV)                                                                            \
+  anc_attn_kernel<T, HDV><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, static_cast<const T*>(Qn),        \
+                                               static_cast<const T*>(Kn), static_cast<const T*>(Vn), \
+                                               qparent, scale, ml, anc_o)
+  if (dt == TCS_BF16) {
+    if (hd == 128) TCS_ANC(bf16_t, 128); else TCS_ANC(bf16_t, 64);
+  } else {
+    if (hd == 128) TCS_ANC(float, 128); else TCS_ANC(float, 64);
+  }
+#undef TCS_ANC
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TCS_EHIP, "anc_attn: %s", hipGetErrorString(e));
+  return TCS_OK;
+}
+
+int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
+                    int32_t hd, const void* Qn, const void* Kd, const void* Vd,
+                    const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
+                    float scale, void* O) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0 || n_int == 0) return TCS_OK;
+  if (dt != TCS_BF16) return fail(TCS_EUNSUPPORTED, "doc_attn: MFMA path is bf16 only");
+  const int G = Hq / Hkv;
+  const long rows = long(n_int) * G;
+  const float2* ml = reinterpret_cast<const float2*>(anc_ml);
+  auto q = static_cast<const uint16_t*>(Qn);
+  auto kd = static_cast<const uint16_t*>(Kd);
+  auto vd = static_cast<const uint16_t*>(Vd);
+  auto o = static_cast<uint16_t*>(O);
+  if (rows <= 64) {
+    const long grid = long(B) * Hkv * ((rows + 31) / 32);
+    if (hd == 128)
+      doc_attn_mfma_kernel<128, 1, 4><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+    else
+      doc_attn_mfma_kernel<64, 1, 4><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+  } else {
+    const long grid = long(B) * Hkv * ((rows + 127) / 128);
+    if (hd == 128)
+      doc_attn_mfma_kernel<128, 4, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+    else
+      doc_attn_mfma_kernel<64, 4, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TCS_EHIP, "doc_attn: %s", hipGetErrorString(e));
+  return TCS_OK;
+}
+
+int launch_attn_simt(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
+                     int32_t hd, const void* Qn, const void* Kn, const void* Vn, const void* Kd,
+                     const void* Vd, const int32_t* doc_offsets, const int32_t* qparent, float scale,
+                     void* O) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long waves = long(B) * n_int * Hq;
+  if (waves == 0) return TCS_OK;
+  const int grid = int((waves + 3) / 4);
+#define TCS_SIMT(T, HDV)                                                                           \
+  attn_simt_kernel<T, HDV><<<grid, 256, 0, s>>>(                                                   \
+      B, n_int, Hq, Hkv, static_cast<const T*>(Qn), static_cast<const T*>(Kn),                     \
+      static_cast<const T*>(Vn), static_cast<const T*>(Kd), static_cast<const T*>(Vd), doc_offsets, \
+      qparent, scale, static_cast<T*>(O))
+  if (dt == TCS_BF16) {
+    if (hd == 128) TCS_SIMT(bf16_t, 128); else TCS_SIMT(bf16_t, 64);
+  } else {
+    if (hd == 128) TCS_SIMT(float, 128); else TCS_SIMT(float, 64);
+  }
+#undef TCS_SIMT
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TCS_EHIP, "attn_simt: %s", hipGetErrorString(e));
+  return TCS_OK;
+}
+
+}  // namespace tcs

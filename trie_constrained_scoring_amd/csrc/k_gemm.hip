@@ -1,0 +1,224 @@
+// Projection GEMMs of the node input block (q/k/v) and of the output projection
+// (o Wo^T + residual), and the RMSNorm row kernels around them.
+#include <cstdio>
+
+#include "gemm_core.h"
+#include "tcs_internal.h"
+
+namespace tcs {
+
+// ------------------------------------------------------------------ bf16 MFMA
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
+    int M, int N, int K, const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B,
+    int ldb, void* __restrict__ C, int ldc, int epi, GemmResid resid) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
+  const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  int mt, nt;
+  tile_coords<8>(nbm, nbn, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  f32x4 acc[S::MB][S::NB];
+  gemm_mainloop<BM, BN, WM, WN, false>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+  for (int i = 0; i < S::MB; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * S::TM + i * 16 + (lane >> 4) * 4 + r;
+      if (row >= M) continue;
+      const uint16_t* xres = nullptr;
+      if (epi == GEMM_RESID) {
+        const int tok = resid.token[resid.qnode[row % resid.n_int]];
+        xres = static_cast<const uint16_t*>(resid.E) + (size_t)tok * N;
+      }
+#pragma unroll
+      for (int j = 0; j < S::NB; ++j) {
+        const int col = n0 + wn * S::TN + j * 16 + (lane & 15);
+        if (col >= N) continue;
+        const float v = acc[i][j][r];
+        if (epi == GEMM_RESID) {
+          static_cast<float*>(C)[(size_t)row * ldc + col] = v + bf16_to_f32(xres[col]);
+        } else {
+          static_cast<uint16_t*>(C)[(size_t)row * ldc + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 SIMT
+
+// 64 x 64 tile, 256 threads, 4 x 4 outputs per thread.
+__global__ __launch_bounds__(256) void gemm_nt_f32_kernel(int M, int N, int K,
+                                                          const float* __restrict__ A, int lda,
+                                                          const float* __restrict__ B, int ldb,
+                                                          float* __restrict__ C, int ldc, int epi,
+                                                          GemmResid resid) {
+  __shared__ float sA[16][68];
+  __shared__ float sB[16][68];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * 256;  // 0..1023 over 64 rows x 16 k
+      const int r = e >> 4, k = e & 15;
+      const int gk = k0 + k;
+      sA[k][r] = (m0 + r < M && gk < K) ? A[(size_t)(m0 + r) * lda + gk] : 0.f;
+      sB[k][r] = (n0 + r < N && gk < K) ? B[(size_t)(n0 + r) * ldb + gk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= M) continue;
+    const float* xres = nullptr;
+    if (epi == GEMM_RESID) {
+      const int tok = resid.token[resid.qnode[row % resid.n_int]];
+      xres = static_cast<const float*>(resid.E) + (size_t)tok * N;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= N) continue;
+      C[(size_t)row * ldc + col] = acc[i][j] + (xres ? xres[col] : 0.f);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ RMSNorm rows
+
+template <typename T>
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const T* __restrict__ E,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ idx2,
+                                                            int d, int V, float eps,
+                                                            T* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int tok = idx2 ? idx2[idx[r]] : idx[r];
+  if (tok < 0 || tok >= V) {  // invalid token id: poison the row instead of reading outside E
+    for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(__builtin_nanf(""));
+    return;
+  }
+  const T* x = E + (size_t)tok * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float v = to_f32(x[i]);
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum256<T>(ss, red);
+  const float rs = 1.0f / sqrtf(ss / float(d) + eps);
+  for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(to_f32(x[i]) * rs);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ y, int d, float eps,
+                                                      T* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const float* x = y + (size_t)r * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(x[i], x[i], ss);
+  ss = block_sum256<T>(ss, red);
+  const float rs = 1.0f / sqrtf(ss / float(d) + eps);
+  for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(x[i] * rs);
+}
+
+// ------------------------------------------------------------------ launchers
+
+static int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TCS_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return TCS_OK;
+}
+
+int launch_embed_rmsnorm(void* stream, tcs_dtype dt, const void* E, const int32_t* idx,
+                         const int32_t* idx2, int32_t n, int32_t d, int32_t V, float eps, void* out) {
+  if (n <= 0) return TCS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == TCS_BF16)
+    embed_rmsnorm_kernel<bf16_t><<<n, 256, 0, s>>>(static_cast<const bf16_t*>(E), idx, idx2, d, V,
+                                                   eps, static_cast<bf16_t*>(out));
+  else
+    embed_rmsnorm_kernel<float><<<n, 256, 0, s>>>(static_cast<const float*>(E), idx, idx2, d, V,
+                                                  eps, static_cast<float*>(out));
+  return check_launch("embed_rmsnorm");
+}
+
+int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, float eps,
+                   void* out) {
+  if (n <= 0) return TCS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == TCS_BF16)
+    rownorm_kernel<bf16_t><<<n, 256, 0, s>>>(y, d, eps, static_cast<bf16_t*>(out));
+  else
+    rownorm_kernel<float><<<n, 256, 0, s>>>(y, d, eps, static_cast<float*>(out));
+  return check_launch("rownorm");
+}
+
+template <int BM, int BN, int WM, int WN>
+static void launch_bf16_cfg(hipStream_t s, int M, int N, int K, const void* A, int lda,
+                            const void* B, int ldb, void* C, int ldc, int epi, GemmResid r) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  gemm_nt_bf16_kernel<BM, BN, WM, WN><<<tiles, 64 * WM * WN, 0, s>>>(
+      M, N, K, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
+      epi, r);
+}
+
+int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N, int32_t K,
+                   const void* A, int32_t lda, const void* B, int32_t ldb, void* C, int32_t ldc,
+                   const GemmResid* resid) {
+  if (M <= 0 || N <= 0) return TCS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GemmResid r = resid ? *resid : GemmResid{nullptr, nullptr, nullptr, 1};
+  if (dt == TCS_BF16) {
+    if (K % GEMM_BK != 0) return fail(TCS_EUNSUPPORTED, "gemm: K=%d is not a multiple of 64", K);
+    const long t256 = long((M + 255) / 256) * ((N + 255) / 256);
+    const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
+    if (t256 >= 512)
+      launch_bf16_cfg<256, 256, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
+    else if (t128 >= 512)
+      launch_bf16_cfg<128, 128, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
+    else
+      launch_bf16_cfg<64, 64, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
+  } else {
+    dim3 grid((N + 63) / 64, (M + 63) / 64);
+    gemm_nt_f32_kernel<<<grid, 256, 0, s>>>(M, N, K, static_cast<const float*>(A), lda,
+                                             static_cast<const float*>(B), ldb,
+                                             static_cast<float*>(C), ldc, epi, r);
+  }
+  return check_launch("gemm_nt");
+}
+
+}  // namespace tcs

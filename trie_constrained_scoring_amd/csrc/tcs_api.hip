@@ -1,0 +1,243 @@
+// C-ABI entry points of libtcs: argument checks, workspace layout, and the
+// classify chain on one stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "tcs_internal.h"
+
+namespace tcs {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+void clear_error() { g_err[0] = 0; }
+
+int launch_attn_simt(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
+                     int32_t hd, const void* Qn, const void* Kn, const void* Vn, const void* Kd,
+                     const void* Vd, const int32_t* doc_offsets, const int32_t* qparent, float scale,
+                     void* O);
+
+static int check_attn_dims(tcs_dtype dt, int32_t Hq, int32_t Hkv, int32_t hd) {
+  if (dt != TCS_F32 && dt != TCS_BF16) return fail(TCS_EUNSUPPORTED, "dtype %d not supported", int(dt));
+  if (hd != 64 && hd != 128) return fail(TCS_EUNSUPPORTED, "head_dim %d (need 64 or 128)", hd);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(TCS_EINVAL, "heads Hq=%d Hkv=%d (Hq must be a multiple of Hkv)", Hq, Hkv);
+  return TCS_OK;
+}
+
+static size_t anc_bytes(int32_t n_int, int32_t Hq, int32_t hd) {
+  return align_up(size_t(n_int) * Hq * 8) + align_up(size_t(n_int) * Hq * hd * 4);
+}
+
+// Tree attention on a workspace laid out as [anc_ml | anc_o].
+static int tree_attn_impl(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq,
+                          int32_t Hkv, int32_t hd, const void* Qn, const void* Kn, const void* Vn,
+                          const void* Kd, const void* Vd, const int32_t* doc_offsets,
+                          const int32_t* qparent, float scale, void* O, void* ws) {
+  if (dt == TCS_F32)
+    return launch_attn_simt(stream, dt, B, n_int, Hq, Hkv, hd, Qn, Kn, Vn, Kd, Vd, doc_offsets,
+                            qparent, scale, O);
+  Carve c(ws);
+  float* ml = c.take<float>(size_t(n_int) * Hq * 2);
+  float* ao = c.take<float>(size_t(n_int) * Hq * hd);
+  int rc = launch_anc_attn(stream, dt, n_int, Hq, Hkv, hd, Qn, Kn, Vn, qparent, scale, ml, ao);
+  if (rc) return rc;
+  return launch_doc_attn(stream, dt, B, n_int, Hq, Hkv, hd, Qn, Kd, Vd, doc_offsets, ml, ao, scale, O);
+}
+
+static size_t lmhead_part_bytes(int32_t rows, int32_t V) {
+  return align_up(size_t(lmhead_n_tiles(TCS_BF16, V)) * size_t(rows) * 8);
+}
+
+}  // namespace tcs
+
+using namespace tcs;
+
+extern "C" {
+
+const char* tcs_last_error(void) { return g_err; }
+const char* tcs_version(void) { return "libtcs 0.1 (gfx950)"; }
+
+size_t tcs_tree_attn_workspace_bytes(int32_t n_int, int32_t Hq, int32_t hd) {
+  return anc_bytes(n_int, Hq, hd);
+}
+
+int tcs_tree_attn(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, int32_t Hq,
+                  int32_t Hkv, int32_t hd, const void* Qn, const void* Kn, const void* Vn,
+                  const void* Kd, const void* Vd, const int32_t* doc_offsets,
+                  const int32_t* qparent, float scale, void* O, void* ws, size_t ws_bytes) {
+  clear_error();
+  if (int rc = check_attn_dims(dtype, Hq, Hkv, hd)) return rc;
+  if (B < 0 || n_int < 0) return fail(TCS_EINVAL, "tree_attn: B=%d n_int=%d", B, n_int);
+  if (B == 0 || n_int == 0) return TCS_OK;
+  if (!Qn || !Kn || !Vn || !Kd || !Vd || !doc_offsets || !qparent || !O)
+    return fail(TCS_EINVAL, "tree_attn: null pointer");
+  if (dtype == TCS_BF16 && (!ws || ws_bytes < anc_bytes(n_int, Hq, hd)))
+    return fail(TCS_ECAPACITY, "tree_attn: workspace %zu < %zu bytes", ws_bytes, anc_bytes(n_int, Hq, hd));
+  return tree_attn_impl(stream, dtype, B, n_int, Hq, Hkv, hd, Qn, Kn, Vn, Kd, Vd, doc_offsets,
+                        qparent, scale, O, ws);
+}
+
+size_t tcs_lmhead_workspace_bytes(tcs_dtype /*h_dtype*/, int32_t rows, int32_t V) {
+  return lmhead_part_bytes(rows, V);
+}
+
+int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
+                          int32_t n_int, int32_t n_nodes, int32_t d, int32_t V, const void* h,
+                          const void* W, const float* w_scale, const int32_t* e_tok,
+                          const int32_t* e_qrow, const int32_t* e_child, float* lse, float* lp,
+                          void* ws, size_t ws_bytes) {
+  clear_error();
+  if (h_dtype != TCS_F32 && h_dtype != TCS_BF16)
+    return fail(TCS_EUNSUPPORTED, "lmhead: h dtype %d", int(h_dtype));
+  if (!(w_dtype == h_dtype || (h_dtype == TCS_BF16 && w_dtype == TCS_FP8_E4M3)))
+    return fail(TCS_EUNSUPPORTED, "lmhead: weight dtype %d with h dtype %d", int(w_dtype), int(h_dtype));
+  if (B < 0 || n_int < 1 || n_nodes < 2 || d < 1 || V < 1)
+    return fail(TCS_EINVAL, "lmhead: B=%d n_int=%d n_nodes=%d d=%d V=%d", B, n_int, n_nodes, d, V);
+  if (h_dtype == TCS_BF16 && d % 64 != 0)
+    return fail(TCS_EUNSUPPORTED, "lmhead: bf16 head needs d %% 64 == 0 (d=%d)", d);
+  if (B == 0) return TCS_OK;
+  if (!h || !W || !e_tok || !e_qrow || !e_child || !lse || !lp || (w_dtype == TCS_FP8_E4M3 && !w_scale))
+    return fail(TCS_EINVAL, "lmhead: null pointer");
+  const int64_t rows = int64_t(B) * n_int;
+  if (rows > INT32_MAX) return fail(TCS_EINVAL, "lmhead: %lld rows", (long long)rows);
+  const size_t need = lmhead_part_bytes(int32_t(rows), V);
+  if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "lmhead: workspace %zu < %zu bytes", ws_bytes, need);
+  return launch_lmhead(stream, h_dtype, w_dtype, B, n_int, n_nodes, d, V, h, W, w_scale, e_tok,
+                       e_qrow, e_child, n_nodes - 1, lse, lp, ws);
+}
+
+int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie, const float* lp,
+                         float* ll, float* prob, int32_t* label) {
+  clear_error();
+  if (!trie) return fail(TCS_EINVAL, "path_sum: null trie");
+  if (B < 0 || trie->n_labels < 1 || trie->n_nodes < 2)
+    return fail(TCS_EINVAL, "path_sum: B=%d M=%d n_nodes=%d", B, trie->n_labels, trie->n_nodes);
+  if (B == 0) return TCS_OK;
+  if (!lp || !ll || !label || !trie->parent || !trie->child_begin || !trie->child_count ||
+      !trie->label_node)
+    return fail(TCS_EINVAL, "path_sum: null pointer");
+  return launch_path_sum(stream, B, trie, lp, ll, prob, label);
+}
+
+// ---------------------------------------------------------------- classify
+
+struct ClassifyLayout {
+  size_t total;
+  void *a_nodes, *Qn, *Kn, *Vn, *a_doc, *Kd, *Vd, *anc, *O, *h, *part, *ll;
+  float *y, *lse, *lp;
+};
+
+static ClassifyLayout classify_layout(const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
+                                      void* ws) {
+  const size_t es = dtype_bytes(m->dtype);
+  const size_t n_int = t->n_int, R = size_t(d->B) * t->n_int;
+  const size_t qd = size_t(m->Hq) * m->hd, kd = size_t(m->Hkv) * m->hd;
+  Carve c(ws);
+  ClassifyLayout L{};
+  L.a_nodes = c.take<char>(n_int * m->d * es);
+  L.Qn = c.take<char>(n_int * qd * es);
+  L.Kn = c.take<char>(n_int * kd * es);
+  L.Vn = c.take<char>(n_int * kd * es);
+  if (!d->Kd) {
+    const size_t T = d->total_tokens;
+    L.a_doc = c.take<char>(T * m->d * es);
+    L.Kd = c.take<char>(T * kd * es);
+    L.Vd = c.take<char>(T * kd * es);
+  }
+  L.anc = c.take<char>(anc_bytes(t->n_int, m->Hq, m->hd));
+  L.O = c.take<char>(R * qd * es);
+  L.y = c.take<float>(R * m->d);
+  L.h = c.take<char>(R * m->d * es);
+  L.part = c.take<char>(lmhead_part_bytes(int32_t(R), m->V));
+  L.lse = c.take<float>(R);
+  L.lp = c.take<float>(size_t(d->B) * t->n_nodes);
+  L.ll = c.take<float>(size_t(d->B) * t->n_labels);
+  L.total = c.used;
+  return L;
+}
+
+static int check_classify(const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d) {
+  if (!m || !t || !d) return fail(TCS_EINVAL, "classify: null model/trie/docs");
+  if (int rc = check_attn_dims(m->dtype, m->Hq, m->Hkv, m->hd)) return rc;
+  if (!(m->head_dtype == m->dtype || (m->dtype == TCS_BF16 && m->head_dtype == TCS_FP8_E4M3)))
+    return fail(TCS_EUNSUPPORTED, "classify: head dtype %d with model dtype %d", int(m->head_dtype),
+                int(m->dtype));
+  if (m->d < 1 || m->V < 1) return fail(TCS_EINVAL, "classify: d=%d V=%d", m->d, m->V);
+  if (m->dtype == TCS_BF16 && m->d % 64 != 0)
+    return fail(TCS_EUNSUPPORTED, "classify: bf16 model needs d %% 64 == 0 (d=%d)", m->d);
+  if (!m->E || !m->Wq || !m->Wk || !m->Wv || !m->Wo || !m->W ||
+      (m->head_dtype == TCS_FP8_E4M3 && !m->W_scale))
+    return fail(TCS_EINVAL, "classify: null weight pointer");
+  if (t->n_nodes < 2 || t->n_int < 1 || t->n_labels < 1)
+    return fail(TCS_EINVAL, "classify: trie with %d nodes, %d rows, %d labels", t->n_nodes, t->n_int,
+                t->n_labels);
+  if (!t->parent || !t->token || !t->child_begin || !t->child_count || !t->qnode || !t->qparent ||
+      !t->label_node || !t->e_tok || !t->e_qrow || !t->e_child)
+    return fail(TCS_EINVAL, "classify: null trie array");
+  if (d->B < 0 || d->total_tokens < 0) return fail(TCS_EINVAL, "classify: B=%d tokens=%d", d->B, d->total_tokens);
+  if (d->B > 0 && !d->doc_offsets) return fail(TCS_EINVAL, "classify: null doc_offsets");
+  if (d->B > 0 && !d->Kd && !d->doc_tokens) return fail(TCS_EINVAL, "classify: docs need Kd/Vd or tokens");
+  if (d->Kd && !d->Vd) return fail(TCS_EINVAL, "classify: Kd without Vd");
+  if (int64_t(d->B) * t->n_int > INT32_MAX) return fail(TCS_EINVAL, "classify: too many rows");
+  return TCS_OK;
+}
+
+size_t tcs_classify_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
+                                    const tcs_docs* docs) {
+  if (check_classify(model, trie, docs)) return 0;
+  return classify_layout(model, trie, docs, nullptr).total;
+}
+
+int tcs_classify(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
+                 int32_t* label, float* prob, float* ll, void* ws, size_t ws_bytes) {
+  clear_error();
+  if (int rc = check_classify(m, t, d)) return rc;
+  if (d->B == 0) return TCS_OK;
+  if (!label) return fail(TCS_EINVAL, "classify: null label output");
+  const ClassifyLayout L = classify_layout(m, t, d, ws);
+  if (!ws || ws_bytes < L.total)
+    return fail(TCS_ECAPACITY, "classify: workspace %zu < %zu bytes", ws_bytes, L.total);
+  const tcs_dtype dt = m->dtype;
+  const int n_int = t->n_int, B = d->B, R = B * n_int;
+  const int qd = m->Hq * m->hd, kd = m->Hkv * m->hd;
+  const float scale = 1.0f / std::sqrt(float(m->hd));
+  int rc;
+  // node input block: a = RMSNorm(E[token]); q, k, v
+  if ((rc = launch_embed_rmsnorm(stream, dt, m->E, t->qnode, t->token, n_int, m->d, m->V, m->eps, L.a_nodes))) return rc;
+  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, qd, m->d, L.a_nodes, m->d, m->Wq, m->d, L.Qn, qd, nullptr))) return rc;
+  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, kd, m->d, L.a_nodes, m->d, m->Wk, m->d, L.Kn, kd, nullptr))) return rc;
+  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, kd, m->d, L.a_nodes, m->d, m->Wv, m->d, L.Vn, kd, nullptr))) return rc;
+  const void* Kd = d->Kd;
+  const void* Vd = d->Vd;
+  if (!Kd) {  // documents given as tokens: their k and v through the same input block
+    const int T = d->total_tokens;
+    if ((rc = launch_embed_rmsnorm(stream, dt, m->E, d->doc_tokens, nullptr, T, m->d, m->V, m->eps, L.a_doc))) return rc;
+    if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, T, kd, m->d, L.a_doc, m->d, m->Wk, m->d, L.Kd, kd, nullptr))) return rc;
+    if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, T, kd, m->d, L.a_doc, m->d, m->Wv, m->d, L.Vd, kd, nullptr))) return rc;
+    Kd = L.Kd;
+    Vd = L.Vd;
+  }
+  if ((rc = tree_attn_impl(stream, dt, B, n_int, m->Hq, m->Hkv, m->hd, L.Qn, L.Kn, L.Vn, Kd, Vd,
+                           d->doc_offsets, t->qparent, scale, L.O, L.anc))) return rc;
+  // y = x + O Wo^T ; h = RMSNorm(y)
+  GemmResid res{m->E, t->token, t->qnode, n_int};
+  if ((rc = launch_gemm_nt(stream, dt, GEMM_RESID, R, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d, &res))) return rc;
+  if ((rc = launch_rownorm(stream, dt, L.y, R, m->d, m->eps, L.h))) return rc;
+  if ((rc = launch_lmhead(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,
+                          m->W_scale, t->e_tok, t->e_qrow, t->e_child, t->n_nodes - 1, L.lse, L.lp,
+                          L.part))) return rc;
+  return launch_path_sum(stream, B, t, L.lp, ll ? ll : static_cast<float*>(L.ll), prob, label);
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal declarations shared by the libtcs translation units.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "tcs.h"
+
+namespace tcs {
+
+// Thread-local error message; returns `code` so callers can `return fail(...)`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// Sub-allocator over a caller workspace: hands out 256-byte aligned slices.
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+  template <typename T>
+  T* take(size_t count) {
+    size_t off = used;
+    used = align_up(used + count * sizeof(T));
+    return base ? reinterpret_cast<T*>(base + off) : nullptr;
+  }
+};
+
+inline size_t dtype_bytes(tcs_dtype t) { return t == TCS_F32 ? 4 : t == TCS_BF16 ? 2 : 1; }
+
+// ---- kernel launchers (each returns TCS_OK or TCS_EHIP) ------------------
+
+// a[r] = RMSNorm(E[tok(r)]), tok(r) = idx2 ? idx2[idx[r]] : idx[r]; a row whose
+// token is outside [0, V) is written as NaN.
+int launch_embed_rmsnorm(void* stream, tcs_dtype dt, const void* E, const int32_t* idx,
+                         const int32_t* idx2, int32_t n, int32_t d, int32_t V, float eps, void* out);
+
+// h[r] = RMSNorm(y[r]) for fp32 y [n, d], written in dtype dt.
+int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, float eps,
+                   void* out);
+
+// C[m, n] = sum_k A[m, k] * B[n, k].  Epilogues:
+//   STORE: C stored in dtype dt (rounded) with leading dimension ldc.
+//   RESID: C + E[tok(row)] stored as fp32, tok(row) = token[qnode[row % n_int]].
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1 };
+struct GemmResid {
+  const void* E;
+  const int32_t* token;
+  const int32_t* qnode;
+  int32_t n_int;
+};
+int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N, int32_t K,
+                   const void* A, int32_t lda, const void* B, int32_t ldb, void* C, int32_t ldc,
+                   const GemmResid* resid);
+
+// Output head, see tcs_lmhead_lse_gather.  `part` holds n_tiles * R float2 partials.
+int lmhead_n_tiles(tcs_dtype h_dtype, int32_t V);
+int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                  int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
+                  const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
+                  const int32_t* e_child, int32_t n_edges, float* lse, float* lp, void* part);
+
+// Tree attention pieces.
+int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32_t Hkv,
+                    int32_t hd, const void* Qn, const void* Kn, const void* Vn,
+                    const int32_t* qparent, float scale, float* anc_ml, float* anc_o);
+int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq,
+                    int32_t Hkv, int32_t hd, const void* Qn, const void* Kd, const void* Vd,
+                    const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
+                    float scale, void* O);
+
+int launch_path_sum(void* stream, int32_t B, const tcs_trie_dev* trie, const float* lp,
+                    float* ll, float* prob, int32_t* label);
+
+}  // namespace tcs
