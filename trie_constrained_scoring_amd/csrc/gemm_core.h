@@ -12,6 +12,8 @@
 // k values; the result lane l holds D[4*(l/16) + i][l%16] in element i.
 #pragma once
 
+#include <type_traits>
+
 #include "tcs_device.h"
 
 namespace tcs {
@@ -55,7 +57,15 @@ __device__ __forceinline__ void tile_coords(int nbm, int nbn, int& mt, int& nt) 
 }
 
 // Main loop.  A: bf16 [M, lda]; B: bf16 [N, ldb] or (B_FP8) E4M3 bytes [N, ldb].
-// Rows of A or B beyond M / N read as zero.  K % 64 == 0.
+// K % 64 == 0.  Rows of A or B at or beyond M / N read as zero.  A tile's rows
+// must span fewer than 2^31 bytes.
+//
+// Software pipeline, one barrier per K tile:
+//   [global loads of tile t+1] [LDS reads of step 1 of tile t  | MFMAs of step 0]
+//   [stores of tile t+1 to the other LDS buffer] barrier
+//   [LDS reads of step 0 of tile t+1 | MFMAs of step 1 of tile t]
+// so every LDS fragment read is in flight under a block of MFMAs, and the global
+// loads have a whole block of MFMAs to land.
 template <int BM, int BN, int WM, int WN, bool B_FP8>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int lda,
                                               const void* __restrict__ Bv, int ldb, int M, int N,
@@ -74,39 +84,34 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[S::A_CHUNKS];
   constexpr int RB = B_FP8 ? S::B8_CHUNKS : S::B_CHUNKS;
+  uint4 ra[S::A_CHUNKS];
   uint4 rb[RB];
-
+  // Buffer resources over this tile's rows: the hardware bounds check returns
+  // zeros past the last valid row, and each chunk differs from the previous one by
+  // a uniform byte stride, so only one per-thread offset register is needed.
+  constexpr uint32_t RSRC_W3 = 0x00020000u;  // gfx9-family raw buffer descriptor word 3
+  const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + (size_t)m0 * lda), 0, a_rows * lda * 2, RSRC_W3);
+  constexpr int B_ES = B_FP8 ? 1 : 2;  // bytes per B element
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(Bv) + (size_t)n0 * ldb * B_ES), 0,
+      b_rows * ldb * B_ES, RSRC_W3);
+  const int voffA = ((tid >> 3) * lda + (tid & 7) * 8) * 2;
+  const int strideA = (S::NT / 8) * lda * 2;
+  const int voffB = B_FP8 ? ((tid >> 2) * ldb + (tid & 3) * 16) : ((tid >> 3) * ldb + (tid & 7) * 8) * 2;
+  const int strideB = B_FP8 ? (S::NT / 4) * ldb : (S::NT / 8) * ldb * 2;
   auto load_stage = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < S::A_CHUNKS; ++i) {
-      const int c = tid + i * S::NT;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int gr = m0 + row;
-      ra[i] = gr < M ? *reinterpret_cast<const uint4*>(A + (size_t)gr * lda + k0 + col)
-                     : uint4{0, 0, 0, 0};
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(rsA, voffA, k0 * 2 + i * strideA, 0);
+      ra[i] = *reinterpret_cast<uint4*>(&v);
     }
-    if constexpr (B_FP8) {
-      const uint8_t* B = static_cast<const uint8_t*>(Bv);
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int c = tid + i * S::NT;
-        const int row = c >> 2, col = (c & 3) * 16;
-        const int gr = n0 + row;
-        rb[i] = gr < N ? *reinterpret_cast<const uint4*>(B + (size_t)gr * ldb + k0 + col)
-                       : uint4{0, 0, 0, 0};
-      }
-    } else {
-      const uint16_t* B = static_cast<const uint16_t*>(Bv);
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int c = tid + i * S::NT;
-        const int row = c >> 3, col = (c & 7) * 8;
-        const int gr = n0 + row;
-        rb[i] = gr < N ? *reinterpret_cast<const uint4*>(B + (size_t)gr * ldb + k0 + col)
-                       : uint4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < RB; ++i) {
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(rsB, voffB, k0 * B_ES + i * strideB, 0);
+      rb[i] = *reinterpret_cast<uint4*>(&v);
     }
   };
   auto store_stage = [&](int buf) {
@@ -115,8 +120,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 #pragma unroll
     for (int i = 0; i < S::A_CHUNKS; ++i) {
       const int c = tid + i * S::NT;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(a + row * GEMM_LDK + col) = ra[i];
+      *reinterpret_cast<uint4*>(a + (c >> 3) * GEMM_LDK + (c & 7) * 8) = ra[i];
     }
     if constexpr (B_FP8) {
 #pragma unroll
@@ -137,44 +141,237 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const int c = tid + i * S::NT;
-        const int row = c >> 3, col = (c & 7) * 8;
-        *reinterpret_cast<uint4*>(b + row * GEMM_LDK + col) = rb[i];
+        *reinterpret_cast<uint4*>(b + (c >> 3) * GEMM_LDK + (c & 7) * 8) = rb[i];
       }
     }
   };
+  bf16x8 fa[2][S::MB], fb[2][S::NB];
+  auto read_frags = [&](int buf, int kk, bf16x8 (&xa)[S::MB], bf16x8 (&xb)[S::NB]) {
+    const uint16_t* a = sA + buf * BM * GEMM_LDK;
+    const uint16_t* b = sB + buf * BN * GEMM_LDK;
+    const int kof = kk * 32 + (lane >> 4) * 8;
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+      xa[i] = *reinterpret_cast<const bf16x8*>(a + (wm * S::TM + i * 16 + (lane & 15)) * GEMM_LDK + kof);
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j)
+      xb[j] = *reinterpret_cast<const bf16x8*>(b + (wn * S::TN + j * 16 + (lane & 15)) * GEMM_LDK + kof);
+  };
+  auto mfma_block = [&](const bf16x8 (&xa)[S::MB], const bf16x8 (&xb)[S::NB]) {
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < S::NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NFRAG = S::MB + S::NB;
+  constexpr int NMFMA = S::MB * S::NB;
 
   const int nk = K / GEMM_BK;
   load_stage(0);
   store_stage(0);
   __syncthreads();
+  read_frags(0, 0, fa[0], fb[0]);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_stage((kt + 1) * GEMM_BK);
-    const uint16_t* a = sA + cur * BM * GEMM_LDK;
-    const uint16_t* b = sB + cur * BN * GEMM_LDK;
+    const int knext = min(kt + 1, nk - 1) * GEMM_BK;
+    load_stage(knext);
+    read_frags(cur, 1, fa[1], fb[1]);
+    mfma_block(fa[0], fb[0]);
+    // interleave: global loads and LDS reads spread across the MFMAs
 #pragma unroll
-    for (int kk = 0; kk < GEMM_BK / 32; ++kk) {
-      const int kof = kk * 32 + (lane >> 4) * 8;
-      bf16x8 fa[S::MB], fb[S::NB];
-#pragma unroll
-      for (int i = 0; i < S::MB; ++i) {
-        const int row = wm * S::TM + i * 16 + (lane & 15);
-        fa[i] = *reinterpret_cast<const bf16x8*>(a + row * GEMM_LDK + kof);
-      }
-#pragma unroll
-      for (int j = 0; j < S::NB; ++j) {
-        const int col = wn * S::TN + j * 16 + (lane & 15);
-        fb[j] = *reinterpret_cast<const bf16x8*>(b + col * GEMM_LDK + kof);
-      }
-#pragma unroll
-      for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-        for (int j = 0; j < S::NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NMFMA / NFRAG, 0);  // MFMA
     }
-    if (kt + 1 < nk) store_stage(cur ^ 1);
+    store_stage(cur ^ 1);
     __syncthreads();
+    read_frags(cur ^ 1, 0, fa[0], fb[0]);
+    mfma_block(fa[1], fb[1]);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMFMA / NFRAG, 0);
+    }
   }
+  __syncthreads();  // LDS is free for the caller's epilogue
+}
+
+
+// ---------------------------------------------------------------------------
+// 256 x 256 main loop fed by the buffer unit straight into LDS (bf16 A and B),
+// used by the output head.
+//
+// K advances in tiles of 64: each operand row contributes 128 contiguous bytes per
+// tile, so every L1->L2 request is a full 128-byte line (measured on MI355X: about
+// 1.8x the per-CU bandwidth of 64-byte requests).  Two 64 KB LDS stages: tile t+1
+// is loaded (buffer_load_dwordx4 ... lds, no register staging) while the matrix
+// cores work on tile t.  In a stage, the eight 16-byte chunks of row r sit at
+// positions chunk ^ swz(r), which spreads the rows read by each group of lanes
+// over distinct LDS banks.  Fragments are double-buffered across the four k-steps
+// of a tile; one barrier per tile.
+constexpr int DMA_BK = 64;
+constexpr int DMA_STAGE_BYTES = 2 * 256 * DMA_BK * 2;  // A + B tiles, bf16: 64 KB
+constexpr int DMA_HALF = 256 * DMA_BK * 2;             // one operand: 32 KB
+
+__device__ __forceinline__ int dma_swz(int r) { return (r ^ (r >> 3)) & 7; }  // r in [0, 16)
+
+#define TCS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with one counter and the others left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+struct DmaLds {
+  uint8_t* st[2];
+};
+
+__device__ __forceinline__ void gemm256_mainloop_dma(const uint16_t* __restrict__ A, int lda,
+                                                     const uint16_t* __restrict__ B, int ldb,
+                                                     int M, int N, int K, int m0, int n0,
+                                                     const DmaLds& L, f32x16 (&acc)[4][4]) {
+  // 4 waves as 2 x 2, each a 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16
+  // blocks.  32x32x16 operand layout (lane l): A row l%32 / B column l%32 with the
+  // 8 k values starting at 8*(l/32); result lane l holds rows 8j + 4(l/32) + i of
+  // column l%32 in element 4j + i.
+  constexpr uint32_t RSRC_W3 = 0x00020000u;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int a_rows = min(256, M - m0), b_rows = min(256, N - n0);
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + (size_t)m0 * lda), 0, a_rows * lda * 2, RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B + (size_t)n0 * ldb), 0, b_rows * ldb * 2, RSRC_W3);
+  // Load j (0..7) of this wave fills LDS rows wave*64 + 8j .. +7 (1 KB): lane i
+  // writes row i/8, position i%8, which holds global chunk (i%8) ^ swz(row % 16);
+  // row % 16 = 8*(j&1) + i/8, so even and odd loads use two lane offsets.
+  const int lr = lane >> 3, lp = lane & 7;
+  const int offA0 = ((wave * 64 + lr) * lda + ((lp ^ dma_swz(lr)) * 8)) * 2;
+  const int offA1 = ((wave * 64 + lr) * lda + ((lp ^ dma_swz(lr + 8)) * 8)) * 2;
+  const int offB0 = ((wave * 64 + lr) * ldb + ((lp ^ dma_swz(lr)) * 8)) * 2;
+  const int offB1 = ((wave * 64 + lr) * ldb + ((lp ^ dma_swz(lr + 8)) * 8)) * 2;
+  const int rowstepA = 8 * lda * 2, rowstepB = 8 * ldb * 2;
+  auto issue = [&](uint8_t* st, int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, TCS_LDS(st + (wave * 64 + j * 8) * 128), 16,
+                                               (j & 1) ? offA1 : offA0, k0 * 2 + j * rowstepA, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, TCS_LDS(st + DMA_HALF + (wave * 64 + j * 8) * 128),
+                                               16, (j & 1) ? offB1 : offB0, k0 * 2 + j * rowstepB, 0, 0);
+  };
+  // fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32
+  int fo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    fo[ks] = (lane & 31) * 128 + (((2 * ks + (lane >> 5)) ^ dma_swz(lane & 15)) * 16);
+  bf16x8 fa[2][4], fb[2][4];
+  auto read_frags = [&](const uint8_t* st, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xa[i] = *reinterpret_cast<const bf16x8*>(st + (wm * 128 + i * 32) * 128 + fo[ks]);
+      xb[i] = *reinterpret_cast<const bf16x8*>(st + DMA_HALF + (wn * 128 + i * 32) * 128 + fo[ks]);
+    }
+  };
+  auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave_ds = [&]() {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    }
+  };
+
+  const int nk = K / DMA_BK;
+  issue(L.st[0], 0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(L.st[0], 0, fa[0], fb[0]);
+  auto tile = [&](auto C, int kt) {
+    constexpr int cur = decltype(C)::value;
+    const uint8_t* st = L.st[cur];
+    const bool more = kt + 1 < nk;
+    if (more) issue(L.st[cur ^ 1], (kt + 1) * DMA_BK);
+    read_frags(st, 1, fa[1], fb[1]);
+    mfma_step(fa[0], fb[0]);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+    read_frags(st, 2, fa[0], fb[0]);
+    mfma_step(fa[1], fb[1]);
+    interleave_ds();
+    read_frags(st, 3, fa[1], fb[1]);
+    mfma_step(fa[0], fb[0]);
+    interleave_ds();
+    if (more) {
+      wait_vmcnt<0>();      // this wave's loads of tile kt+1 have landed
+      wait_lgkmcnt0();      // and its reads of this stage are done
+      __builtin_amdgcn_s_barrier();
+      read_frags(L.st[cur ^ 1], 0, fa[0], fb[0]);
+    }
+    mfma_step(fa[1], fb[1]);
+    interleave_ds();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    tile(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) tile(std::integral_constant<int, 1>{}, kt + 1);
+  }
+  __syncthreads();  // all LDS reads done before the caller reuses LDS
+}
+
+// Output-head tile order: the 256 workgroups that run at once (one per CU) cover
+// a GM x GN block of tiles; each XCD (block i runs on XCD i % 8) takes an MX x NX
+// sub-block so its L2 serves both operands, and all XCDs share the block's other
+// operand through the MALL.  Returns false for slots past the matrix edge.
+__device__ __forceinline__ bool head_tile_coords(int nbm, int nbn, int& mt, int& nt) {
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = (bid >> 3) & 31, w = bid >> 8;
+  int MX, NX, GM, GN, m_local, n_local;
+  if (nbm >= 32) {          // XCDs split the rows: per XCD 4 x 8
+    MX = 4; NX = 8; GM = 32; GN = 8;
+    m_local = xcd * MX + slot % MX;
+    n_local = slot / MX;
+  } else {                  // XCDs split the columns: per XCD MX x (32/MX)
+    MX = nbm >= 16 ? 16 : nbm >= 8 ? 8 : nbm >= 4 ? 4 : nbm >= 2 ? 2 : 1;
+    NX = 32 / MX; GM = MX; GN = 8 * NX;
+    m_local = slot % MX;
+    n_local = xcd * NX + slot / MX;
+  }
+  const int nb_count = (nbn + GN - 1) / GN;
+  const int g = w / nb_count, nb = w % nb_count;
+  mt = g * GM + m_local;
+  nt = nb * GN + n_local;
+  return mt < nbm && nt < nbn;
+}
+
+__host__ __device__ inline int head_grid(int nbm, int nbn) {
+  int GM, GN;
+  if (nbm >= 32) { GM = 32; GN = 8; }
+  else {
+    const int MX = nbm >= 16 ? 16 : nbm >= 8 ? 8 : nbm >= 4 ? 4 : nbm >= 2 ? 2 : 1;
+    GM = MX; GN = 8 * (32 / MX);
+  }
+  return ((nbm + GM - 1) / GM) * ((nbn + GN - 1) / GN) * 256;
 }
 
 }  // namespace tcs

@@ -55,9 +55,7 @@ static int tree_attn_impl(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, 
   return launch_doc_attn(stream, dt, B, n_int, Hq, Hkv, hd, Qn, Kd, Vd, doc_offsets, ml, ao, scale, O);
 }
 
-static size_t lmhead_part_bytes(int32_t rows, int32_t V) {
-  return align_up(size_t(lmhead_n_tiles(TCS_BF16, V)) * size_t(rows) * 8);
-}
+static size_t lmhead_part_bytes(int32_t rows, int32_t V) { return lmhead_ws_bytes(rows, V); }
 
 }  // namespace tcs
 
