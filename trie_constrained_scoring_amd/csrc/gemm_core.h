@@ -204,15 +204,19 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 //
 // K advances in tiles of 64: each operand row contributes 128 contiguous bytes per
 // tile, so every L1->L2 request is a full 128-byte line (measured on MI355X: about
-// 1.8x the per-CU bandwidth of 64-byte requests).  Two 64 KB LDS stages: tile t+1
-// is loaded (buffer_load_dwordx4 ... lds, no register staging) while the matrix
-// cores work on tile t.  In a stage, the eight 16-byte chunks of row r sit at
-// positions chunk ^ swz(r), which spreads the rows read by each group of lanes
-// over distinct LDS banks.  Fragments are double-buffered across the four k-steps
-// of a tile; one barrier per tile.
+// 1.8x the per-CU bandwidth of 64-byte requests).  LDS is a ring of five 32 KB
+// slots, one operand tile each: A(t) lives in slot 2t mod 5 and B(t) in slot
+// 2t+1 mod 5, so while tile t is multiplied, B(t+1) and A(t+2) are in flight --
+// the A operand (the streamed weight matrix) gets two tiles of latency cover.
+// Slots are filled by buffer_load_dwordx4 ... lds (no register staging).  In a
+// slot, the eight 16-byte chunks of row r sit at positions chunk ^ swz(r mod 16),
+// which spreads the rows read by each group of lanes over distinct LDS banks.
+// Fragments are double-buffered across the four k-steps of a tile; one barrier
+// per tile.
 constexpr int DMA_BK = 64;
-constexpr int DMA_STAGE_BYTES = 2 * 256 * DMA_BK * 2;  // A + B tiles, bf16: 64 KB
-constexpr int DMA_HALF = 256 * DMA_BK * 2;             // one operand: 32 KB
+constexpr int DMA_SLOT_BYTES = 256 * DMA_BK * 2;  // one operand tile, bf16: 32 KB
+constexpr int DMA_SLOTS = 5;
+constexpr int DMA_LOADS_PER_OPERAND = 8;          // per wave (per thread) per tile
 
 __device__ __forceinline__ int dma_swz(int r) { return (r ^ (r >> 3)) & 7; }  // r in [0, 16)
 
@@ -226,7 +230,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 struct DmaLds {
-  uint8_t* st[2];
+  uint8_t* slot[DMA_SLOTS];
 };
 
 __device__ __forceinline__ void gemm256_mainloop_dma(const uint16_t* __restrict__ A, int lda,
@@ -252,24 +256,42 @@ __device__ __forceinline__ void gemm256_mainloop_dma(const uint16_t* __restrict_
       const_cast<uint16_t*>(A + (size_t)m0 * lda), 0, a_rows * lda * 2, RSRC_W3);
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(B + (size_t)n0 * ldb), 0, b_rows * ldb * 2, RSRC_W3);
-  // Load j (0..7) of this wave fills LDS rows wave*64 + 8j .. +7 (1 KB): lane i
+  // Zero-range resources: every access through them is out of range, so the
+  // loads issued for k-tiles past the end touch no memory.
+  const __amdgpu_buffer_rsrc_t rsA0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A), 0, 0, RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B), 0, 0, RSRC_W3);
+  // Load j (0..7) of this wave fills slot rows wave*64 + 8j .. +7 (1 KB): lane i
   // writes row i/8, position i%8, which holds global chunk (i%8) ^ swz(row % 16);
-  // row % 16 = 8*(j&1) + i/8, so even and odd loads use two lane offsets.
+  // row % 16 = 8*(j&1) + i/8.  Rows past the operand's end (ragged last tile) are
+  // clamped to its last row, so every address stays inside the operand; the
+  // epilogue discards those rows.  The k offset goes in the scalar offset.
   const int lr = lane >> 3, lp = lane & 7;
-  const int offA0 = ((wave * 64 + lr) * lda + ((lp ^ dma_swz(lr)) * 8)) * 2;
-  const int offA1 = ((wave * 64 + lr) * lda + ((lp ^ dma_swz(lr + 8)) * 8)) * 2;
-  const int offB0 = ((wave * 64 + lr) * ldb + ((lp ^ dma_swz(lr)) * 8)) * 2;
-  const int offB1 = ((wave * 64 + lr) * ldb + ((lp ^ dma_swz(lr + 8)) * 8)) * 2;
-  const int rowstepA = 8 * lda * 2, rowstepB = 8 * ldb * 2;
-  auto issue = [&](uint8_t* st, int k0) {
+  int voA[8], voB[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = wave * 64 + j * 8 + lr;
+    const int ch = (lp ^ dma_swz(lr + 8 * (j & 1))) * 8;
+    voA[j] = (min(row, a_rows - 1) * lda + ch) * 2;
+    voB[j] = (min(row, b_rows - 1) * ldb + ch) * 2;
+  }
+  const int nk = K / DMA_BK;
+  auto issueA = [&](uint8_t* sl, int kt) {
+    const __amdgpu_buffer_rsrc_t r = kt < nk ? rsA : rsA0;
+    const int so = (kt < nk ? kt : 0) * DMA_BK * 2;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, TCS_LDS(st + (wave * 64 + j * 8) * 128), 16,
-                                               (j & 1) ? offA1 : offA0, k0 * 2 + j * rowstepA, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCS_LDS(sl + (wave * 64 + j * 8) * 128), 16,
+                                               voA[j], so, 0, 0);
+  };
+  auto issueB = [&](uint8_t* sl, int kt) {
+    const __amdgpu_buffer_rsrc_t r = kt < nk ? rsB : rsB0;
+    const int so = (kt < nk ? kt : 0) * DMA_BK * 2;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, TCS_LDS(st + DMA_HALF + (wave * 64 + j * 8) * 128),
-                                               16, (j & 1) ? offB1 : offB0, k0 * 2 + j * rowstepB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCS_LDS(sl + (wave * 64 + j * 8) * 128), 16,
+                                               voB[j], so, 0, 0);
   };
   // fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32
   int fo[4];
@@ -277,11 +299,12 @@ __device__ __forceinline__ void gemm256_mainloop_dma(const uint16_t* __restrict_
   for (int ks = 0; ks < 4; ++ks)
     fo[ks] = (lane & 31) * 128 + (((2 * ks + (lane >> 5)) ^ dma_swz(lane & 15)) * 16);
   bf16x8 fa[2][4], fb[2][4];
-  auto read_frags = [&](const uint8_t* st, int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+  auto read_frags = [&](const uint8_t* sa, const uint8_t* sb, int ks, bf16x8 (&xa)[4],
+                        bf16x8 (&xb)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xa[i] = *reinterpret_cast<const bf16x8*>(st + (wm * 128 + i * 32) * 128 + fo[ks]);
-      xb[i] = *reinterpret_cast<const bf16x8*>(st + DMA_HALF + (wn * 128 + i * 32) * 128 + fo[ks]);
+      xa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + fo[ks]);
+      xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
     }
   };
   auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
@@ -299,17 +322,23 @@ __device__ __forceinline__ void gemm256_mainloop_dma(const uint16_t* __restrict_
     }
   };
 
-  const int nk = K / DMA_BK;
-  issue(L.st[0], 0);
-  wait_vmcnt<0>();
+  // prologue: A(0), B(0), A(1)
+  issueA(L.slot[0], 0);
+  issueB(L.slot[1], 0);
+  issueA(L.slot[2], 1);
+  wait_vmcnt<DMA_LOADS_PER_OPERAND>();
   __builtin_amdgcn_s_barrier();
-  read_frags(L.st[0], 0, fa[0], fb[0]);
-  auto tile = [&](auto C, int kt) {
-    constexpr int cur = decltype(C)::value;
-    const uint8_t* st = L.st[cur];
-    const bool more = kt + 1 < nk;
-    if (more) issue(L.st[cur ^ 1], (kt + 1) * DMA_BK);
-    read_frags(st, 1, fa[1], fb[1]);
+  read_frags(L.slot[0], L.slot[1], 0, fa[0], fb[0]);
+  // tile t (t mod 5 = U): A(t) in slot 2U mod 5, B(t) in slot 2U+1 mod 5
+  auto tile = [&](auto Uc, int kt) {
+    constexpr int U = decltype(Uc)::value;
+    constexpr int sA = (2 * U) % 5, sB = (2 * U + 1) % 5;
+    constexpr int sB1 = (2 * U + 3) % 5, sA1 = (2 * U + 2) % 5, sA2 = (2 * U + 4) % 5;
+    const uint8_t* pa = L.slot[sA];
+    const uint8_t* pb = L.slot[sB];
+    issueB(L.slot[sB1], kt + 1);
+    issueA(L.slot[sA2], kt + 2);
+    read_frags(pa, pb, 1, fa[1], fb[1]);
     mfma_step(fa[0], fb[0]);
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
@@ -317,25 +346,29 @@ __device__ __forceinline__ void gemm256_mainloop_dma(const uint16_t* __restrict_
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
-    read_frags(st, 2, fa[0], fb[0]);
+    read_frags(pa, pb, 2, fa[0], fb[0]);
     mfma_step(fa[1], fb[1]);
     interleave_ds();
-    read_frags(st, 3, fa[1], fb[1]);
+    read_frags(pa, pb, 3, fa[1], fb[1]);
     mfma_step(fa[0], fb[0]);
     interleave_ds();
-    if (more) {
-      wait_vmcnt<0>();      // this wave's loads of tile kt+1 have landed
-      wait_lgkmcnt0();      // and its reads of this stage are done
-      __builtin_amdgcn_s_barrier();
-      read_frags(L.st[cur ^ 1], 0, fa[0], fb[0]);
-    }
+    // A(t+1) and B(t+1) of this wave have landed (only A(t+2) may be in flight),
+    // and this wave's reads of the current slots are done
+    wait_vmcnt<DMA_LOADS_PER_OPERAND>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    read_frags(L.slot[sA1], L.slot[sB1], 0, fa[0], fb[0]);
     mfma_step(fa[1], fb[1]);
     interleave_ds();
   };
-  for (int kt = 0; kt < nk; kt += 2) {
+  for (int kt = 0; kt < nk; kt += 5) {
     tile(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < nk) tile(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 < nk) tile(std::integral_constant<int, 2>{}, kt + 2);
+    if (kt + 3 < nk) tile(std::integral_constant<int, 3>{}, kt + 3);
+    if (kt + 4 < nk) tile(std::integral_constant<int, 4>{}, kt + 4);
   }
+  wait_vmcnt<0>();
   __syncthreads();  // all LDS reads done before the caller reuses LDS
 }
 

@@ -44,13 +44,14 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const uint16_t* __restrict__ W, const int32_t* __restrict__ seg, const int32_t* __restrict__ e_tok,
     const int32_t* __restrict__ e_qrow, const int32_t* __restrict__ e_child, float* __restrict__ raw,
     float2* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint8_t st0[DMA_STAGE_BYTES], st1[DMA_STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t st0[DMA_SLOT_BYTES], st1[DMA_SLOT_BYTES],
+      st2[DMA_SLOT_BYTES], st3[DMA_SLOT_BYTES], st4[DMA_SLOT_BYTES];
   const int n_rt = (R + 255) / 256, n_vt = (V + HEAD_BN - 1) / HEAD_BN;
   int rt, vt;
   if (!head_tile_coords(n_rt, n_vt, rt, vt)) return;
   const int r0 = rt * 256, v0 = vt * HEAD_BN;
   f32x16 acc[4][4];
-  const DmaLds L{{st0, st1}};
+  const DmaLds L{{st0, st1, st2, st3, st4}};
   gemm256_mainloop_dma(W, d, h, d, V, R, d, v0, r0, L, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
