@@ -1,7 +1,8 @@
 """Throughput of the trie_tree label-scoring pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
-                    [--no-cpu-baseline] [--no-lmhead-timing]
+                    [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain copy of known size, for HBM counters
 
 One step is one ``tcs_classify`` call over one batch of synthetic documents: the
 node input block, ancestor-masked tree attention, output projection + RMSNorm,
@@ -12,15 +13,22 @@ The trie itself is built once per label set on the host (timed separately).
 Prints ONE JSON line.  ``value`` is documents classified per second at the
 primary workload (default: the running-example shape, 10 labels); the 255- and
 5000-label workloads are reported under ``at_labels``.  ``roofline`` is for the
-dominant kernel (the output head), timed with HIP events on the stream it runs
-on; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-workload on this host's cores.
+dominant kernel (the output head): after the timed steps, the same steps run
+again with the head launches bracketed by HIP events on the stream they run on
+(the library's tcs_timing_enable hook), and achieved = algorithmic FLOP per
+launch / mean launch duration.  ``traffic`` is the HBM bytes per launch measured by the FETCH_SIZE and
+WRITE_SIZE counters (scaled by what they read for a plain copy of known size),
+read from the profile summary under profiles/ while the kernel's sources still
+hash to the value recorded there, else null.  ``cpu_baseline`` times the fp64
+oracle on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +40,32 @@ sys.path.insert(0, ROOT)
 METRIC = "documents classified/sec at 10/255/5000 labels; % of HBM/MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+HEAD_SOURCES = ["gemm_core.h", "k_lmhead.hip", "tcs_device.h"]
+HEAD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lmhead_bf16_running_example_B64_traffic.md")
+COPY_BYTES = 1 << 30
+
+
+def head_source_hash() -> str:
+    """sha256 over the sources the output-head kernel is compiled from."""
+    h = hashlib.sha256()
+    for f in HEAD_SOURCES:
+        with open(os.path.join(ROOT, "trie_constrained_scoring_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per head launch from the committed counter summary, or None when
+    the summary is missing or was taken on other kernel sources."""
+    try:
+        text = open(HEAD_TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != head_source_hash():
+        return None
+    return float(m_val.group(1))
 
 
 def log(*a):
@@ -63,6 +97,11 @@ def setup(cid: int):
 
 
 def run_steps(S, steps, warmup):
+    """Seconds per step over `steps` timed steps (after `warmup` untimed ones), then
+    the mean duration (ms) of the head and document-attention kernel launches over a
+    second pass of `steps` identical steps in which the library brackets those
+    launches with HIP events on their stream (recording events costs host time per
+    launch, so that pass is kept out of the throughput figure)."""
     import torch
     import trie_constrained_scoring_amd as tcs
 
@@ -75,36 +114,36 @@ def run_steps(S, steps, warmup):
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    sec = (time.perf_counter() - t0) / steps
+    tcs.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name, timer in (("head", tcs.TCS_TIMER_HEAD), ("doc_attn", tcs.TCS_TIMER_DOC_ATTN)):
+        ms, n = tcs.timing_read(timer)
+        kern[name] = ms / n if n else None
+    tcs.timing_enable(False)
+    return sec, kern
 
 
-def time_lmhead(S, reps):
-    """Average duration of the output-head entry point (MFMA GEMM + LSE/gather
-    epilogue + finalize) with HIP events on the stream it is launched on, fed the
-    hidden states of the same workload's shape."""
-    import torch
-    import trie_constrained_scoring_amd as tcs
+def head_flops(S):
+    """Algorithmic FLOP of one head launch: 2 * rows * d * V, rows = B * internal nodes."""
+    R = S["docs"].B * S["td"].trie.n_int
+    return 2.0 * R * S["cfg"].d * S["cfg"].V, R
+
+
+def doc_attn_bytes(S):
+    """Algorithmic HBM bytes of one document-attention launch: every document's K
+    and V once, the node queries and the per-trie ancestor partials once, the node
+    outputs once (bf16 storage, fp32 partials)."""
     cfg, td = S["cfg"], S["td"]
-    R = S["docs"].B * td.trie.n_int
-    g = torch.Generator(device="cuda").manual_seed(0)
-    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    h = torch.randn((R, cfg.d), device="cuda", generator=g).to(dt)
-    W, Ws = S["model"].t["W"], S["model"].t["W_scale"]
-    lse = torch.empty(R, dtype=torch.float32, device="cuda")
-    lp = torch.empty((S["docs"].B, td.trie.n_nodes), dtype=torch.float32, device="cuda")
-    ws = torch.empty(tcs.lmhead_workspace_bytes(R, cfg.V), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    for _ in range(2):
-        tcs.lmhead_lse_gather(h, W, td, S["docs"].B, w_scale=Ws, lse=lse, lp=lp, ws=ws, stream=stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        tcs.lmhead_lse_gather(h, W, td, S["docs"].B, w_scale=Ws, lse=lse, lp=lp, ws=ws, stream=stream)
-    e1.record(stream)
-    e1.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    flops = 2.0 * R * cfg.d * cfg.V
-    return ms, flops, R
+    B, n_int, T = S["docs"].B, td.trie.n_int, int(S["inp"]["doc_offsets"][-1])
+    kv = 2 * T * cfg.Hkv * cfg.hd * 2
+    q = n_int * cfg.Hq * cfg.hd * 2
+    anc = n_int * cfg.Hq * (cfg.hd + 2) * 4
+    o = B * n_int * cfg.Hq * cfg.hd * 2
+    return kv + q + anc + o
 
 
 def cpu_baseline(S, budget_s=15.0):
@@ -136,7 +175,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--extra", default="3,4", help="other label-set sizes to report (config ids)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-lmhead-timing", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (3 launches) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); documents shard across GPUs "
@@ -146,10 +186,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return
 
     S = setup(args.config)
     cfg, trie = S["cfg"], S["trie"]
-    sec = run_steps(S, args.steps, args.warmup)
+    sec, kern = run_steps(S, args.steps, args.warmup)
     B = S["docs"].B
     value = B / sec
     res = {
@@ -167,15 +215,22 @@ def main():
         "trie_nodes_per_s": round(B * trie.n_nodes / sec, 1),
         "trie_build_ms": round(S["trie_ms"], 3),
     }
-    if not args.no_lmhead_timing:
-        ms, flops, R = time_lmhead(S, reps=max(3, args.steps))
-        ach = flops / (ms * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "lmhead_lse_gather (bf16 MFMA GEMM + LSE/gather epilogue + finalize)",
-                           "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                           "traffic": None, "rows": R, "flops_per_launch": flops,
-                           "ms_per_launch": round(ms, 4)}
-        res["lmhead_share_of_step"] = round(ms / (sec * 1e3), 4)
+    flops, R = head_flops(S)
+    ach = flops / (kern["head"] * 1e-3) / 1e12
+    kname = "lmhead_fp8_kernel" if cfg.head == "fp8" else "lmhead_bf16_kernel"
+    traffic = recorded_traffic() if cfg.id == 2 and cfg.head == "same" else None
+    res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                       "traffic": traffic, "kernel": kname, "rows": R,
+                       "flops_per_launch": flops, "ms_per_launch": round(kern["head"], 4),
+                       "timing": "HIP events around each head launch of a second pass of the same steps"}
+    res["head_share_of_step"] = round(kern["head"] / (sec * 1e3), 4)
+    if kern["doc_attn"]:
+        by = doc_attn_bytes(S)
+        gbs = by / (kern["doc_attn"] * 1e-3) / 1e9
+        res["doc_attn_roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                    "bytes_per_launch": by, "ms_per_launch": round(kern["doc_attn"], 4)}
     extra = {}
     for c in [int(x) for x in args.extra.split(",") if x.strip()]:
         if c == args.config:
@@ -183,14 +238,18 @@ def main():
         del S
         torch.cuda.empty_cache()
         S2 = setup(c)
-        s2 = run_steps(S2, max(3, args.steps // 2), 2)
-        e = {"docs_per_s": round(S2["docs"].B / s2, 2), "ms_per_step": round(s2 * 1e3, 3),
+        s2, k2 = run_steps(S2, max(3, args.steps // 2), 2)
+        f2, _ = head_flops(S2)
+        tf = f2 / (k2["head"] * 1e-3) / 1e12
+        e = {"config": c, "docs_per_s": round(S2["docs"].B / s2, 2), "ms_per_step": round(s2 * 1e3, 3),
              "labels": S2["trie"].n_labels, "trie_nodes": S2["trie"].n_nodes,
-             "trie_nodes_per_s": round(S2["docs"].B * S2["trie"].n_nodes / s2, 1)}
-        if not args.no_lmhead_timing:
-            ms, flops, R = time_lmhead(S2, reps=5)
-            e["lmhead_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
-            e["lmhead_frac_bf16_peak"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+             "trie_nodes_per_s": round(S2["docs"].B * S2["trie"].n_nodes / s2, 1),
+             "head_tflops": round(tf, 2), "head_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+             "head_ms": round(k2["head"], 4)}
+        if k2["doc_attn"]:
+            gbs = doc_attn_bytes(S2) / (k2["doc_attn"] * 1e-3) / 1e9
+            e["doc_attn_ms"] = round(k2["doc_attn"], 4)
+            e["doc_attn_gbs"] = round(gbs, 1)
         extra[str(S2["trie"].n_labels)] = e
         S = S2
     if extra:

@@ -246,6 +246,33 @@ int tcs_classify(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* 
                  const tcs_docs* docs, int32_t* label, float* prob, float* ll, void* ws,
                  size_t ws_bytes);
 
+/* ----------------------------------------------------------- measurement ---- */
+/*
+ * Per-kernel timing, for measuring a kernel against its roofline from inside a
+ * timed run (not part of the scoring method).  While timing is enabled, every
+ * launch of a timed kernel is bracketed by two HIP events recorded on the stream
+ * it is launched on; tcs_timing_read waits for the recorded events of one timer,
+ * returns their summed duration and launch count, and forgets them.
+ *
+ *   tcs_timing_enable(1)  starts recording (events are created on demand and
+ *                         pooled; they are HIP events, not device memory).
+ *   tcs_timing_enable(0)  stops recording, drops unread records and destroys the
+ *                         pooled events.
+ *   tcs_timing_read(timer, &ms, &n)  ms = total milliseconds, n = launches since
+ *                         the last read; TCS_EINVAL for an unknown timer or NULL
+ *                         outputs, TCS_EHIP if an event query fails.
+ *
+ * Launches from several host threads at once are recorded safely, but a timer's
+ * total then mixes their streams.
+ */
+typedef enum {
+  TCS_TIMER_HEAD = 0,     /* the output-head GEMM + LSE/gather kernel (any dtype) */
+  TCS_TIMER_DOC_ATTN = 1, /* the document part of the tree attention */
+  TCS_TIMER_COUNT = 2
+} tcs_timer;
+int tcs_timing_enable(int enable);
+int tcs_timing_read(int timer, double* total_ms, int32_t* launches);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* tcs_last_error(void);
 

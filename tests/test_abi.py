@@ -108,3 +108,14 @@ def test_null_pointer_errors_without_gpu():
         tcs.TCS_EUNSUPPORTED
     assert lib.tcs_path_sum_softmax(None, 1, None, None, None, None, None) == tcs.TCS_EINVAL
     assert lib.tcs_classify(None, None, None, None, None, None, None, None, 0) == tcs.TCS_EINVAL
+
+
+def test_timing_api_without_launches():
+    tcs.timing_enable(True)
+    assert tcs.timing_read(tcs.TCS_TIMER_HEAD) == (0.0, 0)
+    assert tcs.timing_read(tcs.TCS_TIMER_DOC_ATTN) == (0.0, 0)
+    with pytest.raises(tcs.TcsError):
+        tcs.timing_read(7)
+    lib = tcs.lib()
+    assert lib.tcs_timing_read(0, None, None) == tcs.TCS_EINVAL
+    tcs.timing_enable(False)

@@ -93,6 +93,8 @@ def lib():
                                                    C.POINTER(tcs_docs)]
         L.tcs_classify.argtypes = [vp, C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
                                    C.POINTER(tcs_docs), vp, vp, vp, vp, sz]
+        L.tcs_timing_enable.argtypes = [C.c_int]
+        L.tcs_timing_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i32)]
         _lib_handle = L
     return _lib_handle
 
@@ -104,6 +106,23 @@ def _check(rc):
 
 def version() -> str:
     return lib().tcs_version().decode()
+
+
+TCS_TIMER_HEAD, TCS_TIMER_DOC_ATTN = 0, 1
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (or stop and reset) HIP-event timing of the head and document-attention
+    kernels inside the library (tcs_timing_enable)."""
+    _check(lib().tcs_timing_enable(1 if on else 0))
+
+
+def timing_read(timer: int):
+    """(total milliseconds, launches) recorded for `timer` since the last read
+    (tcs_timing_read); waits for the recorded events."""
+    ms, n = C.c_double(), C.c_int32()
+    _check(lib().tcs_timing_read(int(timer), C.byref(ms), C.byref(n)))
+    return ms.value, n.value
 
 
 # ------------------------------------------------------------------ torch glue

@@ -399,6 +399,7 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
   auto kd = static_cast<const uint16_t*>(Kd);
   auto vd = static_cast<const uint16_t*>(Vd);
   auto o = static_cast<uint16_t*>(O);
+  timer_begin(TCS_TIMER_DOC_ATTN, stream);
   if (rows <= 64) {
     const long grid = long(B) * Hkv * ((rows + 31) / 32);
     if (hd == 128)
@@ -412,6 +413,7 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
     else
       doc_attn_mfma_kernel<64, 4, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   }
+  timer_end(TCS_TIMER_DOC_ATTN, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "doc_attn: %s", hipGetErrorString(e));
   return TCS_OK;

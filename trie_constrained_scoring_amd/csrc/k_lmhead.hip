@@ -346,6 +346,7 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
   float2* p = cv.take<float2>(size_t(n_tiles) * R);
   int32_t* seg = cv.take<int32_t>(n_tiles + 1);
   head_seg_kernel<<<(n_tiles + 256) / 256, 256, 0, s>>>(n_tiles, e_tok, n_edges, seg);
+  timer_begin(TCS_TIMER_HEAD, stream);
   if (h_dtype == TCS_BF16) {
     if (d % 64 != 0) return fail(TCS_EUNSUPPORTED, "lmhead: d=%d is not a multiple of 64", d);
     const int n_rt = (R + 255) / 256;
@@ -364,6 +365,7 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
                                            static_cast<const float*>(W), seg, e_tok, e_qrow, e_child,
                                            lp, p);
   }
+  timer_end(TCS_TIMER_HEAD, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "lmhead: %s", hipGetErrorString(e));
   if (R < 16384)

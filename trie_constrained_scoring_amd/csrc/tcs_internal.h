@@ -29,6 +29,10 @@ struct Carve {
 
 inline size_t dtype_bytes(tcs_dtype t) { return t == TCS_F32 ? 4 : t == TCS_BF16 ? 2 : 1; }
 
+// Kernel timing (tcs_timing_enable): both calls are no-ops while timing is off.
+void timer_begin(int timer, void* stream);
+void timer_end(int timer, void* stream);
+
 // ---- kernel launchers (each returns TCS_OK or TCS_EHIP) ------------------
 
 // a[r] = RMSNorm(E[tok(r)]), tok(r) = idx2 ? idx2[idx[r]] : idx[r]; a row whose
