@@ -172,10 +172,12 @@ int tcs_tree_attn(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, 
  *   h           [R, d];  W [V, d]
  *   edges       trie->e_tok / e_qrow / e_child, sorted by token
  *   lse         [R] fp32 out;  lp [B, n_nodes] fp32 out
- *   ws          workspace of tcs_lmhead_workspace_bytes(...) bytes
+ *   ws          workspace of tcs_lmhead_workspace_bytes(h_dtype, B, n_int, n_nodes, d, V)
+ *               bytes (0 for invalid sizes)
  * bf16 heads need d % 64 == 0.
  */
-size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, int32_t rows, int32_t V);
+size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
+                                  int32_t d, int32_t V);
 int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
                           int32_t n_int, int32_t n_nodes, int32_t d, int32_t V, const void* h,
                           const void* W, const float* w_scale, const int32_t* e_tok,

@@ -84,7 +84,7 @@ def lib():
         L.tcs_tree_attn.argtypes = [vp, C.c_int, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                     C.c_float, vp, vp, sz]
         L.tcs_lmhead_workspace_bytes.restype = sz
-        L.tcs_lmhead_workspace_bytes.argtypes = [C.c_int, i32, i32]
+        L.tcs_lmhead_workspace_bytes.argtypes = [C.c_int, i32, i32, i32, i32, i32]
         L.tcs_lmhead_lse_gather.argtypes = [vp, C.c_int, C.c_int, i32, i32, i32, i32, i32, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, sz]
         L.tcs_path_sum_softmax.argtypes = [vp, i32, C.POINTER(tcs_trie_dev), vp, vp, vp, vp]
@@ -268,8 +268,11 @@ def tree_attn(Qn, Kn, Vn, Kd, Vd, doc_offsets, qparent, scale, O=None, ws=None, 
     return O
 
 
-def lmhead_workspace_bytes(rows, V, h_dtype=TCS_BF16) -> int:
-    return int(lib().tcs_lmhead_workspace_bytes(h_dtype, rows, V))
+def lmhead_workspace_bytes(B, n_int, n_nodes, d, V, h_dtype=TCS_BF16) -> int:
+    n = int(lib().tcs_lmhead_workspace_bytes(h_dtype, B, n_int, n_nodes, d, V))
+    if n == 0:
+        _check(TCS_EINVAL)
+    return n
 
 
 def lmhead_lse_gather(h, W, trie_dev: TrieDevice, B, w_scale=None, lse=None, lp=None, ws=None,
@@ -289,7 +292,7 @@ def lmhead_lse_gather(h, W, trie_dev: TrieDevice, B, w_scale=None, lse=None, lp=
         lse = torch.empty(R, dtype=torch.float32, device=h.device)
     if lp is None:
         lp = torch.empty((B, t.n_nodes), dtype=torch.float32, device=h.device)
-    need = lmhead_workspace_bytes(R, V, _dtype_code(h))
+    need = lmhead_workspace_bytes(B, t.n_int, t.n_nodes, d, V, _dtype_code(h))
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     _need_cuda(h, W, w_scale, lse, lp, ws)

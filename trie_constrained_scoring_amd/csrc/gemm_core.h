@@ -199,20 +199,14 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 
 
 // ---------------------------------------------------------------------------
-// 256 x 256 main loop fed by the buffer unit straight into LDS (bf16 A and B),
-// used by the output head.
+// Pieces of the LDS-DMA pipeline used by the output head (k_lmhead.hip).
 //
 // K advances in tiles of 64: each operand row contributes 128 contiguous bytes per
 // tile, so every L1->L2 request is a full 128-byte line (measured on MI355X: about
-// 1.8x the per-CU bandwidth of 64-byte requests).  LDS is a ring of five 32 KB
-// slots, one operand tile each: A(t) lives in slot 2t mod 5 and B(t) in slot
-// 2t+1 mod 5, so while tile t is multiplied, B(t+1) and A(t+2) are in flight --
-// the A operand (the streamed weight matrix) gets two tiles of latency cover.
-// Slots are filled by buffer_load_dwordx4 ... lds (no register staging).  In a
-// slot, the eight 16-byte chunks of row r sit at positions chunk ^ swz(r mod 16),
-// which spreads the rows read by each group of lanes over distinct LDS banks.
-// Fragments are double-buffered across the four k-steps of a tile; one barrier
-// per tile.
+// 1.8x the per-CU bandwidth of 64-byte requests).  A slot holds one 256-row operand
+// tile (32 KB); in a slot, the eight 16-byte chunks of row r sit at positions
+// chunk ^ swz(r mod 16), which spreads the rows read by each group of lanes over
+// distinct LDS banks.
 constexpr int DMA_BK = 64;
 constexpr int DMA_SLOT_BYTES = 256 * DMA_BK * 2;  // one operand tile, bf16: 32 KB
 constexpr int DMA_SLOTS = 5;
@@ -229,155 +223,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-struct DmaLds {
-  uint8_t* slot[DMA_SLOTS];
-};
-
-__device__ __forceinline__ void gemm256_mainloop_dma(const uint16_t* __restrict__ A, int lda,
-                                                     const uint16_t* __restrict__ B, int ldb,
-                                                     int M, int N, int K, int m0, int n0,
-                                                     const DmaLds& L, f32x16 (&acc)[4][4]) {
-  // 4 waves as 2 x 2, each a 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16
-  // blocks.  32x32x16 operand layout (lane l): A row l%32 / B column l%32 with the
-  // 8 k values starting at 8*(l/32); result lane l holds rows 8j + 4(l/32) + i of
-  // column l%32 in element 4j + i.
-  constexpr uint32_t RSRC_W3 = 0x00020000u;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int a_rows = min(256, M - m0), b_rows = min(256, N - n0);
-  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A + (size_t)m0 * lda), 0, a_rows * lda * 2, RSRC_W3);
-  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(B + (size_t)n0 * ldb), 0, b_rows * ldb * 2, RSRC_W3);
-  // Zero-range resources: every access through them is out of range, so the
-  // loads issued for k-tiles past the end touch no memory.
-  const __amdgpu_buffer_rsrc_t rsA0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A), 0, 0, RSRC_W3);
-  const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(B), 0, 0, RSRC_W3);
-  // Load j (0..7) of this wave fills slot rows wave*64 + 8j .. +7 (1 KB): lane i
-  // writes row i/8, position i%8, which holds global chunk (i%8) ^ swz(row % 16);
-  // row % 16 = 8*(j&1) + i/8.  Rows past the operand's end (ragged last tile) are
-  // clamped to its last row, so every address stays inside the operand; the
-  // epilogue discards those rows.  The k offset goes in the scalar offset.
-  const int lr = lane >> 3, lp = lane & 7;
-  int voA[8], voB[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = wave * 64 + j * 8 + lr;
-    const int ch = (lp ^ dma_swz(lr + 8 * (j & 1))) * 8;
-    voA[j] = (min(row, a_rows - 1) * lda + ch) * 2;
-    voB[j] = (min(row, b_rows - 1) * ldb + ch) * 2;
-  }
-  const int nk = K / DMA_BK;
-  auto issueA = [&](uint8_t* sl, int kt) {
-    const __amdgpu_buffer_rsrc_t r = kt < nk ? rsA : rsA0;
-    const int so = (kt < nk ? kt : 0) * DMA_BK * 2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCS_LDS(sl + (wave * 64 + j * 8) * 128), 16,
-                                               voA[j], so, 0, 0);
-  };
-  auto issueB = [&](uint8_t* sl, int kt) {
-    const __amdgpu_buffer_rsrc_t r = kt < nk ? rsB : rsB0;
-    const int so = (kt < nk ? kt : 0) * DMA_BK * 2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCS_LDS(sl + (wave * 64 + j * 8) * 128), 16,
-                                               voB[j], so, 0, 0);
-  };
-  // fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32
-  int fo[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    fo[ks] = (lane & 31) * 128 + (((2 * ks + (lane >> 5)) ^ dma_swz(lane & 15)) * 16);
-  bf16x8 fa[2][4], fb[2][4];
-  auto read_frags = [&](const uint8_t* sa, const uint8_t* sb, int ks, bf16x8 (&xa)[4],
-                        bf16x8 (&xb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + fo[ks]);
-      xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
-    }
-  };
-  auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
-  };
-  auto interleave_ds = [&]() {
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-    }
-  };
-
-  // prologue: A(0), B(0), A(1)
-  issueA(L.slot[0], 0);
-  issueB(L.slot[1], 0);
-  issueA(L.slot[2], 1);
-  wait_vmcnt<DMA_LOADS_PER_OPERAND>();
-  __builtin_amdgcn_s_barrier();
-  read_frags(L.slot[0], L.slot[1], 0, fa[0], fb[0]);
-  // tile t (t mod 5 = U): A(t) in slot 2U mod 5, B(t) in slot 2U+1 mod 5
-  auto tile = [&](auto Uc, int kt) {
-    constexpr int U = decltype(Uc)::value;
-    constexpr int sA = (2 * U) % 5, sB = (2 * U + 1) % 5;
-    constexpr int sB1 = (2 * U + 3) % 5, sA1 = (2 * U + 2) % 5, sA2 = (2 * U + 4) % 5;
-    const uint8_t* pa = L.slot[sA];
-    const uint8_t* pb = L.slot[sB];
-    issueB(L.slot[sB1], kt + 1);
-    issueA(L.slot[sA2], kt + 2);
-    read_frags(pa, pb, 1, fa[1], fb[1]);
-    mfma_step(fa[0], fb[0]);
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    }
-    read_frags(pa, pb, 2, fa[0], fb[0]);
-    mfma_step(fa[1], fb[1]);
-    interleave_ds();
-    read_frags(pa, pb, 3, fa[1], fb[1]);
-    mfma_step(fa[0], fb[0]);
-    interleave_ds();
-    // A(t+1) and B(t+1) of this wave have landed (only A(t+2) may be in flight),
-    // and this wave's reads of the current slots are done
-    wait_vmcnt<DMA_LOADS_PER_OPERAND>();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    read_frags(L.slot[sA1], L.slot[sB1], 0, fa[0], fb[0]);
-    mfma_step(fa[1], fb[1]);
-    interleave_ds();
-  };
-  for (int kt = 0; kt < nk; kt += 5) {
-    tile(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < nk) tile(std::integral_constant<int, 1>{}, kt + 1);
-    if (kt + 2 < nk) tile(std::integral_constant<int, 2>{}, kt + 2);
-    if (kt + 3 < nk) tile(std::integral_constant<int, 3>{}, kt + 3);
-    if (kt + 4 < nk) tile(std::integral_constant<int, 4>{}, kt + 4);
-  }
-  wait_vmcnt<0>();
-  __syncthreads();  // all LDS reads done before the caller reuses LDS
-}
-
-// Output-head tile order: the 256 workgroups that run at once (one per CU) cover
-// a GM x GN block of tiles; each XCD (block i runs on XCD i % 8) takes an MX x NX
-// sub-block so its L2 serves both operands, and all XCDs share the block's other
-// operand through the MALL.  Returns false for slots past the matrix edge.
-__device__ __forceinline__ bool head_tile_coords(int nbm, int nbn, int& mt, int& nt) {
-  const int bid = blockIdx.x;
+// Output-head tile order: tile slot `bid` = 256 w + b is the w-th tile of the
+// persistent workgroup b (one per CU; b runs on XCD b % 8).  The 256 slots of one
+// round w cover a GM x GN block of tiles; each XCD takes an MX x NX sub-block so
+// its L2 serves both operands, and all XCDs share the block's other operand
+// through the MALL.  Returns false for slots past the matrix edge.
+__device__ __forceinline__ bool head_tile_coords(int bid, int nbm, int nbn, int& mt, int& nt) {
   const int xcd = bid & 7, slot = (bid >> 3) & 31, w = bid >> 8;
   int MX, NX, GM, GN, m_local, n_local;
   if (nbm >= 32) {          // XCDs split the rows: per XCD 4 x 8

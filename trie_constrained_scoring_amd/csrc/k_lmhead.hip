@@ -9,14 +9,16 @@
 // them.  A finalize pass merges the partials into lse and turns the gathered
 // logits into token log-probabilities.
 #include <cstdio>
+#include <utility>
 
 #include "gemm_core.h"
 #include "tcs_internal.h"
 
 namespace tcs {
 
-constexpr int HEAD_BN = 256;  // vocabulary entries per tile: also the partial granularity
-constexpr int GATHER_CHUNK = 4096;
+constexpr int HEAD_BN = 256;   // vocabulary entries per tile
+constexpr int HEAD_SEG = 128;  // vocabulary entries per edge segment (and bf16 partial)
+constexpr int HEAD_WGS = 256;  // persistent bf16 head: one workgroup per CU
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t* __restrict__ a, int n, int key) {
   int lo = 0, hi = n;
@@ -27,122 +29,369 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* __restrict__ a, in
   return lo;
 }
 
-// seg[t] = first edge whose token is >= t * 256 (edges are sorted by token), so
-// vocabulary tile t owns edges [seg[t], seg[t+1]).
-__global__ void head_seg_kernel(int n_tiles, const int32_t* __restrict__ e_tok, int n_edges,
-                                int32_t* __restrict__ seg) {
+// seg[t] = first edge whose token is >= t * 128 (edges are sorted by token), so
+// vocabulary half-tile t (128 entries) owns edges [seg[t], seg[t+1]) and tile t
+// (256 entries) owns [seg[2t], seg[2t+2]).
+// Also clears the bf16 head's zero block (n_zero 16-byte words).
+__global__ void head_prep_kernel(int n_seg, const int32_t* __restrict__ e_tok, int n_edges,
+                                 int32_t* __restrict__ seg, uint4* __restrict__ zero, int n_zero) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t <= n_tiles) seg[t] = t == n_tiles ? n_edges : lower_bound_i32(e_tok, n_edges, t * HEAD_BN);
+  if (t <= n_seg) seg[t] = t == n_seg ? n_edges : lower_bound_i32(e_tok, n_edges, t * HEAD_SEG);
+  if (t < n_zero) zero[t] = uint4{0u, 0u, 0u, 0u};
 }
 
-// bf16 head.  The tile is computed transposed, logits^T[v][r] = W[v] . h[r], so in
-// the 32x32 MFMA result layout each lane holds one hidden row (column l%32 of a
-// block) and 16 vocabulary entries per block: the row's max / sum-exp is reduced
-// in-lane plus one exchange with lane l^32, then across the two vocab-side waves.
+// Gather lists of the bf16 head.  The logit of child c of query row q in document
+// b sits in tile (vocabulary half-tile tok/128, row tile r/256), r = b n_int + q,
+// in accumulator element t = 16 im + e of the lane whose half is hh and whose row
+// is r % 256.  Each (edge, document) pair is pushed on its tile half's list:
+// rec = {next, output index b*n_nodes + c, t | hh << 6 | (r % 256) << 7, 0}.
+__global__ void head_list_init_kernel(int n_keys, int32_t* __restrict__ list_head) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n_keys) list_head[t] = -1;
+}
+
+__global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
+                                      const int32_t* __restrict__ e_tok,
+                                      const int32_t* __restrict__ e_qrow,
+                                      const int32_t* __restrict__ e_child, int n_edges,
+                                      int32_t* __restrict__ list_head, int4* __restrict__ rec) {
+  const long i = long(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= long(n_edges) * B) return;
+  const int e = int(i / B), b = int(i % B);
+  const int tok = e_tok[e];
+  const int r = b * n_int + e_qrow[e];
+  const int off = tok & (HEAD_SEG - 1);  // 32 im + 8 (e>>2) + 4 hh + (e&3)
+  const int t = (off >> 5) * 16 + (((off >> 3) & 3) << 2) + (off & 3);
+  const int hh = (off >> 2) & 1;
+  const int key = (tok / HEAD_SEG) * n_rt + r / 256;
+  const int next = atomicExch(&list_head[key], int(i));
+  rec[i] = int4{next, b * n_nodes + e_child[e], t | (hh << 6) | ((r & 255) << 7), 0};
+}
+
+// ---------------------------------------------------------------------------
+// bf16 head.  Persistent: one workgroup per CU walks its own sequence of 256 x 256
+// tiles (head_tile_coords), and the LDS ring of five 32 KB operand slots runs on
+// across tile boundaries, so the first k-tiles of the next tile load while the
+// current one finishes and while its epilogue runs.
+//
+// Global k-step g (over all tiles of this workgroup) keeps W's k-tile in slot
+// 2g mod 5 and h's in slot 2g+1 mod 5; while step g is multiplied, h(g+1) and
+// W(g+2) are in flight, so the streamed weight matrix gets two steps of latency
+// cover.  One barrier per step.  Each operand is read by its own DMA stream that
+// steps from the last k-tile of one tile to the first of the next; loads past the
+// last tile go through a zero-range buffer resource and touch no memory.
+//
+// The tile is computed transposed, logits^T[v][r] = W[v] . h[r]: in the 32x32
+// MFMA result layout each lane holds one hidden row (column l%32 of a block) and
+// 16 vocabulary entries per block, so a row's max / sum-exp over the wave's 128
+// entries is reduced in-lane plus one exchange with lane l^32 and written as one
+// partial per (row, vocabulary half-tile).  The epilogue touches no LDS: child
+// logits are picked out of the accumulators by a scalar walk over the half-tile's
+// edges.
+
+// One operand k-tile of this wave into an LDS slot: load j (0..7) fills slot rows
+// wave*64 + 8j .. +7 (1 KB), lane i writing 16 bytes at row i/8, position i%8;
+// `vo` holds each load's lane byte offset, `k` the k-tile (scalar offset).
+__device__ __forceinline__ void head_issue(const uint16_t* base, int bytes, int k, uint8_t* sl,
+                                           int wave, const int (&vo)[DMA_LOADS_PER_OPERAND]) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
+  const int so = k * DMA_BK * 2;
+#pragma unroll
+  for (int j = 0; j < DMA_LOADS_PER_OPERAND; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 64 + j * 8) * 128), 16, vo[j],
+                                             so, 0, 0);
+}
+
+// v[jn] = acc[t / 16][jn][t % 16] for a wave-uniform t in [0, 64): a binary
+// select tree on the six bits of t (63 selects per jn, six lane masks), so the
+// accumulators are only read in place.
+__device__ __forceinline__ void head_pick(int t, const f32x16 (&acc)[4][4], float (&v)[4]) {
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn) {
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int c0 = 2 * i, c1 = 2 * i + 1;
+      x[i] = (t & 1) ? acc[c1 / 16][jn][c1 % 16] : acc[c0 / 16][jn][c0 % 16];
+    }
+#pragma unroll
+    for (int lvl = 1, n = 16; n >= 1; ++lvl, n >>= 1)
+#pragma unroll
+      for (int i = 0; i < n; ++i) x[i] = ((t >> lvl) & 1) ? x[2 * i + 1] : x[2 * i];
+    v[jn] = x[0];
+  }
+}
+
+// Max and sum of exp of each of the lane's four rows (jn) over its 64 entries
+// plus the partner lane's (l ^ 32); entries at or past `vlim` are excluded when
+// MASK.  Rows are innermost, so each entry's mask is used as soon as it is made.
+// exp2 is the hardware instruction: arguments are <= 0, and terms below 2^-126
+// of the row maximum, which it flushes, are far below fp32 resolution of the sum.
+template <bool MASK>
+__device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][4], int vlim,
+                                              float2 (&out)[4]) {
+  constexpr float LOG2E = 1.4426950408889634f;
+  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int im = 0; im < 4; ++im)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool ok = !MASK || 32 * im + 8 * (e >> 2) + (e & 3) < vlim;
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) m[jn] = fmaxf(m[jn], ok ? acc[im][jn][e] : -INFINITY);
+    }
+  float ml[4], sum[4];
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn) {
+    m[jn] = fmaxf(m[jn], __shfl_xor(m[jn], 32, 64));
+    ml[jn] = m[jn] == -INFINITY ? 0.f : m[jn] * LOG2E;
+    sum[jn] = 0.f;
+  }
+#pragma unroll
+  for (int im = 0; im < 4; ++im)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool ok = !MASK || 32 * im + 8 * (e >> 2) + (e & 3) < vlim;
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const float x = __builtin_amdgcn_exp2f(fmaf(acc[im][jn][e], LOG2E, -ml[jn]));
+        sum[jn] += ok ? x : 0.f;
+      }
+    }
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn) out[jn] = float2{m[jn], sum[jn] + __shfl_xor(sum[jn], 32, 64)};
+}
+
 __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
-    int R, int V, int d, int n_int, int n_nodes, const uint16_t* __restrict__ h,
-    const uint16_t* __restrict__ W, const int32_t* __restrict__ seg, const int32_t* __restrict__ e_tok,
-    const int32_t* __restrict__ e_qrow, const int32_t* __restrict__ e_child, float* __restrict__ raw,
-    float2* __restrict__ part) {
+    int R, int V, int d, const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ list_head, const int4* __restrict__ rec, float* __restrict__ raw,
+    float2* __restrict__ part, const uint16_t* __restrict__ zero, int rounds_per_wg) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[DMA_SLOT_BYTES], st1[DMA_SLOT_BYTES],
       st2[DMA_SLOT_BYTES], st3[DMA_SLOT_BYTES], st4[DMA_SLOT_BYTES];
+  uint8_t* const slot[DMA_SLOTS] = {st0, st1, st2, st3, st4};
+  constexpr uint32_t RSRC_W3 = 0x00020000u;
   const int n_rt = (R + 255) / 256, n_vt = (V + HEAD_BN - 1) / HEAD_BN;
-  int rt, vt;
-  if (!head_tile_coords(n_rt, n_vt, rt, vt)) return;
-  const int r0 = rt * 256, v0 = vt * HEAD_BN;
-  f32x16 acc[4][4];
-  const DmaLds L{{st0, st1, st2, st3, st4}};
-  gemm256_mainloop_dma(W, d, h, d, V, R, d, v0, r0, L, acc);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // workgroup g takes rounds [w_lo, rounds) of slot g % 256: a bounded run of
+  // consecutive rounds, so the workgroups that share operand tiles in an XCD's L2
+  // stay within a few rounds of each other
+  const int w_lo = int(blockIdx.x) / HEAD_WGS * rounds_per_wg;
+  const int rounds = min(head_grid(n_rt, n_vt) / HEAD_WGS, w_lo + rounds_per_wg);
+  const int bslot = int(blockIdx.x) % HEAD_WGS;
+  const int nk = d / DMA_BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  // acc[im][jn][e]: vocabulary v0 + vlane + 32 im + 8 (e>>2) + (e&3); hidden row
-  // r0 + rloc + 32 jn
-  const int vlane = wm * 128 + 4 * (lane >> 5);
-  const int rloc = wn * 128 + (lane & 31);
 
-  if (v0 + HEAD_BN > V) {  // last vocabulary tile: entries past V drop out
+  auto coords = [&](int w, int& rt, int& vt) __attribute__((always_inline)) {
+    return head_tile_coords(w * HEAD_WGS + bslot, n_rt, n_vt, rt, vt);
+  };
+  auto next_valid = [&](int w) __attribute__((always_inline)) {
+    int rt, vt;
+    while (w < rounds && !coords(w, rt, vt)) ++w;
+    return w;
+  };
+
+  // Rows of W and h that tile w reads, as (base, bytes) of a buffer resource;
+  // zero bytes past the last tile.  Rows past an operand's end lie outside the
+  // resource's range, so the buffer unit drops those loads; the epilogue discards
+  // those rows.  (Resources are built at each issue from these plain values, which
+  // keeps them in scalar registers.)
+  struct Span {
+    const uint16_t* wb;
+    const uint16_t* hb;
+    int wn, hn;
+  };
+  auto span = [&](int w) __attribute__((always_inline)) {
+    int rt, vt;
+    if (w < rounds && coords(w, rt, vt))
+      return Span{W + (size_t)vt * 256 * d, h + (size_t)rt * 256 * d,
+                  min(256, V - vt * 256) * d * 2, min(256, R - rt * 256) * d * 2};
+    return Span{W, h, 0, 0};
+  };
+
+  // Load j (0..7) of this wave fills slot rows wave*64 + 8j .. +7 (1 KB): lane i
+  // writes row i/8, position i%8, which holds global chunk (i%8) ^ swz(row % 16);
+  // row % 16 = 8*(j&1) + i/8.  The k offset goes in the scalar offset.
+  const int lr = lane >> 3, lp = lane & 7;
+  int vo[DMA_LOADS_PER_OPERAND];
 #pragma unroll
-    for (int im = 0; im < 4; ++im)
+  for (int j = 0; j < DMA_LOADS_PER_OPERAND; ++j)
+    vo[j] = ((wave * 64 + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
+  int w = next_valid(w_lo);
+  if (w >= rounds) return;
+  // A tile runs nk5 = nk rounded up to a multiple of 5 steps, so every tile starts
+  // at ring position 0.  Steps past nk load both operands from `zero` (256 x d
+  // zeros), so they run the same code and add nothing.  Loads run up to two steps
+  // ahead, so they reach into the next tile at most.
+  const int nk5 = (nk + 4) / 5 * 5;
+  const int zbytes = nk5 == nk ? 0 : 256 * d * 2;
+  // this tile's spans and the step to the next tile's (kept as differences, so a
+  // load's operand is this tile's value plus a selected offset)
+  Span s0 = span(w);
+  int w1 = next_valid(w + 1);
+  Span s1 = span(w1);
+  long dwb = s1.wb - s0.wb, dhb = s1.hb - s0.hb;
+  int dwn = s1.wn - s0.wn, dhn = s1.hn - s0.hn;
+  // padded position q (steps past this tile's start) -> (operand rows, k-tile)
+  auto issue_w = [&](int q, uint8_t* sl) __attribute__((always_inline)) {
+    const bool nxt = q >= nk5;
+    const int k = nxt ? q - nk5 : q;
+    const bool pad = k >= nk;
+    const uint16_t* b = s0.wb + (nxt ? dwb : 0);
+    const int n = s0.wn + (nxt ? dwn : 0);
+    head_issue(pad ? zero : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
+  };
+  auto issue_h = [&](int q, uint8_t* sl) __attribute__((always_inline)) {
+    const bool nxt = q >= nk5;
+    const int k = nxt ? q - nk5 : q;
+    const bool pad = k >= nk;
+    const uint16_t* b = s0.hb + (nxt ? dhb : 0);
+    const int n = s0.hn + (nxt ? dhn : 0);
+    head_issue(pad ? zero : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
+  };
+
+  // fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32
+  int fo[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const bool ok = v0 + vlane + im * 32 + 8 * (e >> 2) + (e & 3) < V;
+  for (int ks = 0; ks < 4; ++ks)
+    fo[ks] = (lane & 31) * 128 + (((2 * ks + (lane >> 5)) ^ dma_swz(lane & 15)) * 16);
+  bf16x8 fa[2][4], fb[2][4];
+  f32x16 acc[4][4];
+  auto read_frags = [&](const uint8_t* sa, const uint8_t* sb, int ks, bf16x8 (&xa)[4],
+                        bf16x8 (&xb)[4]) {
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) acc[im][jn][e] = ok ? acc[im][jn][e] : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      xa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + fo[ks]);
+      xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
+    }
+  };
+  auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave_ds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    }
+  };
+  // global k-step with ring position U: W in slot 2U mod 5, h in slot 2U+1 mod 5
+  // LAST: the tile's final step, which leaves the next tile's first fragments to
+  // be read after the epilogue (fewer registers live across it)
+  auto step = [&](auto Uc, int kt, auto Lc) __attribute__((always_inline)) {
+    constexpr int U = decltype(Uc)::value;
+    constexpr bool LAST = decltype(Lc)::value;
+    constexpr int sA = (2 * U) % 5, sB = (2 * U + 1) % 5;
+    constexpr int sA1 = (2 * U + 2) % 5, sB1 = (2 * U + 3) % 5, sA2 = (2 * U + 4) % 5;
+    issue_h(kt + 1, slot[sB1]);  // h(g+1)
+    issue_w(kt + 2, slot[sA2]);  // W(g+2)
+    {
+      read_frags(slot[sA], slot[sB], 1, fa[1], fb[1]);
+      mfma_step(fa[0], fb[0]);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
-  }
+      read_frags(slot[sA], slot[sB], 2, fa[0], fb[0]);
+      mfma_step(fa[1], fb[1]);
+      interleave_ds();
+      read_frags(slot[sA], slot[sB], 3, fa[1], fb[1]);
+      mfma_step(fa[0], fb[0]);
+      interleave_ds();
+    }
+    // W(g+1) and h(g+1) of this wave have landed (only W(g+2) may be in flight),
+    // and this wave's reads of the current slots are done
+    wait_vmcnt<DMA_LOADS_PER_OPERAND>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    if constexpr (!LAST) read_frags(slot[sA1], slot[sB1], 0, fa[0], fb[0]);
+    mfma_step(fa[1], fb[1]);
+    if constexpr (!LAST) interleave_ds();
+  };
 
-  // child-token gather: this tile's edges [e_lo, e_hi) are indexed in LDS by
-  // vocabulary offset; each lane looks up its 64 vocabulary entries and copies the
-  // logit of each of its hidden rows whose query row matches an edge.
-  const int e_lo = seg[vt], e_hi = seg[vt + 1];
-  if (e_lo < e_hi) {
-    int* vmap = reinterpret_cast<int*>(st0);
-    int rq[4], rb[4];
+  // prologue: W(0), h(0), W(1)
+  issue_w(0, slot[0]);
+  issue_h(0, slot[1]);
+  issue_w(1, slot[2]);
+  wait_vmcnt<DMA_LOADS_PER_OPERAND>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
+
+  const int vhalf = wm * 128 + 4 * (lane >> 5);  // + 32 im + 8 (e>>2) + (e&3)
+  const int rloc = wn * 128 + (lane & 31);       // + 32 jn
+  for (; w < rounds;) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    using F = std::false_type;
+    int kt = 0;
+    for (; kt + 5 < nk5; kt += 5) {
+      step(std::integral_constant<int, 0>{}, kt, F{});
+      step(std::integral_constant<int, 1>{}, kt + 1, F{});
+      step(std::integral_constant<int, 2>{}, kt + 2, F{});
+      step(std::integral_constant<int, 3>{}, kt + 3, F{});
+      step(std::integral_constant<int, 4>{}, kt + 4, F{});
+    }
+    step(std::integral_constant<int, 0>{}, kt, F{});
+    step(std::integral_constant<int, 1>{}, kt + 1, F{});
+    step(std::integral_constant<int, 2>{}, kt + 2, F{});
+    step(std::integral_constant<int, 3>{}, kt + 3, F{});
+    step(std::integral_constant<int, 4>{}, kt + 4, std::true_type{});
+
+    // ---- epilogue of tile w (no LDS: the ring keeps loading the next tile) ----
+    int rt, vt;
+    coords(w, rt, vt);
+    const int r0 = rt * 256, v0 = vt * HEAD_BN;
+    // acc[im][jn][e]: vocabulary v0 + vhalf + 32 im + 8 (e>>2) + (e&3); hidden row
+    // r0 + rloc + 32 jn
+    // entries at or past V (last vocabulary tile) drop out of the row sums; the
+    // accumulators are only read from here on
+    const int vlim = V - v0 - vhalf;  // entry (im, e) is valid iff 32 im + 8 (e>>2) + (e&3) < vlim
+    // child-token gather: walk this half-tile's list for this row tile (scalar)
+    for (int k = list_head[(2 * vt + wm) * n_rt + rt]; k >= 0;) {
+      const int4 q = rec[k];
+      const int t = q.z & 63, hh = (q.z >> 6) & 1, rit = q.z >> 7;
+      if ((rit >> 7) == wn) {  // row r0 + rit is in this wave's half of the rows
+        float v[4];
+        head_pick(t, acc, v);
+        const int jn = (rit >> 5) & 3;
+        const float x = jn == 0 ? v[0] : jn == 1 ? v[1] : jn == 2 ? v[2] : v[3];
+        if (lane == (rit & 31) + 32 * hh) raw[q.y] = x;
+      }
+      k = q.x;
+    }
+    // per hidden row: max and sum of exp over this wave's 128 vocabulary entries
+    // (only the last vocabulary tile has entries at or past V)
+    float2 ms[4];
+    if (v0 + HEAD_BN <= V) head_rows_lse<false>(acc, vlim, ms);
+    else head_rows_lse<true>(acc, vlim, ms);
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
       const int r = r0 + rloc + 32 * jn;
-      rq[jn] = r < R ? r % n_int : -1;
-      rb[jn] = r / n_int;
+      if (lane < 32 && r < R) part[(size_t)(2 * vt + wm) * R + r] = ms[jn];
     }
-    for (int c0 = e_lo; c0 < e_hi; c0 += GATHER_CHUNK) {
-      const int c1 = min(e_hi, c0 + GATHER_CHUNK);
-      vmap[threadIdx.x] = -1;
-      __syncthreads();
-      for (int k = c0 + threadIdx.x; k < c1; k += 256) {
-        const int tok = e_tok[k];
-        if (k == c0 || e_tok[k - 1] != tok) vmap[tok - v0] = k;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int im = 0; im < 4; ++im)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int vo = vlane + im * 32 + 8 * (e >> 2) + (e & 3);
-          int k = vmap[vo];
-          if (k >= 0) {
-            for (; k < c1 && e_tok[k] == v0 + vo; ++k) {
-              const int q = e_qrow[k], c = e_child[k];
-#pragma unroll
-              for (int jn = 0; jn < 4; ++jn)
-                if (rq[jn] == q) raw[(size_t)rb[jn] * n_nodes + c] = acc[im][jn][e];
-            }
-          }
-        }
-      __syncthreads();
-    }
+    // the next tile's W(0) and h(0) are in slots 0 and 1 (landed at the last barrier)
+    read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
+    w = w1;
+    w1 = next_valid(w1 + 1);
+    s0 = s1;
+    s1 = span(w1);
+    dwb = s1.wb - s0.wb;
+    dhb = s1.hb - s0.hb;
+    dwn = s1.wn - s0.wn;
+    dhn = s1.hn - s0.hn;
   }
-
-  // per hidden row: max and sum of exp over this wave's 128 vocabulary entries
-  float2* red = reinterpret_cast<float2*>(st1);  // [2 vocab halves][256 rows]
-  constexpr float LOG2E = 1.4426950408889634f;
-#pragma unroll
-  for (int jn = 0; jn < 4; ++jn) {
-    float m = acc[0][jn][0];
-#pragma unroll
-    for (int im = 0; im < 4; ++im)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, acc[im][jn][e]);
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    float s = 0.f;
-    if (m != -INFINITY) {
-      const float ml = m * LOG2E;
-#pragma unroll
-      for (int im = 0; im < 4; ++im)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s += exp2f(fmaf(acc[im][jn][e], LOG2E, -ml));
-    }
-    s += __shfl_xor(s, 32, 64);
-    if (lane < 32) red[wm * 256 + rloc + 32 * jn] = float2{m, s};
-  }
-  __syncthreads();
-  {
-    const int t = threadIdx.x;
-    float2 a = red[t];
-    const float2 b = red[256 + t];
-    lse_merge(a.x, a.y, b.x, b.y);
-    if (r0 + t < R) part[(size_t)vt * R + r0 + t] = a;
-  }
+  wait_vmcnt<0>();  // loads past the last tile: nothing may still target LDS at exit
 }
 
 // fp8-weight head (E4M3 codes converted to bf16 while staging; per-row fp32 scale
@@ -176,7 +425,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_fp8_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = ok ? acc[i][j][r] * sc : -INFINITY;
   }
-  const int e_lo = seg[nt], e_hi = seg[nt + 1];
+  const int e_lo = seg[2 * nt], e_hi = seg[2 * nt + 2];
   if (e_lo < e_hi) {
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) {
@@ -251,7 +500,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
     }
     __syncthreads();
   }
-  for (int e = seg[nt]; e < seg[nt + 1]; ++e) {
+  for (int e = seg[2 * nt]; e < seg[2 * nt + 2]; ++e) {
     if (e_tok[e] != col) continue;
     const int q = e_qrow[e], c = e_child[e];
 #pragma unroll
@@ -276,30 +525,31 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(
   }
 }
 
-// Merge the per-tile (max, sum exp) partials of each row into lse.  Many rows:
+// Merge the (max, sum exp) partials of each row (one per vocabulary tile, or per
+// half-tile for the bf16 head) into lse.  Many rows:
 // one thread per row, reads coalesced across rows.  Few rows: one wave per row,
 // lanes stride over the tiles, then a shuffle merge.
-__global__ void lse_finalize_kernel(int R, int n_tiles, const float2* __restrict__ part,
+__global__ void lse_finalize_kernel(int R, int n_parts, const float2* __restrict__ part,
                                     float* __restrict__ lse) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= R) return;
   float m = -INFINITY, s = 0.f;
 #pragma unroll 8
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = 0; t < n_parts; ++t) {
     const float2 p = part[(size_t)t * R + r];
     lse_merge(m, s, p.x, p.y);
   }
   lse[r] = m + logf(s);
 }
 
-__global__ __launch_bounds__(256) void lse_finalize_wave_kernel(int R, int n_tiles,
+__global__ __launch_bounds__(256) void lse_finalize_wave_kernel(int R, int n_parts,
                                                                 const float2* __restrict__ part,
                                                                 float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   float m = -INFINITY, s = 0.f;
-  for (int t = lane; t < n_tiles; t += 64) {
+  for (int t = lane; t < n_parts; t += 64) {
     const float2 p = part[(size_t)t * R + r];
     lse_merge(m, s, p.x, p.y);
   }
@@ -329,9 +579,30 @@ __global__ void lp_finalize_kernel(int B, int n_int, int n_nodes, const int32_t*
 
 int lmhead_n_tiles(tcs_dtype /*h_dtype*/, int32_t V) { return (V + HEAD_BN - 1) / HEAD_BN; }
 
-size_t lmhead_ws_bytes(int32_t rows, int32_t V) {
-  const int n_tiles = lmhead_n_tiles(TCS_BF16, V);
-  return align_up(size_t(n_tiles) * size_t(rows) * 8) + align_up(size_t(n_tiles + 1) * 4);
+// Rounds of 256 tiles per bf16-head workgroup: long enough to amortise the
+// prologue and launch, short enough that the workgroups sharing operand tiles in
+// an XCD's L2 stay within a few rounds of each other (measured on MI355X: 8 is
+// 9% faster than a fully persistent grid on a 97k-row head, 2% faster than 1).
+static int head_rounds_per_wg(int /*rounds*/) { return 8; }
+
+// 256 x d zeros for the padding steps of the bf16 head when d / 64 is not a
+// multiple of 5 (else none).
+static size_t head_zero_bytes(int32_t d) {
+  const int nk = d / DMA_BK;
+  return nk % 5 == 0 ? 0 : size_t(256) * d * 2;
+}
+
+size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
+                       int32_t V) {
+  const size_t R = size_t(B) * n_int;
+  const size_t n_tiles = size_t(lmhead_n_tiles(h_dtype, V));
+  size_t n = align_up(2 * n_tiles * R * 8) + align_up((2 * n_tiles + 1) * 4);
+  if (h_dtype == TCS_BF16) {  // zero block and gather lists of the bf16 head
+    const size_t n_rt = (R + 255) / 256;
+    n += align_up(head_zero_bytes(d)) + align_up(2 * n_tiles * n_rt * 4) +
+         align_up(size_t(n_nodes - 1) * B * 16);
+  }
+  return n;
 }
 
 int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
@@ -343,22 +614,43 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
   if (R <= 0) return TCS_OK;
   const int n_tiles = lmhead_n_tiles(h_dtype, V);
   Carve cv(ws);
-  float2* p = cv.take<float2>(size_t(n_tiles) * R);
-  int32_t* seg = cv.take<int32_t>(n_tiles + 1);
-  head_seg_kernel<<<(n_tiles + 256) / 256, 256, 0, s>>>(n_tiles, e_tok, n_edges, seg);
+  float2* p = cv.take<float2>(size_t(2 * n_tiles) * R);
+  int32_t* seg = cv.take<int32_t>(2 * n_tiles + 1);
+  const bool bf16_head = h_dtype == TCS_BF16 && w_dtype == TCS_BF16;
+  const bool bf16_h = h_dtype == TCS_BF16;
+  const size_t zbytes = bf16_head ? head_zero_bytes(d) : 0;
+  uint4* zero = cv.take<uint4>(bf16_h ? head_zero_bytes(d) / 16 : 0);
+  const int n_rt = (R + 255) / 256;
+  const int n_keys = bf16_head ? 2 * n_tiles * n_rt : 0;
+  const long n_pairs = bf16_head ? long(n_edges) * B : 0;
+  int32_t* list_head = cv.take<int32_t>(bf16_h ? size_t(2) * n_tiles * n_rt : 0);
+  int4* rec = cv.take<int4>(bf16_h ? size_t(n_edges) * B : 0);
+  const int n_prep = max(2 * n_tiles + 1, int(zbytes / 16));
+  head_prep_kernel<<<(n_prep + 255) / 256, 256, 0, s>>>(2 * n_tiles, e_tok, n_edges, seg, zero,
+                                                        int(zbytes / 16));
+  if (bf16_head) {
+    head_list_init_kernel<<<(n_keys + 255) / 256, 256, 0, s>>>(n_keys, list_head);
+    if (n_pairs > 0)
+      head_list_link_kernel<<<int((n_pairs + 255) / 256), 256, 0, s>>>(
+          B, n_int, n_nodes, n_rt, e_tok, e_qrow, e_child, n_edges, list_head, rec);
+  }
+  int n_parts = n_tiles;
   timer_begin(TCS_TIMER_HEAD, stream);
   if (h_dtype == TCS_BF16) {
     if (d % 64 != 0) return fail(TCS_EUNSUPPORTED, "lmhead: d=%d is not a multiple of 64", d);
-    const int n_rt = (R + 255) / 256;
-    if (w_dtype == TCS_FP8_E4M3)
+    if (w_dtype == TCS_FP8_E4M3) {
       lmhead_fp8_kernel<<<n_rt * n_tiles, 256, 0, s>>>(R, V, d, n_int, n_nodes,
                                                         static_cast<const uint16_t*>(h),
                                                         static_cast<const uint8_t*>(W), w_scale, seg,
                                                         e_tok, e_qrow, e_child, lp, p);
-    else
-      lmhead_bf16_kernel<<<head_grid(n_rt, n_tiles), 256, 0, s>>>(
-          R, V, d, n_int, n_nodes, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
-          seg, e_tok, e_qrow, e_child, lp, p);
+    } else {
+      const int rounds = head_grid(n_rt, n_tiles) / HEAD_WGS;
+      const int per = head_rounds_per_wg(rounds);
+      lmhead_bf16_kernel<<<(rounds + per - 1) / per * HEAD_WGS, 256, 0, s>>>(
+          R, V, d, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), list_head, rec,
+          lp, p, reinterpret_cast<const uint16_t*>(zero), per);
+      n_parts = 2 * n_tiles;
+    }
   } else {
     dim3 grid(n_tiles, (R + 7) / 8);
     lmhead_f32_kernel<<<grid, 256, 0, s>>>(R, V, d, n_int, n_nodes, static_cast<const float*>(h),
@@ -369,9 +661,9 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "lmhead: %s", hipGetErrorString(e));
   if (R < 16384)
-    lse_finalize_wave_kernel<<<(R + 3) / 4, 256, 0, s>>>(R, n_tiles, p, lse);
+    lse_finalize_wave_kernel<<<(R + 3) / 4, 256, 0, s>>>(R, n_parts, p, lse);
   else
-    lse_finalize_kernel<<<(R + 255) / 256, 256, 0, s>>>(R, n_tiles, p, lse);
+    lse_finalize_kernel<<<(R + 255) / 256, 256, 0, s>>>(R, n_parts, p, lse);
   const long nlp = long(B) * n_nodes;
   lp_finalize_kernel<<<int((nlp + 255) / 256), 256, 0, s>>>(B, n_int, n_nodes, e_qrow, e_child, lse,
                                                              lp);

@@ -55,7 +55,6 @@ static int tree_attn_impl(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, 
   return launch_doc_attn(stream, dt, B, n_int, Hq, Hkv, hd, Qn, Kd, Vd, doc_offsets, ml, ao, scale, O);
 }
 
-static size_t lmhead_part_bytes(int32_t rows, int32_t V) { return lmhead_ws_bytes(rows, V); }
 
 }  // namespace tcs
 
@@ -86,8 +85,10 @@ int tcs_tree_attn(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, 
                         qparent, scale, O, ws);
 }
 
-size_t tcs_lmhead_workspace_bytes(tcs_dtype /*h_dtype*/, int32_t rows, int32_t V) {
-  return lmhead_part_bytes(rows, V);
+size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
+                                  int32_t d, int32_t V) {
+  if (B < 0 || n_int < 1 || n_nodes < 2 || d < 1 || V < 1 || int64_t(B) * n_int > INT32_MAX) return 0;
+  return lmhead_ws_bytes(h_dtype, B, n_int, n_nodes, d, V);
 }
 
 int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
@@ -109,7 +110,7 @@ int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtyp
     return fail(TCS_EINVAL, "lmhead: null pointer");
   const int64_t rows = int64_t(B) * n_int;
   if (rows > INT32_MAX) return fail(TCS_EINVAL, "lmhead: %lld rows", (long long)rows);
-  const size_t need = lmhead_part_bytes(int32_t(rows), V);
+  const size_t need = lmhead_ws_bytes(h_dtype, B, n_int, n_nodes, d, V);
   if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "lmhead: workspace %zu < %zu bytes", ws_bytes, need);
   return launch_lmhead(stream, h_dtype, w_dtype, B, n_int, n_nodes, d, V, h, W, w_scale, e_tok,
                        e_qrow, e_child, n_nodes - 1, lse, lp, ws);
@@ -157,7 +158,7 @@ static ClassifyLayout classify_layout(const tcs_model* m, const tcs_trie_dev* t,
   L.O = c.take<char>(R * qd * es);
   L.y = c.take<float>(R * m->d);
   L.h = c.take<char>(R * m->d * es);
-  L.part = c.take<char>(lmhead_part_bytes(int32_t(R), m->V));
+  L.part = c.take<char>(lmhead_ws_bytes(m->dtype, d->B, t->n_int, t->n_nodes, m->d, m->V));
   L.lse = c.take<float>(R);
   L.lp = c.take<float>(size_t(d->B) * t->n_nodes);
   L.ll = c.take<float>(size_t(d->B) * t->n_labels);

@@ -61,7 +61,8 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
 // Output head, see tcs_lmhead_lse_gather.  The workspace holds n_tiles * R float2
 // partials and the per-tile edge segment table.
 int lmhead_n_tiles(tcs_dtype h_dtype, int32_t V);
-size_t lmhead_ws_bytes(int32_t rows, int32_t V);
+size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
+                       int32_t V);
 int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
                   int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                   const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
