@@ -50,6 +50,81 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
   }
 }
 
+// ------------------------------------------------------------------ bf16 skinny
+
+// C = A B^T for few rows (M <= 16 RB), e.g. the node projections of a small trie:
+// the work is streaming the weight matrix B once.  A workgroup owns 16 rows of B;
+// its four waves take every fourth 32-wide k-chunk, each chunk one
+// v_mfma_f32_16x16x32_bf16 per 16-row block of A with the fragments loaded
+// straight from global memory (16 bytes per lane, no LDS staging), four chunks of
+// loads in flight per wave.  The waves' partial tiles are summed through LDS.
+// Rows past M / N read as zero (outside the buffer resources' ranges); chunks past
+// K use an offset outside them too.
+template <int RB>
+__global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(
+    int M, int N, int K, const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B,
+    int ldb, void* __restrict__ C, int ldc, int epi, GemmResid resid) {
+  constexpr uint32_t RSRC_W3 = 0x00020000u, OOB = 0x80000000u;
+  constexpr int U = 4;
+  __shared__ float red[4][RB][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int n0 = blockIdx.x * 16;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, M * lda * 2, RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B + (size_t)n0 * ldb), 0, min(16, N - n0) * ldb * 2, RSRC_W3);
+  // 16x16x32 operand layout: row (A) / column (B) l%16, k values 8*(l/16) .. +8
+  const uint32_t ob = uint32_t(((lane & 15) * ldb + 8 * (lane >> 4)) * 2);
+  uint32_t oa[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) oa[r] = uint32_t(((r * 16 + (lane & 15)) * lda + 8 * (lane >> 4)) * 2);
+  f32x4 acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = K / 32;
+  for (int c0 = wave; c0 < nch; c0 += 4 * U) {
+    bf16x8 fb[U], fa[U][RB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      const uint32_t kb = uint32_t(c) * 64u;  // byte offset of the chunk in a row
+      const bool ok = c < nch;
+      fb[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? ob + kb : OOB, 0, 0));
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        fa[u][r] = __builtin_bit_cast(bf16x8,
+                                      __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? oa[r] + kb : OOB, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[u][r], fb[u], acc[r], 0, 0, 0);
+  }
+  // result lane l, element i: row 4 (l/16) + i, column l%16 of each 16 x 16 block
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][r][i * 64 + lane] = acc[r][i];
+  __syncthreads();
+  const int t = threadIdx.x, l = t & 63, i = t >> 6;
+  const int col = n0 + (l & 15);
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int row = r * 16 + 4 * (l >> 4) + i;
+    if (row >= M || col >= N) continue;
+    const float v = red[0][r][t] + red[1][r][t] + red[2][r][t] + red[3][r][t];
+    if (epi == GEMM_RESID) {
+      const int tok = resid.token[resid.qnode[row % resid.n_int]];
+      static_cast<float*>(C)[(size_t)row * ldc + col] =
+          v + bf16_to_f32(static_cast<const uint16_t*>(resid.E)[(size_t)tok * N + col]);
+    } else {
+      static_cast<uint16_t*>(C)[(size_t)row * ldc + col] = f32_to_bf16(v);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 SIMT
 
 // 64 x 64 tile, 256 threads, 4 x 4 outputs per thread.
@@ -206,7 +281,15 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
     if (K % GEMM_BK != 0) return fail(TCS_EUNSUPPORTED, "gemm: K=%d is not a multiple of 64", K);
     const long t256 = long((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
-    if (t256 >= 512)
+    if (M <= 64 && long(M) * lda < (1L << 30) && long(N) * ldb < (1L << 30)) {
+      const int g = (N + 15) / 16;
+      auto a = static_cast<const uint16_t*>(A);
+      auto b = static_cast<const uint16_t*>(B);
+      if (M <= 16) gemm_skinny_bf16_kernel<1><<<g, 256, 0, s>>>(M, N, K, a, lda, b, ldb, C, ldc, epi, r);
+      else if (M <= 32) gemm_skinny_bf16_kernel<2><<<g, 256, 0, s>>>(M, N, K, a, lda, b, ldb, C, ldc, epi, r);
+      else if (M <= 48) gemm_skinny_bf16_kernel<3><<<g, 256, 0, s>>>(M, N, K, a, lda, b, ldb, C, ldc, epi, r);
+      else gemm_skinny_bf16_kernel<4><<<g, 256, 0, s>>>(M, N, K, a, lda, b, ldb, C, ldc, epi, r);
+    } else if (t256 >= 512)
       launch_bf16_cfg<256, 256, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
     else if (t128 >= 512)
       launch_bf16_cfg<128, 128, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
