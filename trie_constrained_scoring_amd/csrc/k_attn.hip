@@ -385,6 +385,243 @@ int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32
   return TCS_OK;
 }
 
+// Document part for tries with many query rows per (document, KV head): each wave
+// owns 32 query rows (j -> node j / G, head g G + j % G) and all four waves share
+// one 64-key stage of K (row-major) and V^T in LDS, loaded through registers one
+// stage ahead.  The stage is processed in two 32-key blocks with the same MFMA
+// formulation as doc_attn_mfma_kernel (S^T = K Q^T with a lane per row; O^T +=
+// V^T P^T with P split into bf16 high and low parts).  Two workgroups fit on a CU
+// (at most 256 registers per lane, ~70 KB of LDS), so one's loads and barriers
+// overlap the other's MFMAs.  The epilogue merges each row with its path partial
+// and writes whole rows through a per-wave LDS tile.
+template <int HD>
+__global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
+    int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn, const uint16_t* __restrict__ Kd,
+    const uint16_t* __restrict__ Vd, const int32_t* __restrict__ doc_offsets,
+    const float2* __restrict__ anc_ml, const float* __restrict__ anc_o, float scale,
+    uint16_t* __restrict__ O) {
+  constexpr int KT = 64;                       // keys per stage
+  constexpr int LDK = HD + 8;                  // sK row (bf16): conflict-free 16-byte reads
+  constexpr int LDV = KT + 4;                  // sVt row (bf16): conflict-free 8-byte reads
+  constexpr int STAGE = KT * LDK + HD * LDV;   // bf16 elements
+  constexpr int K_CH = KT * (HD / 8) / 256;    // 16-byte K chunks per thread
+  constexpr int V_GROUPS = (KT / 4) * (HD / 8);  // 4 keys x 8 hd per group
+  constexpr int NBLK = HD / 32, KSTEPS = HD / 16;
+  constexpr int OUT_LD = HD + 1;               // epilogue fp32 row
+  constexpr int EPI_BYTES = 4 * 32 * OUT_LD * 4 + 4 * 32 * 2 * 4;
+  constexpr int LDS_BYTES = 2 * STAGE * 2 > EPI_BYTES ? 2 * STAGE * 2 : EPI_BYTES;
+  static_assert(K_CH * 256 == KT * (HD / 8) && V_GROUPS <= 256, "staging");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LDS_BYTES];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+
+  const int G = Hq / Hkv;
+  const int rows_total = n_int * G;
+  const int n_rb = (rows_total + 127) / 128;
+  const int rb = blockIdx.x % n_rb;
+  const int g = (blockIdx.x / n_rb) % Hkv;
+  const int b = blockIdx.x / (n_rb * Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = rb * 128 + wave * 32;  // this wave's first row
+  const int doc0 = doc_offsets[b];
+  const int L = doc_offsets[b + 1] - doc0;
+
+  // Q^T fragments (lane: row l%32, hd 16 ks + 8 (l/32) ..)
+  bf16x8 qf[KSTEPS];
+  {
+    const int j = j0 + (lane & 31);
+    const bool ok = j < rows_total;
+    const int r = ok ? j / G : 0, h = g * G + (ok ? j % G : 0);
+    const uint16_t* qp = Qn + ((size_t)r * Hq + h) * HD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : uint4{0, 0, 0, 0};
+      qf[ks] = *reinterpret_cast<bf16x8*>(&v);
+    }
+  }
+
+  uint4 rk[K_CH];
+  uint4 rv[4];
+  auto load_stage = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < K_CH; ++i) {
+      const int c = tid + i * 256;
+      const int kk = c / (HD / 8), hc = c % (HD / 8);
+      const int key = key0 + kk;
+      rk[i] = key < L ? *reinterpret_cast<const uint4*>(Kd + ((size_t)(doc0 + key) * Hkv + g) * HD + hc * 8)
+                      : uint4{0, 0, 0, 0};
+    }
+    const int kg = tid / (HD / 8), hc = tid % (HD / 8);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = key0 + kg * 4 + t;
+      rv[t] = (tid < V_GROUPS && key < L)
+                  ? *reinterpret_cast<const uint4*>(Vd + ((size_t)(doc0 + key) * Hkv + g) * HD + hc * 8)
+                  : uint4{0, 0, 0, 0};
+    }
+  };
+  auto store_stage = [&](int buf) {
+    uint16_t* sK = lds + buf * STAGE;
+    uint16_t* sV = sK + KT * LDK;
+#pragma unroll
+    for (int i = 0; i < K_CH; ++i) {
+      const int c = tid + i * 256;
+      const int kk = c / (HD / 8), hc = c % (HD / 8);
+      *reinterpret_cast<uint4*>(sK + kk * LDK + hc * 8) = rk[i];
+    }
+    if (tid < V_GROUPS) {
+      const int kg = tid / (HD / 8), hc = tid % (HD / 8);
+      const uint32_t w[4][4] = {{rv[0].x, rv[0].y, rv[0].z, rv[0].w},
+                                {rv[1].x, rv[1].y, rv[1].z, rv[1].w},
+                                {rv[2].x, rv[2].y, rv[2].z, rv[2].w},
+                                {rv[3].x, rv[3].y, rv[3].z, rv[3].w}};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t k0 = (w[0][e >> 1] >> sh) & 0xFFFFu, k1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t k2 = (w[2][e >> 1] >> sh) & 0xFFFFu, k3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(sV + (hc * 8 + e) * LDV + kg * 4) = uint2{k0 | (k1 << 16), k2 | (k3 << 16)};
+      }
+    }
+  };
+
+  f32x16 acc[NBLK];
+#pragma unroll
+  for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  float m = -INFINITY, lsum = 0.f;  // base-2 running max; this lane's share of the sum
+  const float qk = scale * LOG2E;
+
+  const int n_it = (L + KT - 1) / KT;
+  if (n_it > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < n_it) load_stage((it + 1) * KT);
+    const uint16_t* sK = lds + cur * STAGE;
+    const uint16_t* sV = sK + KT * LDK;
+    // S^T for the stage's two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+      const uint16_t* kp = sK + (kb * 32 + (lane & 31)) * LDK + 8 * (lane >> 5);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+    // online softmax (base 2) over the 64 keys; keys past the document end are masked
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = it * KT + kb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        s[kb][e] = key < L ? s[kb][e] * qk : -INFINITY;
+        tmax = fmaxf(tmax, s[kb][e]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);
+    const float c = mn == -INFINITY ? 1.f : exp2f(m - mn);
+    lsum *= c;
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] *= c;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = mn == -INFINITY ? 0.f : exp2f(s[kb][e] - mn);
+        lsum += p[e];
+      }
+      // P^T fragments: keys {8j + 4(l/32) + i}; step 0 takes j = 0,1, step 1 j = 2,3.
+      bf16x8 ph[2], pl[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const float a = p[8 * st + 2 * q2], c2 = p[8 * st + 2 * q2 + 1];
+          const uint16_t ah = f32_to_bf16(a), ch = f32_to_bf16(c2);
+          const uint16_t al = f32_to_bf16(a - bf16_to_f32(ah)), cl = f32_to_bf16(c2 - bf16_to_f32(ch));
+          wh[q2] = uint32_t(ah) | (uint32_t(ch) << 16);
+          wl[q2] = uint32_t(al) | (uint32_t(cl) << 16);
+        }
+        uint4 uh{wh[0], wh[1], wh[2], wh[3]}, ul{wl[0], wl[1], wl[2], wl[3]};
+        ph[st] = *reinterpret_cast<bf16x8*>(&uh);
+        pl[st] = *reinterpret_cast<bf16x8*>(&ul);
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const uint16_t* vp = sV + (blk * 32 + (lane & 31)) * LDV + kb * 32 + 4 * (lane >> 5);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(vp + 16 * st);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16 * st + 8);
+          uint4 u{lo.x, lo.y, hi.x, hi.y};
+          const bf16x8 vf = *reinterpret_cast<bf16x8*>(&u);
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[st], acc[blk], 0, 0, 0);
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[st], acc[blk], 0, 0, 0);
+        }
+      }
+    }
+    if (it + 1 < n_it) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: this wave's 32 rows through its own LDS tile (the stages are free)
+  lsum += __shfl_xor(lsum, 32, 64);
+  float* so = reinterpret_cast<float*>(lds_raw) + (size_t)wave * 32 * OUT_LD;
+  float* sf = reinterpret_cast<float*>(lds_raw) + 4 * 32 * OUT_LD + wave * 64;  // [32][2]
+  const int rw = lane & 31;
+  {
+    const int j = j0 + rw;
+    float s_doc = 0.f, s_anc = 0.f;
+    if (j < rows_total) {
+      const int r = j / G, h = g * G + j % G;
+      const float2 a = anc_ml[(size_t)r * Hq + h];
+      const float ma = a.x * LOG2E;
+      const float Mt = fmaxf(m, ma);
+      const float fd = m == -INFINITY ? 0.f : exp2f(m - Mt);
+      const float fa = exp2f(ma - Mt);
+      const float inv = 1.0f / (lsum * fd + a.y * fa);
+      s_doc = fd * inv;
+      s_anc = fa * inv;
+    }
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int hd = blk * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        so[rw * OUT_LD + hd] = acc[blk][e];
+      }
+    if (lane < 32) {
+      sf[rw * 2 + 0] = s_doc;
+      sf[rw * 2 + 1] = s_anc;
+    }
+  }
+  __syncthreads();
+  for (int idx = lane; idx < 32 * HD; idx += 64) {
+    const int row = idx / HD, hd = idx % HD;
+    const int j = j0 + row;
+    if (j >= rows_total) continue;
+    const int r = j / G, h = g * G + j % G;
+    const float v = so[row * OUT_LD + hd] * sf[row * 2] +
+                    anc_o[((size_t)r * Hq + h) * HD + hd] * sf[row * 2 + 1];
+    O[(((size_t)b * n_int + r) * Hq + h) * HD + hd] = f32_to_bf16(v);
+  }
+}
+
 int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
                     int32_t hd, const void* Qn, const void* Kd, const void* Vd,
                     const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
@@ -409,9 +646,9 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
   } else {
     const long grid = long(B) * Hkv * ((rows + 127) / 128);
     if (hd == 128)
-      doc_attn_mfma_kernel<128, 4, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+      doc_attn_rows_kernel<128><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
     else
-      doc_attn_mfma_kernel<64, 4, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+      doc_attn_rows_kernel<64><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   }
   timer_end(TCS_TIMER_DOC_ATTN, stream);
   const hipError_t e = hipGetLastError();
