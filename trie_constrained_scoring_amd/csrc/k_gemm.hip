@@ -19,6 +19,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
   int mt, nt;
   tile_coords<8>(nbm, nbn, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
+  // split-K (RESID only): split z takes k in [z K, (z+1) K) and writes its fp32
+  // partial to C + z M ldc; the residual goes with split 0
+  const int z = blockIdx.y;
+  if (z > 0) {
+    A += (size_t)z * K;
+    B += (size_t)z * K;
+    C = static_cast<float*>(C) + (size_t)z * M * ldc;
+    epi = GEMM_PART;
+  }
   f32x4 acc[S::MB][S::NB];
   gemm_mainloop<BM, BN, WM, WN, false>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
 
@@ -42,6 +51,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
         const float v = acc[i][j][r];
         if (epi == GEMM_RESID) {
           static_cast<float*>(C)[(size_t)row * ldc + col] = v + bf16_to_f32(xres[col]);
+        } else if (epi == GEMM_PART) {
+          static_cast<float*>(C)[(size_t)row * ldc + col] = v;
         } else {
           static_cast<uint16_t*>(C)[(size_t)row * ldc + col] = f32_to_bf16(v);
         }
@@ -218,16 +229,24 @@ __global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const T* __restrict_
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ y, int d, float eps,
-                                                      T* __restrict__ out) {
+__global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ y, int n, int d,
+                                                      int n_part, float eps, T* __restrict__ out) {
   __shared__ float red[4];
   const int r = blockIdx.x;
-  const float* x = y + (size_t)r * d;
+  // y is n_part partial sums [n_part][n][d], added in a fixed order
+  auto val = [&](int i) {
+    float v = y[(size_t)r * d + i];
+    for (int p = 1; p < n_part; ++p) v += y[((size_t)p * n + r) * d + i];
+    return v;
+  };
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(x[i], x[i], ss);
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float v = val(i);
+    ss = fmaf(v, v, ss);
+  }
   ss = block_sum256<T>(ss, red);
   const float rs = 1.0f / sqrtf(ss / float(d) + eps);
-  for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(x[i] * rs);
+  for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(val(i) * rs);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -251,24 +270,35 @@ int launch_embed_rmsnorm(void* stream, tcs_dtype dt, const void* E, const int32_
   return check_launch("embed_rmsnorm");
 }
 
-int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, float eps,
-                   void* out) {
+int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, int32_t n_part,
+                   float eps, void* out) {
   if (n <= 0) return TCS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TCS_BF16)
-    rownorm_kernel<bf16_t><<<n, 256, 0, s>>>(y, d, eps, static_cast<bf16_t*>(out));
+    rownorm_kernel<bf16_t><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
   else
-    rownorm_kernel<float><<<n, 256, 0, s>>>(y, d, eps, static_cast<float*>(out));
+    rownorm_kernel<float><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
   return check_launch("rownorm");
 }
 
 template <int BM, int BN, int WM, int WN>
 static void launch_bf16_cfg(hipStream_t s, int M, int N, int K, const void* A, int lda,
-                            const void* B, int ldb, void* C, int ldc, int epi, GemmResid r) {
+                            const void* B, int ldb, void* C, int ldc, int epi, GemmResid r,
+                            int splits = 1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  gemm_nt_bf16_kernel<BM, BN, WM, WN><<<tiles, 64 * WM * WN, 0, s>>>(
-      M, N, K, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
-      epi, r);
+  gemm_nt_bf16_kernel<BM, BN, WM, WN><<<dim3(tiles, splits), 64 * WM * WN, 0, s>>>(
+      M, N, K / splits, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb,
+      C, ldc, epi, r);
+}
+
+int gemm_resid_splits(tcs_dtype dt, int32_t M, int32_t N, int32_t K) {
+  if (dt != TCS_BF16 || M <= 64) return 1;
+  const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
+  if (long((M + 255) / 256) * ((N + 255) / 256) >= 512 || t128 >= 512) return 1;
+  const long tiles = long((M + 63) / 64) * ((N + 63) / 64);
+  int s = 1;
+  while (s < 8 && tiles * s * 2 <= 2048 && (K / GEMM_BK) % (s * 2) == 0) s *= 2;
+  return s;
 }
 
 int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N, int32_t K,
@@ -294,7 +324,8 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
     else if (t128 >= 512)
       launch_bf16_cfg<128, 128, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
     else
-      launch_bf16_cfg<64, 64, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
+      launch_bf16_cfg<64, 64, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r,
+                                    epi == GEMM_RESID ? gemm_resid_splits(dt, M, N, K) : 1);
   } else {
     dim3 grid((N + 63) / 64, (M + 63) / 64);
     gemm_nt_f32_kernel<<<grid, 256, 0, s>>>(M, N, K, static_cast<const float*>(A), lda,

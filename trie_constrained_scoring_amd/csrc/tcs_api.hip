@@ -156,7 +156,7 @@ static ClassifyLayout classify_layout(const tcs_model* m, const tcs_trie_dev* t,
   }
   L.anc = c.take<char>(anc_bytes(t->n_int, m->Hq, m->hd));
   L.O = c.take<char>(R * qd * es);
-  L.y = c.take<float>(R * m->d);
+  L.y = c.take<float>(R * m->d * gemm_resid_splits(m->dtype, int32_t(R), m->d, int32_t(qd)));
   L.h = c.take<char>(R * m->d * es);
   L.part = c.take<char>(lmhead_ws_bytes(m->dtype, d->B, t->n_int, t->n_nodes, m->d, m->V));
   L.lse = c.take<float>(R);
@@ -232,7 +232,8 @@ int tcs_classify(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, c
   // y = x + O Wo^T ; h = RMSNorm(y)
   GemmResid res{m->E, t->token, t->qnode, n_int};
   if ((rc = launch_gemm_nt(stream, dt, GEMM_RESID, R, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d, &res))) return rc;
-  if ((rc = launch_rownorm(stream, dt, L.y, R, m->d, m->eps, L.h))) return rc;
+  if ((rc = launch_rownorm(stream, dt, L.y, R, m->d, gemm_resid_splits(dt, R, m->d, qd), m->eps,
+                           L.h))) return rc;
   if ((rc = launch_lmhead(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,
                           m->W_scale, t->e_tok, t->e_qrow, t->e_child, t->n_nodes - 1, L.lse, L.lp,
                           L.part))) return rc;

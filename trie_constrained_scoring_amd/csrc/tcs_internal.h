@@ -40,14 +40,19 @@ void timer_end(int timer, void* stream);
 int launch_embed_rmsnorm(void* stream, tcs_dtype dt, const void* E, const int32_t* idx,
                          const int32_t* idx2, int32_t n, int32_t d, int32_t V, float eps, void* out);
 
-// h[r] = RMSNorm(y[r]) for fp32 y [n, d], written in dtype dt.
-int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, float eps,
-                   void* out);
+// h[r] = RMSNorm(y[r]) for fp32 y = sum of n_part partials [n_part][n][d], written in
+// dtype dt.
+int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, int32_t n_part,
+                   float eps, void* out);
 
 // C[m, n] = sum_k A[m, k] * B[n, k].  Epilogues:
 //   STORE: C stored in dtype dt (rounded) with leading dimension ldc.
-//   RESID: C + E[tok(row)] stored as fp32, tok(row) = token[qnode[row % n_int]].
-enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1 };
+//   RESID: C + E[tok(row)] stored as fp32, tok(row) = token[qnode[row % n_int]]; may
+//          be split over K into gemm_resid_splits(...) fp32 partials [splits][M][ldc]
+//          (the residual in the first), to be summed by launch_rownorm.
+//   PART:  (internal) one split's fp32 partial.
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_PART = 2 };
+int gemm_resid_splits(tcs_dtype dt, int32_t M, int32_t N, int32_t K);
 struct GemmResid {
   const void* E;
   const int32_t* token;
