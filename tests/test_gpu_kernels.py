@@ -163,8 +163,11 @@ def test_lmhead_zero_hidden_gives_log_vocab(dev):
 # ------------------------------------------------------------------ tree attention
 
 ATTN_CASES = {
-    # n_int small -> 32-row / 4-key-slice kernel; large -> 128-row kernel
+    # rows per (document, KV head) <= 64 -> key-streaming kernel (hd 128) or the
+    # 32-row / 4-key-slice kernel (hd 64); more rows -> 128-row kernel
     "running-hd128": dict(labels=("running",), Hq=8, Hkv=2, hd=128, lens=(0, 1, 31, 32, 129, 300)),
+    "running-hd128-g8": dict(labels=("running",), Hq=16, Hkv=2, hd=128, lens=(3, 64, 257, 1000)),
+    "running-hd128-long": dict(labels=("running",), Hq=4, Hkv=1, hd=128, lens=(4113, 2, 4096)),
     "running-hd64": dict(labels=("running",), Hq=4, Hkv=1, hd=64, lens=(5, 64, 200)),
     "zipf-hd128": dict(labels=("zipf", 30, 2, 6, 1.2), Hq=8, Hkv=2, hd=128, lens=(0, 33, 97)),
     "zipf-hd64-g8": dict(labels=("zipf", 20, 2, 5, 1.2), Hq=8, Hkv=1, hd=64, lens=(7, 70)),

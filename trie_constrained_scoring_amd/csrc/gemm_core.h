@@ -214,14 +214,6 @@ constexpr int DMA_LOADS_PER_OPERAND = 8;          // per wave (per thread) per t
 
 __device__ __forceinline__ int dma_swz(int r) { return (r ^ (r >> 3)) & 7; }  // r in [0, 16)
 
-#define TCS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// s_waitcnt with one counter and the others left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Output-head tile order: tile slot `bid` = 256 w + b is the w-th tile of the
 // persistent workgroup b (one per CU; b runs on XCD b % 8).  The 256 slots of one

@@ -360,6 +360,292 @@ __global__ __launch_bounds__(256) void doc_attn_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------- document part, few rows
+//
+// When a trie's query rows for one (document, KV head) fill one or two 32-row
+// blocks, the document part is a stream over the document's keys at ~48 FLOP per
+// byte of K and V, far below the matrix cores' ridge: the kernel is built to keep
+// HBM busy.  One workgroup takes one (document, KV head, 32-row block); each of its
+// four waves streams its own 32-key stages (keys [32 t, 32 t + 32) for
+// t = wave, wave + 4, ...) through a private two-slot LDS ring filled by direct
+// buffer-to-LDS loads, so the key loop has no workgroup barrier.
+//
+// K and V stay in their natural [key][hd] layout.  In a slot, the 16-byte chunk c
+// of key row r sits at position c ^ kv_swz(r mod 16), which puts both the K
+// fragment reads (16 key rows per LDS phase) and the transposing reads of V (4 keys
+// x 64 bytes per half-wave) on distinct banks.
+//   S^T[key][row] = K Q^T   (A = K rows from LDS, B = Q^T in registers): each lane
+//     holds one query row and 16 of the 32 keys;
+//   O^T[hd][row] += V^T P^T (A = V^T read with ds_read_tr16_b64 straight from the
+//     natural V tile, B = P^T from the S^T registers, P split into a bf16 high
+//     part and a bf16 remainder, which keeps the weights to ~2^-17 relative error).
+// The four waves' key slices and the row's path partial are merged by log-sum-exp
+// in the epilogue.
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Two transposing 8-byte LDS reads (ds_read_tr16_b64) joined into one MFMA operand:
+// within each group of 16 lanes, lane i receives element i%4 of the 4-element
+// pieces that lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 point at.
+__device__ __forceinline__ bf16x8 lds_read_tr_x2(const uint8_t* p0, const uint8_t* p1) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)TCS_LDS(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)TCS_LDS(p1));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// Two floats -> packed bf16 (round to nearest even, hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// NLD 1 KB buffer-to-LDS loads of one operand stage: load j writes dst + 1 KB j,
+// lane i at 16 i, from byte vo[j] of a buffer resource over [base, base + bytes).
+template <int NLD>
+__device__ __forceinline__ void kv_issue(const uint16_t* base, int bytes, uint8_t* dst,
+                                         const int (&vo)[NLD]) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NLD; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(dst + j * 1024), 16, vo[j], 0, 0, 0);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void doc_attn_stream_kernel(
+    int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn, const uint16_t* __restrict__ Kd,
+    const uint16_t* __restrict__ Vd, const int32_t* __restrict__ doc_offsets,
+    const float2* __restrict__ anc_ml, const float* __restrict__ anc_o, float scale,
+    uint16_t* __restrict__ O) {
+  static_assert(HD == 128, "256-byte key rows: 16 chunks, one per swizzle position");
+  constexpr int KB = 32;                 // keys per stage
+  constexpr int ROW = HD * 2;            // bytes per key row
+  constexpr int OPB = KB * ROW;          // bytes per operand per stage (8 KB)
+  constexpr int NLD = OPB / 1024;        // 1 KB loads per operand per stage
+  constexpr int NS = 2;                  // ring slots per wave
+  constexpr int WAVE_BYTES = NS * 2 * OPB;
+  constexpr int NBLK = HD / 32, KSTEPS = HD / 16;
+  constexpr int OUT_LD = HD + 1;
+  constexpr int EPI_BYTES = 4 * 32 * OUT_LD * 4 + 4 * 32 * 2 * 4;
+  constexpr int LDS_BYTES = 4 * WAVE_BYTES > EPI_BYTES ? 4 * WAVE_BYTES : EPI_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+  const int G = Hq / Hkv;
+  const int rows_total = n_int * G;
+  const int n_rb = (rows_total + 31) / 32;
+  const int rb = blockIdx.x % n_rb;
+  const int g = (blockIdx.x / n_rb) % Hkv;
+  const int b = blockIdx.x / (n_rb * Hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j0 = rb * 32;
+  const int doc0 = doc_offsets[b];
+  const int L = doc_offsets[b + 1] - doc0;
+  const int RS = Hkv * HD * 2;           // bytes between consecutive keys of one head
+  uint8_t* const ring = lds + wave * WAVE_BYTES;
+
+  // this wave's slots start as zeros, so a key past the document end that no load
+  // writes still holds finite values (its weight is 0)
+#pragma unroll
+  for (int i = 0; i < WAVE_BYTES / (64 * 16); ++i)
+    *reinterpret_cast<uint4*>(ring + (i * 64 + lane) * 16) = uint4{0u, 0u, 0u, 0u};
+
+  // Q^T fragments: lane holds row l%32, hd 16 ks + 8 (l/32) ..
+  bf16x8 qf[KSTEPS];
+  {
+    const int j = j0 + (lane & 31);
+    const bool ok = j < rows_total;
+    const int r = ok ? j / G : 0, h = g * G + (ok ? j % G : 0);
+    const uint16_t* qp = Qn + ((size_t)r * Hq + h) * HD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : uint4{0, 0, 0, 0};
+      qf[ks] = *reinterpret_cast<bf16x8*>(&v);
+    }
+  }
+
+  // DMA: load j of an operand fills slot rows 4j .. 4j+3 (1 KB); lane i writes row
+  // 4j + i/16 at position i%16, which holds chunk (i%16) ^ kv_swz(row).
+  int vo[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int row = 4 * j + (lane >> 4);
+    vo[j] = row * RS + (((lane & 15) ^ kv_swz(row & 15)) << 4);
+  }
+  const uint16_t* const kbase = Kd + ((size_t)doc0 * Hkv + g) * HD;
+  const uint16_t* const vbase = Vd + ((size_t)doc0 * Hkv + g) * HD;
+  // Stage t into slot s: one buffer resource per stage over its valid keys, so keys
+  // past the document end fall outside the range and read nothing.
+  auto issue = [&](int t, int s) __attribute__((always_inline)) {
+    const int nkeys = min(KB, L - t * KB);
+    const int bytes = (nkeys - 1) * RS + ROW;
+    const size_t off = (size_t)t * KB * Hkv * HD;
+    uint8_t* sk = ring + s * 2 * OPB;
+    kv_issue<NLD>(kbase + off, bytes, sk, vo);
+    kv_issue<NLD>(vbase + off, bytes, sk + OPB, vo);
+  };
+
+  // fragment offsets inside a slot
+  const int kr = lane & 31, c = lane >> 5;
+  int ko[KSTEPS];  // K: row kr, chunk 2 ks + c
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) ko[ks] = kr * ROW + (((2 * ks + c) ^ kv_swz(kr & 15)) << 4);
+  // V^T by transposing reads: for step st and half q, the 16 lanes of group
+  // gq = lane/16 read keys 16 st + 8 q + 4 c + 0..3 at hd 32 blk + 16 (gq%2) + 0..15;
+  // as a source lane, lane s of the group points at key (.. + s/4), hd (.. + 4 (s%4)).
+  int vof[2][2][NBLK];
+  {
+    const int s = lane & 15, hsel = (lane >> 4) & 1;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int key = 16 * st + 8 * q + 4 * c + (s >> 2);
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+          const int chunk = 4 * blk + 2 * hsel + ((s & 3) >> 1);
+          vof[st][q][blk] = OPB + key * ROW + ((chunk ^ kv_swz(key & 15)) << 4) + 8 * (s & 1);
+        }
+      }
+  }
+
+  f32x16 acc[NBLK];
+#pragma unroll
+  for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  float m = -INFINITY, lsum = 0.f;  // base-2 running max; this lane's share of the sum
+  const float qk = scale * LOG2E;
+
+  auto compute = [&](const uint8_t* sl, int t) __attribute__((always_inline)) {
+    f32x16 sc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + ko[ks]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
+    }
+    // online softmax (base 2); keys past the document end are masked
+    const int kb0 = t * KB + 4 * c;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kb0 + 8 * (e >> 2) + (e & 3);
+      sc[e] = key < L ? sc[e] * qk : -INFINITY;
+      tmax = fmaxf(tmax, sc[e]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);  // finite: every stage has a valid key
+    const float cf = exp2f(m - mn);
+    m = mn;
+    lsum *= cf;
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] *= cf;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = exp2f(sc[e] - mn);
+      lsum += p[e];
+    }
+    // P^T fragments: step st takes keys {16 st + 4c + 0..3, 16 st + 8 + 4c + 0..3}
+    bf16x8 ph[2], pl[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const float a = p[8 * st + 2 * q2], a2 = p[8 * st + 2 * q2 + 1];
+        wh[q2] = pack_bf16(a, a2);
+        wl[q2] = pack_bf16(a - __uint_as_float(wh[q2] << 16), a2 - __uint_as_float(wh[q2] & 0xFFFF0000u));
+      }
+      uint4 uh{wh[0], wh[1], wh[2], wh[3]}, ul{wl[0], wl[1], wl[2], wl[3]};
+      ph[st] = *reinterpret_cast<bf16x8*>(&uh);
+      pl[st] = *reinterpret_cast<bf16x8*>(&ul);
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 vf = lds_read_tr_x2(sl + vof[st][0][blk], sl + vof[st][1][blk]);
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[st], acc[blk], 0, 0, 0);
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[st], acc[blk], 0, 0, 0);
+      }
+  };
+
+  const int n_st = (L + KB - 1) / KB;
+  const int cnt = n_st > wave ? (n_st - wave + 3) / 4 : 0;
+  wait_lgkmcnt0();  // the zero fill is in LDS before any load can land on it
+  if (cnt > 0) issue(wave, 0);
+  if (cnt > 1) issue(wave + 4, 1);
+  for (int i = 0; i < cnt; ++i) {
+    if (i + 1 < cnt) wait_vmcnt<2 * NLD>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ring + (i & 1) * 2 * OPB, wave + 4 * i);
+    if (i + 2 < cnt) {
+      wait_lgkmcnt0();  // this slot's reads are done before it is refilled
+      __builtin_amdgcn_sched_barrier(0);
+      issue(wave + 4 * (i + 2), i & 1);
+    }
+  }
+  __syncthreads();
+
+  // merge the four key slices of each row and the row's path partial
+  float* so = reinterpret_cast<float*>(lds);          // [4][32][HD+1]
+  float* sml = so + 4 * 32 * OUT_LD;                  // [4][32][2]
+  lsum += __shfl_xor(lsum, 32, 64);
+  {
+    float* base = so + (size_t)wave * 32 * OUT_LD;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int hd = blk * 32 + 8 * (e >> 2) + 4 * c + (e & 3);
+        base[kr * OUT_LD + hd] = acc[blk][e];
+      }
+    if (lane < 32) {
+      sml[(wave * 32 + kr) * 2 + 0] = m;
+      sml[(wave * 32 + kr) * 2 + 1] = lsum;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 32 * HD; idx += 256) {
+    const int row = idx / HD, hd = idx % HD;
+    const int j = j0 + row;
+    if (j >= rows_total) continue;
+    const int r = j / G, h = g * G + j % G;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) M = fmaxf(M, sml[(k * 32 + row) * 2]);
+    float Ls = 0.f, Os = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float f = exp2f(sml[(k * 32 + row) * 2] - M);
+        Ls += f * sml[(k * 32 + row) * 2 + 1];
+        Os += f * so[((size_t)k * 32 + row) * OUT_LD + hd];
+      }
+    }
+    const float2 a = anc_ml[(size_t)r * Hq + h];
+    const float ma = a.x * LOG2E;
+    const float Mt = fmaxf(M, ma);
+    const float fd = M == -INFINITY ? 0.f : exp2f(M - Mt);
+    const float fa = exp2f(ma - Mt);
+    const float num = Os * fd + anc_o[((size_t)r * Hq + h) * HD + hd] * fa;
+    const float den = Ls * fd + a.y * fa;
+    O[(((size_t)b * n_int + r) * Hq + h) * HD + hd] = f32_to_bf16(num / den);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32_t Hkv, int32_t hd,
@@ -640,7 +926,7 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
   if (rows <= 64) {
     const long grid = long(B) * Hkv * ((rows + 31) / 32);
     if (hd == 128)
-      doc_attn_mfma_kernel<128, 1, 4><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+      doc_attn_stream_kernel<128><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
     else
       doc_attn_mfma_kernel<64, 1, 4><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   } else {

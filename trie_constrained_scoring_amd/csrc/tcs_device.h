@@ -53,6 +53,16 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t byte) {
   return s | (em >= 8u ? normal : sub);
 }
 
+// LDS pointer for the buffer-to-LDS load builtins.
+#define TCS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with one counter and the others left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // ---- wavefront reductions over groups of 16 consecutive lanes (DPP) ----
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
