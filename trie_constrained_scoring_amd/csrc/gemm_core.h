@@ -1,4 +1,4 @@
-// bf16 MFMA main loop shared by the projection GEMMs and the output head.
+// bf16 MFMA main loop of the projection GEMMs, and the LDS-DMA pieces of the output head.
 //
 // C[m, n] = sum_k A[m, k] * B[n, k]: both operands are K-contiguous ("NT"), as
 // every weight here is stored [out, in].  One workgroup computes a BM x BN tile
@@ -30,7 +30,6 @@ struct GemmShape {
   static constexpr int NB = TN / 16;       // 16x16 blocks per wave (cols)
   static constexpr int A_CHUNKS = BM * (GEMM_BK / 8) / NT;   // 16-byte chunks per thread
   static constexpr int B_CHUNKS = BN * (GEMM_BK / 8) / NT;
-  static constexpr int B8_CHUNKS = BN * (GEMM_BK / 16) / NT; // fp8 B: 16 elements per chunk
   static constexpr int LDS_ELEMS = 2 * (BM + BN) * GEMM_LDK;  // bf16 elements, both stages
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "tile");
   static_assert(A_CHUNKS * NT == BM * 8 && B_CHUNKS * NT == BN * 8, "chunking");
@@ -56,7 +55,7 @@ __device__ __forceinline__ void tile_coords(int nbm, int nbn, int& mt, int& nt) 
   nt = in_group / gm;
 }
 
-// Main loop.  A: bf16 [M, lda]; B: bf16 [N, ldb] or (B_FP8) E4M3 bytes [N, ldb].
+// Main loop.  A: bf16 [M, lda]; B: bf16 [N, ldb].
 // K % 64 == 0.  Rows of A or B at or beyond M / N read as zero.  A tile's rows
 // must span fewer than 2^31 bytes.
 //
@@ -66,7 +65,7 @@ __device__ __forceinline__ void tile_coords(int nbm, int nbn, int& mt, int& nt) 
 //   [LDS reads of step 0 of tile t+1 | MFMAs of step 1 of tile t]
 // so every LDS fragment read is in flight under a block of MFMAs, and the global
 // loads have a whole block of MFMAs to land.
-template <int BM, int BN, int WM, int WN, bool B_FP8>
+template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int lda,
                                               const void* __restrict__ Bv, int ldb, int M, int N,
                                               int K, int m0, int n0, uint16_t* lds,
@@ -84,7 +83,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int RB = B_FP8 ? S::B8_CHUNKS : S::B_CHUNKS;
+  constexpr int RB = S::B_CHUNKS;
   uint4 ra[S::A_CHUNKS];
   uint4 rb[RB];
   // Buffer resources over this tile's rows: the hardware bounds check returns
@@ -94,14 +93,14 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
   const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(A + (size_t)m0 * lda), 0, a_rows * lda * 2, RSRC_W3);
-  constexpr int B_ES = B_FP8 ? 1 : 2;  // bytes per B element
+  constexpr int B_ES = 2;  // bytes per B element
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(static_cast<const uint8_t*>(Bv) + (size_t)n0 * ldb * B_ES), 0,
       b_rows * ldb * B_ES, RSRC_W3);
   const int voffA = ((tid >> 3) * lda + (tid & 7) * 8) * 2;
   const int strideA = (S::NT / 8) * lda * 2;
-  const int voffB = B_FP8 ? ((tid >> 2) * ldb + (tid & 3) * 16) : ((tid >> 3) * ldb + (tid & 7) * 8) * 2;
-  const int strideB = B_FP8 ? (S::NT / 4) * ldb : (S::NT / 8) * ldb * 2;
+  const int voffB = ((tid >> 3) * ldb + (tid & 7) * 8) * 2;
+  const int strideB = (S::NT / 8) * ldb * 2;
   auto load_stage = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < S::A_CHUNKS; ++i) {
@@ -122,27 +121,10 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
       const int c = tid + i * S::NT;
       *reinterpret_cast<uint4*>(a + (c >> 3) * GEMM_LDK + (c & 7) * 8) = ra[i];
     }
-    if constexpr (B_FP8) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int c = tid + i * S::NT;
-        const int row = c >> 2, col = (c & 3) * 16;
-        const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[2 * q] = e4m3_to_bf16(w[q] & 0xFFu) | (e4m3_to_bf16((w[q] >> 8) & 0xFFu) << 16);
-          o[2 * q + 1] = e4m3_to_bf16((w[q] >> 16) & 0xFFu) | (e4m3_to_bf16(w[q] >> 24) << 16);
-        }
-        *reinterpret_cast<uint4*>(b + row * GEMM_LDK + col) = uint4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<uint4*>(b + row * GEMM_LDK + col + 8) = uint4{o[4], o[5], o[6], o[7]};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int c = tid + i * S::NT;
-        *reinterpret_cast<uint4*>(b + (c >> 3) * GEMM_LDK + (c & 7) * 8) = rb[i];
-      }
+    for (int i = 0; i < RB; ++i) {
+      const int c = tid + i * S::NT;
+      *reinterpret_cast<uint4*>(b + (c >> 3) * GEMM_LDK + (c & 7) * 8) = rb[i];
     }
   };
   bf16x8 fa[2][S::MB], fb[2][S::NB];

@@ -383,8 +383,6 @@ __global__ __launch_bounds__(256) void doc_attn_mfma_kernel(
 // in the epilogue.
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 

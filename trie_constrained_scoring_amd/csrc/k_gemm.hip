@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
     epi = GEMM_PART;
   }
   f32x4 acc[S::MB][S::NB];
-  gemm_mainloop<BM, BN, WM, WN, false>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
+  gemm_mainloop<BM, BN, WM, WN>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;

@@ -69,10 +69,11 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 head.  Persistent: one workgroup per CU walks its own sequence of 256 x 256
-// tiles (head_tile_coords), and the LDS ring of five 32 KB operand slots runs on
-// across tile boundaries, so the first k-tiles of the next tile load while the
-// current one finishes and while its epilogue runs.
+// Matrix-core head (bf16 or fp8 weights, bf16 hidden states).  Persistent: one
+// workgroup per CU walks its own sequence of 256 x 256 tiles (head_tile_coords),
+// and the LDS ring of five 32 KB operand slots runs on across tile boundaries, so
+// the first k-tiles of the next tile load while the current one finishes and while
+// its epilogue runs.
 //
 // Global k-step g (over all tiles of this workgroup) keeps W's k-tile in slot
 // 2g mod 5 and h's in slot 2g+1 mod 5; while step g is multiplied, h(g+1) and
@@ -88,19 +89,54 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
 // partial per (row, vocabulary half-tile).  The epilogue touches no LDS: child
 // logits are picked out of the accumulators by a scalar walk over the half-tile's
 // edges.
+//
+// fp8 weights (E4M3 codes + one fp32 scale per vocabulary row) take half the
+// bytes: a W k-tile is 256 rows x 64 bytes, each lane reads 16 codes (k-steps 2m
+// and 2m+1) with one 16-byte LDS read, the codes are converted to bf16 in
+// registers (exact: every E4M3 value is a bf16 value) and the row scale multiplies
+// the fp32 logits in the epilogue.  The k order inside a pair of k-steps is
+// permuted the same way on both operands (lane half c supplies k 32m + 16c + 8s +
+// 0..7 in step 2m+s), which leaves the dot products unchanged.
 
 // One operand k-tile of this wave into an LDS slot: load j (0..7) fills slot rows
 // wave*64 + 8j .. +7 (1 KB), lane i writing 16 bytes at row i/8, position i%8;
 // `vo` holds each load's lane byte offset, `k` the k-tile (scalar offset).
-__device__ __forceinline__ void head_issue(const uint16_t* base, int bytes, int k, uint8_t* sl,
+__device__ __forceinline__ void head_issue(const void* base, int bytes, int k, uint8_t* sl,
                                            int wave, const int (&vo)[DMA_LOADS_PER_OPERAND]) {
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
   const int so = k * DMA_BK * 2;
 #pragma unroll
   for (int j = 0; j < DMA_LOADS_PER_OPERAND; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 64 + j * 8) * 128), 16, vo[j],
                                              so, 0, 0);
+}
+
+// fp8 W k-tile (256 rows x 64 bytes, 16 KB) of this wave: load j (0..3) fills slot
+// rows wave*64 + 16j .. +15, lane i writing 16 bytes at row i/4, position i%4.
+constexpr int DMA8_LOADS = 4;
+__device__ __forceinline__ void head_issue8(const void* base, int bytes, int k, uint8_t* sl,
+                                            int wave, const int (&vo)[DMA8_LOADS]) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  const int so = k * DMA_BK;
+#pragma unroll
+  for (int j = 0; j < DMA8_LOADS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 64 + j * 16) * 64), 16, vo[j],
+                                             so, 0, 0);
+}
+// fp8 W slot: row r (64 bytes) keeps its 16-byte chunk c at position c ^ dma8_swz(r),
+// so the 16 rows read by a group of lanes fall on distinct banks.
+__device__ __forceinline__ int dma8_swz(int r) { return (r >> 2) & 3; }
+
+// Eight E4M3 codes (bytes of w0, w1, lowest first) -> eight bf16 (hardware
+// conversion, scale 1: exact).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
 // v[jn] = acc[t / 16][jn][t % 16] for a wave-uniform t in [0, 64): a binary
@@ -163,14 +199,44 @@ __device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][4], int vli
   for (int jn = 0; jn < 4; ++jn) out[jn] = float2{m[jn], sum[jn] + __shfl_xor(sum[jn], 32, 64)};
 }
 
-__global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
-    int R, int V, int d, const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ list_head, const int4* __restrict__ rec, float* __restrict__ raw,
-    float2* __restrict__ part, const uint16_t* __restrict__ zero, int rounds_per_wg) {
+// acc[im][jn][e] *= scale of vocabulary entry vb + 32 im + 8 (e>>2) + (e&3) (fp8
+// head); entries at or past V are left alone (the row sums exclude them).
+__device__ __forceinline__ void head_scale_rows(f32x16 (&acc)[4][4], const float* __restrict__ w_scale,
+                                                int vb, int V) {
+#pragma unroll
+  for (int im = 0; im < 4; ++im)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int v = vb + 32 * im + 8 * g;
+      float4 sc;
+      if (v + 4 <= V) {
+        sc = *reinterpret_cast<const float4*>(w_scale + v);
+      } else {
+        sc.x = v < V ? w_scale[v] : 1.f;
+        sc.y = v + 1 < V ? w_scale[v + 1] : 1.f;
+        sc.z = v + 2 < V ? w_scale[v + 2] : 1.f;
+        sc.w = 1.f;
+      }
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        acc[im][jn][4 * g + 0] *= sc.x;
+        acc[im][jn][4 * g + 1] *= sc.y;
+        acc[im][jn][4 * g + 2] *= sc.z;
+        acc[im][jn][4 * g + 3] *= sc.w;
+      }
+    }
+}
+
+template <bool W8>
+__global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
+    int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
+    const float* __restrict__ w_scale, const int32_t* __restrict__ list_head,
+    const int4* __restrict__ rec, float* __restrict__ raw, float2* __restrict__ part,
+    const uint16_t* __restrict__ zero, int rounds_per_wg) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[DMA_SLOT_BYTES], st1[DMA_SLOT_BYTES],
       st2[DMA_SLOT_BYTES], st3[DMA_SLOT_BYTES], st4[DMA_SLOT_BYTES];
   uint8_t* const slot[DMA_SLOTS] = {st0, st1, st2, st3, st4};
-  constexpr uint32_t RSRC_W3 = 0x00020000u;
+  constexpr int WRB = W8 ? 1 : 2;  // bytes per weight element
   const int n_rt = (R + 255) / 256, n_vt = (V + HEAD_BN - 1) / HEAD_BN;
   // workgroup g takes rounds [w_lo, rounds) of slot g % 256: a bounded run of
   // consecutive rounds, so the workgroups that share operand tiles in an XCD's L2
@@ -198,15 +264,15 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   // those rows.  (Resources are built at each issue from these plain values, which
   // keeps them in scalar registers.)
   struct Span {
-    const uint16_t* wb;
+    const uint8_t* wb;
     const uint16_t* hb;
     int wn, hn;
   };
   auto span = [&](int w) __attribute__((always_inline)) {
     int rt, vt;
     if (w < rounds && coords(w, rt, vt))
-      return Span{W + (size_t)vt * 256 * d, h + (size_t)rt * 256 * d,
-                  min(256, V - vt * 256) * d * 2, min(256, R - rt * 256) * d * 2};
+      return Span{W + (size_t)vt * 256 * d * WRB, h + (size_t)rt * 256 * d,
+                  min(256, V - vt * 256) * d * WRB, min(256, R - rt * 256) * d * 2};
     return Span{W, h, 0, 0};
   };
 
@@ -218,12 +284,21 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < DMA_LOADS_PER_OPERAND; ++j)
     vo[j] = ((wave * 64 + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
+  // fp8 W: load j (0..3) fills rows wave*64 + 16j + i/4, position i%4, which holds
+  // chunk (i%4) ^ dma8_swz(row % 16)
+  int vo8[DMA8_LOADS];
+#pragma unroll
+  for (int j = 0; j < DMA8_LOADS; ++j) {
+    const int row = wave * 64 + j * 16 + (lane >> 2);
+    vo8[j] = row * d + (((lane & 3) ^ dma8_swz(row & 15)) << 4);
+  }
+  constexpr int W_LOADS = W8 ? DMA8_LOADS : DMA_LOADS_PER_OPERAND;
   int w = next_valid(w_lo);
   if (w >= rounds) return;
   // A tile runs nk5 = nk rounded up to a multiple of 5 steps, so every tile starts
   // at ring position 0.  Steps past nk load both operands from `zero` (256 x d
-  // zeros), so they run the same code and add nothing.  Loads run up to two steps
-  // ahead, so they reach into the next tile at most.
+  // bf16 zeros), so they run the same code and add nothing.  Loads run up to two
+  // steps ahead, so they reach into the next tile at most.
   const int nk5 = (nk + 4) / 5 * 5;
   const int zbytes = nk5 == nk ? 0 : 256 * d * 2;
   // this tile's spans and the step to the next tile's (kept as differences, so a
@@ -238,9 +313,12 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const bool nxt = q >= nk5;
     const int k = nxt ? q - nk5 : q;
     const bool pad = k >= nk;
-    const uint16_t* b = s0.wb + (nxt ? dwb : 0);
+    const uint8_t* b = s0.wb + (nxt ? dwb : 0);
     const int n = s0.wn + (nxt ? dwn : 0);
-    head_issue(pad ? zero : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
+    if constexpr (W8)
+      head_issue8(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo8);
+    else
+      head_issue(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
   };
   auto issue_h = [&](int q, uint8_t* sl) __attribute__((always_inline)) {
     const bool nxt = q >= nk5;
@@ -251,19 +329,41 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     head_issue(pad ? zero : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
   };
 
-  // fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32
+  // h fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32 (bf16 W) or
+  // 4 (ks/2) + 2 (lane/32) + ks%2 (fp8 W's k order)
   int fo[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    fo[ks] = (lane & 31) * 128 + (((2 * ks + (lane >> 5)) ^ dma_swz(lane & 15)) * 16);
+  for (int ks = 0; ks < 4; ++ks) {
+    const int chunk = W8 ? 4 * (ks >> 1) + 2 * (lane >> 5) + (ks & 1) : 2 * ks + (lane >> 5);
+    fo[ks] = (lane & 31) * 128 + ((chunk ^ dma_swz(lane & 15)) * 16);
+  }
+  // fp8 W fragment pair m: row base + lane%32, chunk 2m + lane/32
+  int fo8[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) fo8[m] = (lane & 31) * 64 + (((2 * m + (lane >> 5)) ^ dma8_swz(lane & 15)) << 4);
   bf16x8 fa[2][4], fb[2][4];
+  uint4 wraw[4];  // fp8 W codes of the current pair of k-steps
   f32x16 acc[4][4];
   auto read_frags = [&](const uint8_t* sa, const uint8_t* sb, int ks, bf16x8 (&xa)[4],
                         bf16x8 (&xb)[4]) {
+    if constexpr (W8) {
+      if ((ks & 1) == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + fo[ks]);
-      xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
+        for (int i = 0; i < 4; ++i)
+          wraw[i] = *reinterpret_cast<const uint4*>(sa + (wm * 128 + i * 32) * 64 + fo8[ks >> 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xa[i] = (ks & 1) ? e4m3x8_to_bf16(wraw[i].z, wraw[i].w) : e4m3x8_to_bf16(wraw[i].x, wraw[i].y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + fo[ks]);
+        xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
+      }
     }
   };
   auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
@@ -274,10 +374,23 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
   };
   auto interleave_ds = [&]() __attribute__((always_inline)) {
+    if constexpr (W8) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (code conversion)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      }
     }
   };
   // global k-step with ring position U: W in slot 2U mod 5, h in slot 2U+1 mod 5
@@ -295,8 +408,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
       mfma_step(fa[0], fb[0]);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        if (g < DMA_LOADS_PER_OPERAND + W_LOADS)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
+        if (W8) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
       read_frags(slot[sA], slot[sB], 2, fa[0], fb[0]);
@@ -308,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     }
     // W(g+1) and h(g+1) of this wave have landed (only W(g+2) may be in flight),
     // and this wave's reads of the current slots are done
-    wait_vmcnt<DMA_LOADS_PER_OPERAND>();
+    wait_vmcnt<W_LOADS>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     if constexpr (!LAST) read_frags(slot[sA1], slot[sB1], 0, fa[0], fb[0]);
@@ -320,7 +435,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
   issue_w(0, slot[0]);
   issue_h(0, slot[1]);
   issue_w(1, slot[2]);
-  wait_vmcnt<DMA_LOADS_PER_OPERAND>();
+  wait_vmcnt<W_LOADS>();
   __builtin_amdgcn_s_barrier();
   read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
 
@@ -354,6 +469,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     const int r0 = rt * 256, v0 = vt * HEAD_BN;
     // acc[im][jn][e]: vocabulary v0 + vhalf + 32 im + 8 (e>>2) + (e&3); hidden row
     // r0 + rloc + 32 jn
+    if constexpr (W8) head_scale_rows(acc, w_scale, v0 + vhalf, V);
     // entries at or past V (last vocabulary tile) drop out of the row sums; the
     // accumulators are only read from here on
     const int vlim = V - v0 - vhalf;  // entry (im, e) is valid iff 32 im + 8 (e>>2) + (e&3) < vlim
@@ -392,82 +508,6 @@ __global__ __launch_bounds__(256, 1) void lmhead_bf16_kernel(
     dhn = s1.hn - s0.hn;
   }
   wait_vmcnt<0>();  // loads past the last tile: nothing may still target LDS at exit
-}
-
-// fp8-weight head (E4M3 codes converted to bf16 while staging; per-row fp32 scale
-// applied to the dot product).  256 rows x 256 vocabulary entries per tile.
-__global__ __launch_bounds__(256, 1) void lmhead_fp8_kernel(
-    int R, int V, int d, int n_int, int n_nodes, const uint16_t* __restrict__ h,
-    const uint8_t* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ seg,
-    const int32_t* __restrict__ e_tok, const int32_t* __restrict__ e_qrow,
-    const int32_t* __restrict__ e_child, float* __restrict__ raw, float2* __restrict__ part) {
-  constexpr int BM = 256, BN = HEAD_BN, WM = 2, WN = 2;
-  using S = GemmShape<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
-  const int nbm = (R + BM - 1) / BM, nbn = (V + BN - 1) / BN;
-  int mt, nt;
-  tile_coords<8>(nbm, nbn, mt, nt);
-  const int m0 = mt * BM, n0 = nt * BN;
-  f32x4 acc[S::MB][S::NB];
-  gemm_mainloop<BM, BN, WM, WN, true>(h, d, W, d, R, V, d, m0, n0, lds, acc);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int col_base = n0 + wn * S::TN + (lane & 15);
-  const int row_base = m0 + wm * S::TM + (lane >> 4) * 4;
-#pragma unroll
-  for (int j = 0; j < S::NB; ++j) {
-    const int col = col_base + j * 16;
-    const bool ok = col < V;
-    const float sc = ok ? w_scale[col] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = ok ? acc[i][j][r] * sc : -INFINITY;
-  }
-  const int e_lo = seg[2 * nt], e_hi = seg[2 * nt + 2];
-  if (e_lo < e_hi) {
-#pragma unroll
-    for (int j = 0; j < S::NB; ++j) {
-      const int col = col_base + j * 16;
-      for (int e = e_lo; e < e_hi; ++e) {
-        if (e_tok[e] != col) continue;
-        const int q = e_qrow[e], c = e_child[e];
-#pragma unroll
-        for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = row_base + i * 16 + r;
-            if (row < R && row % n_int == q) raw[(size_t)(row / n_int) * n_nodes + c] = acc[i][j][r];
-          }
-      }
-    }
-  }
-  float2* red = reinterpret_cast<float2*>(lds);  // [WN][BM]
-#pragma unroll
-  for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float m = acc[i][0][r];
-#pragma unroll
-      for (int j = 1; j < S::NB; ++j) m = fmaxf(m, acc[i][j][r]);
-      m = max16(m);
-      float s = 0.f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int j = 0; j < S::NB; ++j) s += __expf(acc[i][j][r] - m);
-      }
-      s = sum16(s);
-      if ((lane & 15) == 0) red[wn * BM + wm * S::TM + i * 16 + (lane >> 4) * 4 + r] = float2{m, s};
-    }
-  __syncthreads();
-  {
-    const int t = threadIdx.x;
-    float2 a = red[t];
-    const float2 b = red[BM + t];
-    lse_merge(a.x, a.y, b.x, b.y);
-    if (m0 + t < R) part[(size_t)nt * R + m0 + t] = a;
-  }
 }
 
 // fp32 head: one thread per vocabulary entry of a 256-entry tile, 8 rows per block.
@@ -616,19 +656,18 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
   Carve cv(ws);
   float2* p = cv.take<float2>(size_t(2 * n_tiles) * R);
   int32_t* seg = cv.take<int32_t>(2 * n_tiles + 1);
-  const bool bf16_head = h_dtype == TCS_BF16 && w_dtype == TCS_BF16;
-  const bool bf16_h = h_dtype == TCS_BF16;
-  const size_t zbytes = bf16_head ? head_zero_bytes(d) : 0;
-  uint4* zero = cv.take<uint4>(bf16_h ? head_zero_bytes(d) / 16 : 0);
+  const bool mfma_head = h_dtype == TCS_BF16;  // matrix-core head (bf16 or fp8 W)
+  const size_t zbytes = mfma_head ? head_zero_bytes(d) : 0;
+  uint4* zero = cv.take<uint4>(mfma_head ? head_zero_bytes(d) / 16 : 0);
   const int n_rt = (R + 255) / 256;
-  const int n_keys = bf16_head ? 2 * n_tiles * n_rt : 0;
-  const long n_pairs = bf16_head ? long(n_edges) * B : 0;
-  int32_t* list_head = cv.take<int32_t>(bf16_h ? size_t(2) * n_tiles * n_rt : 0);
-  int4* rec = cv.take<int4>(bf16_h ? size_t(n_edges) * B : 0);
+  const int n_keys = mfma_head ? 2 * n_tiles * n_rt : 0;
+  const long n_pairs = mfma_head ? long(n_edges) * B : 0;
+  int32_t* list_head = cv.take<int32_t>(mfma_head ? size_t(2) * n_tiles * n_rt : 0);
+  int4* rec = cv.take<int4>(mfma_head ? size_t(n_edges) * B : 0);
   const int n_prep = max(2 * n_tiles + 1, int(zbytes / 16));
   head_prep_kernel<<<(n_prep + 255) / 256, 256, 0, s>>>(2 * n_tiles, e_tok, n_edges, seg, zero,
                                                         int(zbytes / 16));
-  if (bf16_head) {
+  if (mfma_head) {
     head_list_init_kernel<<<(n_keys + 255) / 256, 256, 0, s>>>(n_keys, list_head);
     if (n_pairs > 0)
       head_list_link_kernel<<<int((n_pairs + 255) / 256), 256, 0, s>>>(
@@ -638,19 +677,17 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
   timer_begin(TCS_TIMER_HEAD, stream);
   if (h_dtype == TCS_BF16) {
     if (d % 64 != 0) return fail(TCS_EUNSUPPORTED, "lmhead: d=%d is not a multiple of 64", d);
-    if (w_dtype == TCS_FP8_E4M3) {
-      lmhead_fp8_kernel<<<n_rt * n_tiles, 256, 0, s>>>(R, V, d, n_int, n_nodes,
-                                                        static_cast<const uint16_t*>(h),
-                                                        static_cast<const uint8_t*>(W), w_scale, seg,
-                                                        e_tok, e_qrow, e_child, lp, p);
-    } else {
-      const int rounds = head_grid(n_rt, n_tiles) / HEAD_WGS;
-      const int per = head_rounds_per_wg(rounds);
-      lmhead_bf16_kernel<<<(rounds + per - 1) / per * HEAD_WGS, 256, 0, s>>>(
-          R, V, d, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), list_head, rec,
-          lp, p, reinterpret_cast<const uint16_t*>(zero), per);
-      n_parts = 2 * n_tiles;
-    }
+    const int rounds = head_grid(n_rt, n_tiles) / HEAD_WGS;
+    const int per = head_rounds_per_wg(rounds);
+    const int grid = (rounds + per - 1) / per * HEAD_WGS;
+    auto hp = static_cast<const uint16_t*>(h);
+    auto wp = static_cast<const uint8_t*>(W);
+    auto zp = reinterpret_cast<const uint16_t*>(zero);
+    if (w_dtype == TCS_FP8_E4M3)
+      lmhead_ring_kernel<true><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, list_head, rec, lp, p, zp, per);
+    else
+      lmhead_ring_kernel<false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, list_head, rec, lp, p, zp, per);
+    n_parts = 2 * n_tiles;
   } else {
     dim3 grid(n_tiles, (R + 7) / 8);
     lmhead_f32_kernel<<<grid, 256, 0, s>>>(R, V, d, n_int, n_nodes, static_cast<const float*>(h),

@@ -1,5 +1,5 @@
-// Device helpers shared by the gfx950 kernels: bf16 / fp8 conversion, MFMA operand
-// types, wavefront reductions.
+// Device helpers shared by the gfx950 kernels: bf16 conversion, MFMA operand types,
+// LDS-DMA helpers, wavefront reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,6 +11,8 @@ namespace tcs {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Storage tags: the kernels move bf16 as raw 16-bit patterns.
 struct bf16_t {
@@ -39,19 +41,6 @@ template <>
 __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return bf16_t{f32_to_bf16(v)}; }
-
-// One OCP E4M3FN byte -> its bf16 bit pattern (exact: every E4M3 value is a bf16
-// value).  A normal code (exponent field e >= 1, bias 7) maps to bf16 exponent
-// field e + 120 with the 3 mantissa bits moved up by 4; a subnormal code (e == 0,
-// value m * 2^-9) is converted through fp32.
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t byte) {
-  const uint32_t s = (byte & 0x80u) << 8;
-  const uint32_t em = byte & 0x7Fu;
-  const uint32_t normal = (em << 4) + (120u << 7);
-  // m * 2^-9 is exact in fp32 and in bf16; its bf16 pattern is the top half
-  const uint32_t sub = __float_as_uint(float(em) * 0x1p-9f) >> 16;
-  return s | (em >= 8u ? normal : sub);
-}
 
 // LDS pointer for the buffer-to-LDS load builtins.
 #define TCS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
