@@ -240,13 +240,47 @@ typedef struct {
  * output projection + residual + RMSNorm, output head with LSE and gather, path
  * sums, label softmax and argmax.
  *   label [B] int32 out; prob [B, M] fp32 out or NULL; ll [B, M] fp32 out or NULL.
- *   ws    workspace of tcs_classify_workspace_bytes(model, trie, docs) bytes.
+ *   ws    workspace of tcs_classify_workspace_bytes(model, trie, docs) bytes (the
+ *         prepared state of tcs_classify_prepare followed by a run workspace).
  */
 size_t tcs_classify_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
                                     const tcs_docs* docs);
 int tcs_classify(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* trie,
                  const tcs_docs* docs, int32_t* label, float* prob, float* ll, void* ws,
                  size_t ws_bytes);
+
+/*
+ * The same pass split at the label set.  In this single-layer model a trie node's
+ * q, k and v come from its token alone and its attention over its own path
+ * ("attend only to the prompt and your own path", section 3.2) does not involve
+ * the document, so they are computed once per label set; so are the output head's
+ * gather lists, which depend only on the trie and the batch size B.  The pages run
+ * one label set over a whole table of documents (section 2), so this work is paid
+ * once per query rather than once per batch.
+ *
+ * tcs_classify_prepare fills a caller-owned device buffer of
+ * tcs_classify_prepared_bytes(model, trie, B) bytes (prep->buf, prep->bytes set
+ * by the caller; prep->B is written) with the node q/k/v, the per-(node, head) path
+ * partials and the gather lists for batches of exactly B documents.  The buffer
+ * must stay untouched while runs use it; the trie and weights must not change.
+ * tcs_classify_run scores one batch (docs->B == prep->B) with that state on a
+ * workspace of tcs_classify_run_workspace_bytes(model, trie, docs) bytes; it gives
+ * the same results as tcs_classify.  Errors: EINVAL for a batch size other than
+ * prep->B or null pointers; ECAPACITY for short buffers.
+ */
+typedef struct {
+  int32_t B;     /* batch size the state was prepared for (written by prepare) */
+  void* buf;     /* device buffer, caller-owned */
+  size_t bytes;  /* its size */
+} tcs_prepared;
+size_t tcs_classify_prepared_bytes(const tcs_model* model, const tcs_trie_dev* trie, int32_t B);
+int tcs_classify_prepare(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* trie,
+                         int32_t B, tcs_prepared* prep);
+size_t tcs_classify_run_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
+                                        const tcs_docs* docs);
+int tcs_classify_run(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* trie,
+                     const tcs_docs* docs, const tcs_prepared* prep, int32_t* label, float* prob,
+                     float* ll, void* ws, size_t ws_bytes);
 
 /* ----------------------------------------------------------- measurement ---- */
 /*

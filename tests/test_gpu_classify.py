@@ -17,13 +17,16 @@ def _torch():
     return torch
 
 
-def run_gpu(cfg, inp):
+def run_gpu(cfg, inp, prepared=False):
+    """tcs_classify, or (prepared) tcs_classify_prepare + tcs_classify_run as bench.py
+    times it."""
     torch = _torch()
     t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
     td = tcs.TrieDevice(t)
     model = tcs.Model(cfg, inp)
     docs = tcs.Docs(cfg, inp)
-    label, prob, ll = tcs.classify(model, td, docs)
+    prep = tcs.Prepared(model, td, docs.B) if prepared else None
+    label, prob, ll = tcs.classify(model, td, docs, prepared=prep)
     torch.cuda.synchronize()
     out = label.cpu().numpy(), prob.cpu().numpy(), ll.cpu().numpy()
     del model, docs
@@ -52,6 +55,30 @@ def test_classify_small_vs_oracle(dev, name):
     check_labels(ll, prob, label, o["ll"], o["prob"], o["label"], f"classify[{name}]")
 
 
+@pytest.mark.parametrize("name", ["tiny-f32", "running-bf16-small", "zipf-bf16-small", "fp8-small"])
+def test_prepared_run_equals_classify(dev, name):
+    """tcs_classify_run on prepared state gives tcs_classify's results bit for bit,
+    for two batches in a row on the same state; a batch of another size is refused."""
+    torch = _torch()
+    cfg = SMALL[name]
+    inp = make_inputs(cfg, seed=101)
+    t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(t)
+    model = tcs.Model(cfg, inp)
+    docs = tcs.Docs(cfg, inp)
+    ref = [x.cpu().numpy() for x in tcs.classify(model, td, docs)]
+    prep = tcs.Prepared(model, td, docs.B)
+    for _ in range(2):
+        got = [x.cpu().numpy() for x in tcs.classify(model, td, docs, prepared=prep)]
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            np.testing.assert_array_equal(a, b)
+    other = tcs.Prepared(model, td, docs.B + 1)
+    with pytest.raises(tcs.TcsError):
+        tcs.classify(model, td, docs, prepared=other)
+    say(f"prepared[{name}]: run == classify on 2 batches")
+
+
 @pytest.fixture(scope="module")
 def cfg2():
     cfg = config(2)
@@ -68,7 +95,7 @@ def cfg5():
 def test_classify_full_size_sampled_docs(dev, which, request):
     """Running-example trie at full size: every label of sampled documents."""
     cfg, inp = request.getfixturevalue(which)
-    label, prob, ll = run_gpu(cfg, inp)
+    label, prob, ll = run_gpu(cfg, inp, prepared=True)
     docs = [0, 1, cfg.B // 2, cfg.B - 1]
     o = O.classify(inp, docs=docs)
     check_labels(ll[docs], prob[docs], label[docs], o["ll"], o["prob"], o["label"],
@@ -82,7 +109,7 @@ def test_classify_full_size_sampled_labels(dev, cid):
     oracle's path-restricted pass; probabilities and labels by their properties."""
     cfg = config(cid)
     inp = make_inputs(cfg)
-    label, prob, ll = run_gpu(cfg, inp)
+    label, prob, ll = run_gpu(cfg, inp, prepared=True)
     M = len(inp["labels"])
     rng = np.random.default_rng(cid)
     model = O.OracleModel(inp)

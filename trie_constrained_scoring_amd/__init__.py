@@ -64,6 +64,10 @@ class tcs_docs(C.Structure):
                 ("Kd", C.c_void_p), ("Vd", C.c_void_p), ("doc_tokens", C.c_void_p)]
 
 
+class tcs_prepared(C.Structure):
+    _fields_ = [("B", C.c_int32), ("buf", C.c_void_p), ("bytes", C.c_size_t)]
+
+
 _lib_handle = None
 
 
@@ -93,6 +97,15 @@ def lib():
                                                    C.POINTER(tcs_docs)]
         L.tcs_classify.argtypes = [vp, C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
                                    C.POINTER(tcs_docs), vp, vp, vp, vp, sz]
+        L.tcs_classify_prepared_bytes.restype = sz
+        L.tcs_classify_prepared_bytes.argtypes = [C.POINTER(tcs_model), C.POINTER(tcs_trie_dev), i32]
+        L.tcs_classify_prepare.argtypes = [vp, C.POINTER(tcs_model), C.POINTER(tcs_trie_dev), i32,
+                                           C.POINTER(tcs_prepared)]
+        L.tcs_classify_run_workspace_bytes.restype = sz
+        L.tcs_classify_run_workspace_bytes.argtypes = [C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
+                                                       C.POINTER(tcs_docs)]
+        L.tcs_classify_run.argtypes = [vp, C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
+                                       C.POINTER(tcs_docs), C.POINTER(tcs_prepared), vp, vp, vp, vp, sz]
         L.tcs_timing_enable.argtypes = [C.c_int]
         L.tcs_timing_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i32)]
         _lib_handle = L
@@ -372,9 +385,35 @@ def classify_workspace_bytes(model: Model, trie_dev: TrieDevice, docs: Docs) -> 
     return n
 
 
+class Prepared:
+    """Per-label-set state of classify for batches of B documents (tcs_classify_prepare):
+    a device buffer owned here, valid while the model and trie stay unchanged."""
+
+    def __init__(self, model: Model, trie_dev: TrieDevice, B: int, stream=None):
+        torch = _torch()
+        n = int(lib().tcs_classify_prepared_bytes(C.byref(model.struct), C.byref(trie_dev.struct), B))
+        if n == 0:
+            _check(TCS_EINVAL)
+        self.buf = torch.empty(n, dtype=torch.uint8, device=trie_dev["parent"].device)
+        _need_cuda(self.buf)
+        self.struct = tcs_prepared(B=0, buf=self.buf.data_ptr(), bytes=n)
+        _check(lib().tcs_classify_prepare(_stream(stream), C.byref(model.struct),
+                                          C.byref(trie_dev.struct), B, C.byref(self.struct)))
+        self.B = B
+
+
+def classify_run_workspace_bytes(model: Model, trie_dev: TrieDevice, docs: Docs) -> int:
+    n = int(lib().tcs_classify_run_workspace_bytes(C.byref(model.struct), C.byref(trie_dev.struct),
+                                                   C.byref(docs.struct)))
+    if n == 0:
+        _check(TCS_EINVAL)
+    return n
+
+
 def classify(model: Model, trie_dev: TrieDevice, docs: Docs, label=None, prob=None, ll=None,
-             with_prob=True, ws=None, stream=None):
-    """The whole trie_tree pass (tcs_classify).  Returns (label [B], prob [B, M], ll [B, M])."""
+             with_prob=True, ws=None, stream=None, prepared: Prepared = None):
+    """The whole trie_tree pass (tcs_classify), or with `prepared` one batch on
+    per-label-set state (tcs_classify_run).  Returns (label [B], prob [B, M], ll [B, M])."""
     torch = _torch()
     B, M = docs.B, trie_dev.trie.n_labels
     dev = docs.offsets.device
@@ -384,11 +423,20 @@ def classify(model: Model, trie_dev: TrieDevice, docs: Docs, label=None, prob=No
         prob = torch.empty((B, M), dtype=torch.float32, device=dev)
     if ll is None:
         ll = torch.empty((B, M), dtype=torch.float32, device=dev)
-    need = classify_workspace_bytes(model, trie_dev, docs)
+    if prepared is None:
+        need = classify_workspace_bytes(model, trie_dev, docs)
+    else:
+        need = classify_run_workspace_bytes(model, trie_dev, docs)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _need_cuda(label, prob, ll, ws)
-    _check(lib().tcs_classify(_stream(stream), C.byref(model.struct), C.byref(trie_dev.struct),
-                              C.byref(docs.struct), _ptr(label), _ptr(prob), _ptr(ll), _ptr(ws),
-                              ws.numel()))
+    if prepared is None:
+        _check(lib().tcs_classify(_stream(stream), C.byref(model.struct), C.byref(trie_dev.struct),
+                                  C.byref(docs.struct), _ptr(label), _ptr(prob), _ptr(ll), _ptr(ws),
+                                  ws.numel()))
+    else:
+        _check(lib().tcs_classify_run(_stream(stream), C.byref(model.struct),
+                                      C.byref(trie_dev.struct), C.byref(docs.struct),
+                                      C.byref(prepared.struct), _ptr(label), _ptr(prob), _ptr(ll),
+                                      _ptr(ws), ws.numel()))
     return label, prob, ll

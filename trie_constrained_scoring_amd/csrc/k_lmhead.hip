@@ -632,47 +632,85 @@ static size_t head_zero_bytes(int32_t d) {
   return nk % 5 == 0 ? 0 : size_t(256) * d * 2;
 }
 
-size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
-                       int32_t V) {
+// Per-label-set part of the head's workspace: the edge segment table (fp32 head),
+// the zero block and the gather lists (matrix-core head), for batches of B documents.
+struct HeadPrep {
+  int32_t* seg;
+  uint4* zero;
+  int32_t* list_head;
+  int4* rec;
+};
+static HeadPrep head_prep_layout(Carve& cv, tcs_dtype h_dtype, int32_t B, int32_t n_int,
+                                 int32_t n_nodes, int32_t d, int32_t V) {
   const size_t R = size_t(B) * n_int;
   const size_t n_tiles = size_t(lmhead_n_tiles(h_dtype, V));
-  size_t n = align_up(2 * n_tiles * R * 8) + align_up((2 * n_tiles + 1) * 4);
-  if (h_dtype == TCS_BF16) {  // zero block and gather lists of the bf16 head
-    const size_t n_rt = (R + 255) / 256;
-    n += align_up(head_zero_bytes(d)) + align_up(2 * n_tiles * n_rt * 4) +
-         align_up(size_t(n_nodes - 1) * B * 16);
-  }
-  return n;
+  const bool mfma_head = h_dtype == TCS_BF16;
+  const size_t n_rt = (R + 255) / 256;
+  HeadPrep P;
+  P.seg = cv.take<int32_t>(2 * n_tiles + 1);
+  P.zero = cv.take<uint4>(mfma_head ? head_zero_bytes(d) / 16 : 0);
+  P.list_head = cv.take<int32_t>(mfma_head ? 2 * n_tiles * n_rt : 0);
+  P.rec = cv.take<int4>(mfma_head ? size_t(n_nodes - 1) * B : 0);
+  return P;
 }
 
-int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
-                  int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
-                  const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
-                  const int32_t* e_child, int32_t n_edges, float* lse, float* lp, void* ws) {
+size_t lmhead_prep_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
+                         int32_t V) {
+  Carve cv(nullptr);
+  head_prep_layout(cv, h_dtype, B, n_int, n_nodes, d, V);
+  return cv.used;
+}
+
+size_t lmhead_part_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t V) {
+  const size_t parts = size_t(lmhead_n_tiles(h_dtype, V)) * (h_dtype == TCS_BF16 ? 2 : 1);
+  return align_up(parts * size_t(B) * n_int * 8);
+}
+
+size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
+                       int32_t V) {
+  return lmhead_prep_bytes(h_dtype, B, n_int, n_nodes, d, V) + lmhead_part_bytes(h_dtype, B, n_int, V);
+}
+
+int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
+                       int32_t d, int32_t V, const int32_t* e_tok, const int32_t* e_qrow,
+                       const int32_t* e_child, int32_t n_edges, void* prep) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = B * n_int;
   if (R <= 0) return TCS_OK;
   const int n_tiles = lmhead_n_tiles(h_dtype, V);
-  Carve cv(ws);
-  float2* p = cv.take<float2>(size_t(2 * n_tiles) * R);
-  int32_t* seg = cv.take<int32_t>(2 * n_tiles + 1);
-  const bool mfma_head = h_dtype == TCS_BF16;  // matrix-core head (bf16 or fp8 W)
+  Carve cv(prep);
+  const HeadPrep P = head_prep_layout(cv, h_dtype, B, n_int, n_nodes, d, V);
+  const bool mfma_head = h_dtype == TCS_BF16;
   const size_t zbytes = mfma_head ? head_zero_bytes(d) : 0;
-  uint4* zero = cv.take<uint4>(mfma_head ? head_zero_bytes(d) / 16 : 0);
   const int n_rt = (R + 255) / 256;
   const int n_keys = mfma_head ? 2 * n_tiles * n_rt : 0;
   const long n_pairs = mfma_head ? long(n_edges) * B : 0;
-  int32_t* list_head = cv.take<int32_t>(mfma_head ? size_t(2) * n_tiles * n_rt : 0);
-  int4* rec = cv.take<int4>(mfma_head ? size_t(n_edges) * B : 0);
   const int n_prep = max(2 * n_tiles + 1, int(zbytes / 16));
-  head_prep_kernel<<<(n_prep + 255) / 256, 256, 0, s>>>(2 * n_tiles, e_tok, n_edges, seg, zero,
+  head_prep_kernel<<<(n_prep + 255) / 256, 256, 0, s>>>(2 * n_tiles, e_tok, n_edges, P.seg, P.zero,
                                                         int(zbytes / 16));
   if (mfma_head) {
-    head_list_init_kernel<<<(n_keys + 255) / 256, 256, 0, s>>>(n_keys, list_head);
+    head_list_init_kernel<<<(n_keys + 255) / 256, 256, 0, s>>>(n_keys, P.list_head);
     if (n_pairs > 0)
       head_list_link_kernel<<<int((n_pairs + 255) / 256), 256, 0, s>>>(
-          B, n_int, n_nodes, n_rt, e_tok, e_qrow, e_child, n_edges, list_head, rec);
+          B, n_int, n_nodes, n_rt, e_tok, e_qrow, e_child, n_edges, P.list_head, P.rec);
   }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TCS_EHIP, "lmhead prep: %s", hipGetErrorString(e));
+  return TCS_OK;
+}
+
+int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                      int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
+                      const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
+                      const int32_t* e_child, float* lse, float* lp, const void* prep, void* part) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int R = B * n_int;
+  if (R <= 0) return TCS_OK;
+  const int n_tiles = lmhead_n_tiles(h_dtype, V);
+  Carve cv(const_cast<void*>(prep));
+  const HeadPrep P = head_prep_layout(cv, h_dtype, B, n_int, n_nodes, d, V);
+  float2* p = static_cast<float2*>(part);
+  const int n_rt = (R + 255) / 256;
   int n_parts = n_tiles;
   timer_begin(TCS_TIMER_HEAD, stream);
   if (h_dtype == TCS_BF16) {
@@ -682,16 +720,16 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
     const int grid = (rounds + per - 1) / per * HEAD_WGS;
     auto hp = static_cast<const uint16_t*>(h);
     auto wp = static_cast<const uint8_t*>(W);
-    auto zp = reinterpret_cast<const uint16_t*>(zero);
+    auto zp = reinterpret_cast<const uint16_t*>(P.zero);
     if (w_dtype == TCS_FP8_E4M3)
-      lmhead_ring_kernel<true><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, list_head, rec, lp, p, zp, per);
+      lmhead_ring_kernel<true><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per);
     else
-      lmhead_ring_kernel<false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, list_head, rec, lp, p, zp, per);
+      lmhead_ring_kernel<false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per);
     n_parts = 2 * n_tiles;
   } else {
     dim3 grid(n_tiles, (R + 7) / 8);
     lmhead_f32_kernel<<<grid, 256, 0, s>>>(R, V, d, n_int, n_nodes, static_cast<const float*>(h),
-                                           static_cast<const float*>(W), seg, e_tok, e_qrow, e_child,
+                                           static_cast<const float*>(W), P.seg, e_tok, e_qrow, e_child,
                                            lp, p);
   }
   timer_end(TCS_TIMER_HEAD, stream);
@@ -707,6 +745,18 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "lmhead finalize: %s", hipGetErrorString(e));
   return TCS_OK;
+}
+
+int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                  int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
+                  const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
+                  const int32_t* e_child, int32_t n_edges, float* lse, float* lp, void* ws) {
+  const size_t pb = lmhead_prep_bytes(h_dtype, B, n_int, n_nodes, d, V);
+  if (int rc = launch_lmhead_prep(stream, h_dtype, B, n_int, n_nodes, d, V, e_tok, e_qrow, e_child,
+                                  n_edges, ws))
+    return rc;
+  return launch_lmhead_run(stream, h_dtype, w_dtype, B, n_int, n_nodes, d, V, h, W, w_scale, e_tok,
+                           e_qrow, e_child, lse, lp, ws, static_cast<char*>(ws) + pb);
 }
 
 }  // namespace tcs

@@ -131,34 +131,52 @@ int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie,
 
 // ---------------------------------------------------------------- classify
 
-struct ClassifyLayout {
+// Per-label-set state (tcs_classify_prepare): node input rows, node q/k/v, the path
+// partials (bf16 models) and the head's gather lists for B documents.
+struct PrepLayout {
   size_t total;
-  void *a_nodes, *Qn, *Kn, *Vn, *a_doc, *Kd, *Vd, *anc, *O, *h, *part, *ll;
+  void *a_nodes, *Qn, *Kn, *Vn, *anc, *head;
+};
+
+static PrepLayout prep_layout(const tcs_model* m, const tcs_trie_dev* t, int32_t B, void* buf) {
+  const size_t es = dtype_bytes(m->dtype);
+  const size_t n_int = t->n_int;
+  const size_t qd = size_t(m->Hq) * m->hd, kd = size_t(m->Hkv) * m->hd;
+  Carve c(buf);
+  PrepLayout P{};
+  P.a_nodes = c.take<char>(n_int * m->d * es);
+  P.Qn = c.take<char>(n_int * qd * es);
+  P.Kn = c.take<char>(n_int * kd * es);
+  P.Vn = c.take<char>(n_int * kd * es);
+  P.anc = c.take<char>(m->dtype == TCS_BF16 ? anc_bytes(t->n_int, m->Hq, m->hd) : 0);
+  P.head = c.take<char>(lmhead_prep_bytes(m->dtype, B, t->n_int, t->n_nodes, m->d, m->V));
+  P.total = c.used;
+  return P;
+}
+
+// Per-batch workspace (tcs_classify_run).
+struct RunLayout {
+  size_t total;
+  void *a_doc, *Kd, *Vd, *O, *h, *part, *ll;
   float *y, *lse, *lp;
 };
 
-static ClassifyLayout classify_layout(const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
-                                      void* ws) {
+static RunLayout run_layout(const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d, void* ws) {
   const size_t es = dtype_bytes(m->dtype);
-  const size_t n_int = t->n_int, R = size_t(d->B) * t->n_int;
+  const size_t R = size_t(d->B) * t->n_int;
   const size_t qd = size_t(m->Hq) * m->hd, kd = size_t(m->Hkv) * m->hd;
   Carve c(ws);
-  ClassifyLayout L{};
-  L.a_nodes = c.take<char>(n_int * m->d * es);
-  L.Qn = c.take<char>(n_int * qd * es);
-  L.Kn = c.take<char>(n_int * kd * es);
-  L.Vn = c.take<char>(n_int * kd * es);
+  RunLayout L{};
   if (!d->Kd) {
     const size_t T = d->total_tokens;
     L.a_doc = c.take<char>(T * m->d * es);
     L.Kd = c.take<char>(T * kd * es);
     L.Vd = c.take<char>(T * kd * es);
   }
-  L.anc = c.take<char>(anc_bytes(t->n_int, m->Hq, m->hd));
   L.O = c.take<char>(R * qd * es);
   L.y = c.take<float>(R * m->d * gemm_resid_splits(m->dtype, int32_t(R), m->d, int32_t(qd)));
   L.h = c.take<char>(R * m->d * es);
-  L.part = c.take<char>(lmhead_ws_bytes(m->dtype, d->B, t->n_int, t->n_nodes, m->d, m->V));
+  L.part = c.take<char>(lmhead_part_bytes(m->dtype, d->B, t->n_int, m->V));
   L.lse = c.take<float>(R);
   L.lp = c.take<float>(size_t(d->B) * t->n_nodes);
   L.ll = c.take<float>(size_t(d->B) * t->n_labels);
@@ -192,31 +210,46 @@ static int check_classify(const tcs_model* m, const tcs_trie_dev* t, const tcs_d
   return TCS_OK;
 }
 
-size_t tcs_classify_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
-                                    const tcs_docs* docs) {
-  if (check_classify(model, trie, docs)) return 0;
-  return classify_layout(model, trie, docs, nullptr).total;
+static int check_model_trie(const tcs_model* m, const tcs_trie_dev* t) {
+  if (!m || !t) return fail(TCS_EINVAL, "classify: null model/trie");
+  tcs_docs none{};
+  return check_classify(m, t, &none);
 }
 
-int tcs_classify(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
-                 int32_t* label, float* prob, float* ll, void* ws, size_t ws_bytes) {
-  clear_error();
-  if (int rc = check_classify(m, t, d)) return rc;
-  if (d->B == 0) return TCS_OK;
-  if (!label) return fail(TCS_EINVAL, "classify: null label output");
-  const ClassifyLayout L = classify_layout(m, t, d, ws);
-  if (!ws || ws_bytes < L.total)
-    return fail(TCS_ECAPACITY, "classify: workspace %zu < %zu bytes", ws_bytes, L.total);
+// Node input block, path partials and head gather lists for batches of B documents.
+static int prepare_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, int32_t B,
+                        void* buf) {
+  const PrepLayout P = prep_layout(m, t, B, buf);
+  const tcs_dtype dt = m->dtype;
+  const int n_int = t->n_int;
+  const int qd = m->Hq * m->hd, kd = m->Hkv * m->hd;
+  const float scale = 1.0f / std::sqrt(float(m->hd));
+  int rc;
+  // a = RMSNorm(E[token]); q, k, v
+  if ((rc = launch_embed_rmsnorm(stream, dt, m->E, t->qnode, t->token, n_int, m->d, m->V, m->eps, P.a_nodes))) return rc;
+  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, qd, m->d, P.a_nodes, m->d, m->Wq, m->d, P.Qn, qd, nullptr))) return rc;
+  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, kd, m->d, P.a_nodes, m->d, m->Wk, m->d, P.Kn, kd, nullptr))) return rc;
+  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, kd, m->d, P.a_nodes, m->d, m->Wv, m->d, P.Vn, kd, nullptr))) return rc;
+  if (dt == TCS_BF16) {
+    Carve c(P.anc);
+    float* ml = c.take<float>(size_t(n_int) * m->Hq * 2);
+    float* ao = c.take<float>(size_t(n_int) * m->Hq * m->hd);
+    if ((rc = launch_anc_attn(stream, dt, n_int, m->Hq, m->Hkv, m->hd, P.Qn, P.Kn, P.Vn, t->qparent, scale, ml, ao))) return rc;
+  }
+  return launch_lmhead_prep(stream, dt, B, n_int, t->n_nodes, m->d, m->V, t->e_tok, t->e_qrow,
+                            t->e_child, t->n_nodes - 1, P.head);
+}
+
+// One batch on prepared state.
+static int run_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
+                    const void* prep_buf, int32_t* label, float* prob, float* ll, void* ws) {
+  const PrepLayout P = prep_layout(m, t, d->B, const_cast<void*>(prep_buf));
+  const RunLayout L = run_layout(m, t, d, ws);
   const tcs_dtype dt = m->dtype;
   const int n_int = t->n_int, B = d->B, R = B * n_int;
   const int qd = m->Hq * m->hd, kd = m->Hkv * m->hd;
   const float scale = 1.0f / std::sqrt(float(m->hd));
   int rc;
-  // node input block: a = RMSNorm(E[token]); q, k, v
-  if ((rc = launch_embed_rmsnorm(stream, dt, m->E, t->qnode, t->token, n_int, m->d, m->V, m->eps, L.a_nodes))) return rc;
-  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, qd, m->d, L.a_nodes, m->d, m->Wq, m->d, L.Qn, qd, nullptr))) return rc;
-  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, kd, m->d, L.a_nodes, m->d, m->Wk, m->d, L.Kn, kd, nullptr))) return rc;
-  if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, n_int, kd, m->d, L.a_nodes, m->d, m->Wv, m->d, L.Vn, kd, nullptr))) return rc;
   const void* Kd = d->Kd;
   const void* Vd = d->Vd;
   if (!Kd) {  // documents given as tokens: their k and v through the same input block
@@ -227,17 +260,88 @@ int tcs_classify(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, c
     Kd = L.Kd;
     Vd = L.Vd;
   }
-  if ((rc = tree_attn_impl(stream, dt, B, n_int, m->Hq, m->Hkv, m->hd, L.Qn, L.Kn, L.Vn, Kd, Vd,
-                           d->doc_offsets, t->qparent, scale, L.O, L.anc))) return rc;
+  if (dt == TCS_F32) {
+    rc = launch_attn_simt(stream, dt, B, n_int, m->Hq, m->Hkv, m->hd, P.Qn, P.Kn, P.Vn, Kd, Vd,
+                          d->doc_offsets, t->qparent, scale, L.O);
+  } else {
+    Carve c(P.anc);
+    const float* ml = c.take<float>(size_t(n_int) * m->Hq * 2);
+    const float* ao = c.take<float>(size_t(n_int) * m->Hq * m->hd);
+    rc = launch_doc_attn(stream, dt, B, n_int, m->Hq, m->Hkv, m->hd, P.Qn, Kd, Vd, d->doc_offsets,
+                         ml, ao, scale, L.O);
+  }
+  if (rc) return rc;
   // y = x + O Wo^T ; h = RMSNorm(y)
   GemmResid res{m->E, t->token, t->qnode, n_int};
   if ((rc = launch_gemm_nt(stream, dt, GEMM_RESID, R, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d, &res))) return rc;
   if ((rc = launch_rownorm(stream, dt, L.y, R, m->d, gemm_resid_splits(dt, R, m->d, qd), m->eps,
                            L.h))) return rc;
-  if ((rc = launch_lmhead(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,
-                          m->W_scale, t->e_tok, t->e_qrow, t->e_child, t->n_nodes - 1, L.lse, L.lp,
-                          L.part))) return rc;
+  if ((rc = launch_lmhead_run(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,
+                              m->W_scale, t->e_tok, t->e_qrow, t->e_child, L.lse, L.lp, P.head,
+                              L.part))) return rc;
   return launch_path_sum(stream, B, t, L.lp, ll ? ll : static_cast<float*>(L.ll), prob, label);
+}
+
+size_t tcs_classify_prepared_bytes(const tcs_model* model, const tcs_trie_dev* trie, int32_t B) {
+  if (B < 1 || check_model_trie(model, trie) || int64_t(B) * trie->n_int > INT32_MAX) return 0;
+  return prep_layout(model, trie, B, nullptr).total;
+}
+
+int tcs_classify_prepare(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, int32_t B,
+                         tcs_prepared* prep) {
+  clear_error();
+  if (int rc = check_model_trie(m, t)) return rc;
+  if (!prep || !prep->buf) return fail(TCS_EINVAL, "classify_prepare: null prepared buffer");
+  if (B < 1 || int64_t(B) * t->n_int > INT32_MAX) return fail(TCS_EINVAL, "classify_prepare: B=%d", B);
+  const size_t need = prep_layout(m, t, B, nullptr).total;
+  if (prep->bytes < need)
+    return fail(TCS_ECAPACITY, "classify_prepare: buffer %zu < %zu bytes", prep->bytes, need);
+  prep->B = B;
+  return prepare_impl(stream, m, t, B, prep->buf);
+}
+
+size_t tcs_classify_run_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
+                                        const tcs_docs* docs) {
+  if (check_classify(model, trie, docs)) return 0;
+  return run_layout(model, trie, docs, nullptr).total;
+}
+
+int tcs_classify_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
+                     const tcs_prepared* prep, int32_t* label, float* prob, float* ll, void* ws,
+                     size_t ws_bytes) {
+  clear_error();
+  if (int rc = check_classify(m, t, d)) return rc;
+  if (d->B == 0) return TCS_OK;
+  if (!label) return fail(TCS_EINVAL, "classify: null label output");
+  if (!prep || !prep->buf) return fail(TCS_EINVAL, "classify_run: null prepared state");
+  if (prep->B != d->B)
+    return fail(TCS_EINVAL, "classify_run: state prepared for B=%d, batch has B=%d", prep->B, d->B);
+  if (prep->bytes < prep_layout(m, t, d->B, nullptr).total)
+    return fail(TCS_ECAPACITY, "classify_run: prepared buffer too small");
+  const size_t need = run_layout(m, t, d, nullptr).total;
+  if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "classify_run: workspace %zu < %zu bytes", ws_bytes, need);
+  return run_impl(stream, m, t, d, prep->buf, label, prob, ll, ws);
+}
+
+size_t tcs_classify_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
+                                    const tcs_docs* docs) {
+  if (check_classify(model, trie, docs)) return 0;
+  const int32_t B = docs->B > 0 ? docs->B : 1;
+  return prep_layout(model, trie, B, nullptr).total + run_layout(model, trie, docs, nullptr).total;
+}
+
+int tcs_classify(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
+                 int32_t* label, float* prob, float* ll, void* ws, size_t ws_bytes) {
+  clear_error();
+  if (int rc = check_classify(m, t, d)) return rc;
+  if (d->B == 0) return TCS_OK;
+  if (!label) return fail(TCS_EINVAL, "classify: null label output");
+  const size_t pb = prep_layout(m, t, d->B, nullptr).total;
+  const size_t need = pb + run_layout(m, t, d, nullptr).total;
+  if (!ws || ws_bytes < need)
+    return fail(TCS_ECAPACITY, "classify: workspace %zu < %zu bytes", ws_bytes, need);
+  if (int rc = prepare_impl(stream, m, t, d->B, ws)) return rc;
+  return run_impl(stream, m, t, d, ws, label, prob, ll, static_cast<char*>(ws) + pb);
 }
 
 }  // extern "C"

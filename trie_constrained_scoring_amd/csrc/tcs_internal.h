@@ -63,11 +63,23 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
                    const void* A, int32_t lda, const void* B, int32_t ldb, void* C, int32_t ldc,
                    const GemmResid* resid);
 
-// Output head, see tcs_lmhead_lse_gather.  The workspace holds n_tiles * R float2
-// partials and the per-tile edge segment table.
+// Output head, see tcs_lmhead_lse_gather.  Its workspace is a per-label-set part
+// (lmhead_prep_bytes: edge segments, zero block, gather lists for batches of B
+// documents; written by launch_lmhead_prep) followed by the per-batch (max, sum exp)
+// partials (lmhead_part_bytes).  launch_lmhead does both on one workspace.
 int lmhead_n_tiles(tcs_dtype h_dtype, int32_t V);
+size_t lmhead_prep_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
+                         int32_t V);
+size_t lmhead_part_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t V);
 size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
                        int32_t V);
+int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
+                       int32_t d, int32_t V, const int32_t* e_tok, const int32_t* e_qrow,
+                       const int32_t* e_child, int32_t n_edges, void* prep);
+int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                      int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
+                      const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
+                      const int32_t* e_child, float* lse, float* lp, const void* prep, void* part);
 int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
                   int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                   const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
