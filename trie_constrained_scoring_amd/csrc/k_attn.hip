@@ -18,6 +18,12 @@ namespace tcs {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Two floats -> packed bf16 (round to nearest even, hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------- fp32 path
 // One wave per (document, query row, head): keys are the document's keys, then
 // the path from the row up to the root.
@@ -283,10 +289,8 @@ __global__ __launch_bounds__(256) void doc_attn_mfma_kernel(
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
         const float a = p[8 * st + 2 * q2], c2 = p[8 * st + 2 * q2 + 1];
-        const uint16_t ah = f32_to_bf16(a), ch = f32_to_bf16(c2);
-        const uint16_t al = f32_to_bf16(a - bf16_to_f32(ah)), cl = f32_to_bf16(c2 - bf16_to_f32(ch));
-        wh[q2] = uint32_t(ah) | (uint32_t(ch) << 16);
-        wl[q2] = uint32_t(al) | (uint32_t(cl) << 16);
+        wh[q2] = pack_bf16(a, c2);
+        wl[q2] = pack_bf16(a - __uint_as_float(wh[q2] << 16), c2 - __uint_as_float(wh[q2] & 0xFFFF0000u));
       }
       uint4 uh{wh[0], wh[1], wh[2], wh[3]}, ul{wl[0], wl[1], wl[2], wl[3]};
       ph[st] = *reinterpret_cast<bf16x8*>(&uh);
@@ -397,11 +401,6 @@ __device__ __forceinline__ bf16x8 lds_read_tr_x2(const uint8_t* p0, const uint8_
   return __builtin_bit_cast(bf16x8, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
-// Two floats -> packed bf16 (round to nearest even, hardware conversion).
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // NLD 1 KB buffer-to-LDS loads of one operand stage: load j writes dst + 1 KB j,
 // lane i at 16 i, from byte vo[j] of a buffer resource over [base, base + bytes).
@@ -835,10 +834,8 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
           const float a = p[8 * st + 2 * q2], c2 = p[8 * st + 2 * q2 + 1];
-          const uint16_t ah = f32_to_bf16(a), ch = f32_to_bf16(c2);
-          const uint16_t al = f32_to_bf16(a - bf16_to_f32(ah)), cl = f32_to_bf16(c2 - bf16_to_f32(ch));
-          wh[q2] = uint32_t(ah) | (uint32_t(ch) << 16);
-          wl[q2] = uint32_t(al) | (uint32_t(cl) << 16);
+          wh[q2] = pack_bf16(a, c2);
+          wl[q2] = pack_bf16(a - __uint_as_float(wh[q2] << 16), c2 - __uint_as_float(wh[q2] & 0xFFFF0000u));
         }
         uint4 uh{wh[0], wh[1], wh[2], wh[3]}, ul{wl[0], wl[1], wl[2], wl[3]};
         ph[st] = *reinterpret_cast<bf16x8*>(&uh);

@@ -228,12 +228,12 @@ __global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const T* __restrict_
   for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(to_f32(x[i]) * rs);
 }
 
+// Any d: one workgroup per row, two passes over y.
 template <typename T>
-__global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ y, int n, int d,
-                                                      int n_part, float eps, T* __restrict__ out) {
+__global__ __launch_bounds__(256) void rownorm_any_kernel(const float* __restrict__ y, int n, int d,
+                                                          int n_part, float eps, T* __restrict__ out) {
   __shared__ float red[4];
   const int r = blockIdx.x;
-  // y is n_part partial sums [n_part][n][d], added in a fixed order
   auto val = [&](int i) {
     float v = y[(size_t)r * d + i];
     for (int p = 1; p < n_part; ++p) v += y[((size_t)p * n + r) * d + i];
@@ -247,6 +247,48 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ 
   ss = block_sum256<T>(ss, red);
   const float rs = 1.0f / sqrtf(ss / float(d) + eps);
   for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(val(i) * rs);
+}
+
+// One wave per row, the row held in registers: lane l takes the float4 chunks
+// l, l + 64, ... (at most RN4 of them, so d <= 256 RN4), summed over the n_part
+// partials in a fixed order; one read of y, one write of h.
+template <typename T, int RN4>
+__global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ y, int n, int d,
+                                                      int n_part, float eps, T* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const int d4 = d / 4;
+  float4 v[RN4];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < RN4; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = float4{0.f, 0.f, 0.f, 0.f};
+    if (c < d4) {
+      v[i] = reinterpret_cast<const float4*>(y + (size_t)r * d)[c];
+      for (int p = 1; p < n_part; ++p) {
+        const float4 w = reinterpret_cast<const float4*>(y + ((size_t)p * n + r) * d)[c];
+        v[i].x += w.x; v[i].y += w.y; v[i].z += w.z; v[i].w += w.w;
+      }
+    }
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / float(d) + eps);
+#pragma unroll
+  for (int i = 0; i < RN4; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= d4) continue;
+    T* o = out + (size_t)r * d + 4 * c;
+    o[0] = from_f32<T>(v[i].x * rs);
+    o[1] = from_f32<T>(v[i].y * rs);
+    o[2] = from_f32<T>(v[i].z * rs);
+    o[3] = from_f32<T>(v[i].w * rs);
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -274,10 +316,23 @@ int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_
                    float eps, void* out) {
   if (n <= 0) return TCS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dt == TCS_BF16)
-    rownorm_kernel<bf16_t><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
-  else
-    rownorm_kernel<float><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+  const int grid = (n + 3) / 4;
+  if (d % 4 != 0 || d > 256 * 16) {
+    if (dt == TCS_BF16)
+      rownorm_any_kernel<bf16_t><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+    else
+      rownorm_any_kernel<float><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+  } else if (dt == TCS_BF16) {
+    if (d <= 256 * 10)
+      rownorm_kernel<bf16_t, 10><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+    else
+      rownorm_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+  } else {
+    if (d <= 256 * 10)
+      rownorm_kernel<float, 10><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+    else
+      rownorm_kernel<float, 16><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+  }
   return check_launch("rownorm");
 }
 
