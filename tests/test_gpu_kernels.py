@@ -216,3 +216,39 @@ def test_tree_attn_vs_oracle(dev, name):
         err = np.abs(got - want)
         say(f"tree_attn[{name}] n_int={n}: max |dO| {err.max():.2e}")
         assert np.all(err <= 1e-5 + 1e-5 * np.abs(want))
+
+
+def test_tree_attn_many_rows_many_docs(dev):
+    """Many query rows and many documents, so the many-row kernel scores several
+    documents per workgroup (their queries and path partials read once): sampled
+    documents across the batch, including empty ones, against the oracle."""
+    torch = _torch()
+    B = 80
+    lens = tuple(int(x) for x in np.random.default_rng(11).integers(0, 70, size=B))
+    lens = (0,) + lens[1:-1] + (65,)
+    cfg = config(2, V=20000, d=64, Hq=8, Hkv=2, hd=128, trie=("zipf", 1000, 2, 6, 1.2), doc_lens=lens)
+    inp = make_inputs(cfg, seed=29, weights=False)
+    trie = O.build_trie(inp["labels"], inp["root_token"], cfg.V)
+    rng = np.random.default_rng(6)
+    n = trie.n_int
+    assert n * 4 > 64 * 4, "needs the many-row kernel"
+    qn = O.round_bf16(rng.standard_normal((n, cfg.Hq, cfg.hd)))
+    kn = O.round_bf16(rng.standard_normal((n, cfg.Hkv, cfg.hd)))
+    vn = O.round_bf16(rng.standard_normal((n, cfg.Hkv, cfg.hd)))
+    Kd, Vd = O.decode_bf16(inp["Kd"]), O.decode_bf16(inp["Vd"])
+    scale = 1.0 / np.sqrt(cfg.hd)
+    docs = [0, 1, 2, 3, 4, 5, 39, 40, 78, 79]
+    want = O.tree_attention(qn, kn, vn, trie, Kd, Vd, inp["doc_offsets"], scale, docs=docs)
+    conv = lambda a: to_bf16_exact(a).cuda()
+    t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(t)
+    out = tcs.tree_attn(conv(qn), conv(kn), conv(vn), conv(Kd), conv(Vd),
+                        torch.from_numpy(inp["doc_offsets"]).cuda(), td["qparent"], scale)
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy()[docs]
+    ref = O.round_bf16(want)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ref) + 1e-30)[1] - 8)
+    off = np.maximum(np.abs(got - ref) - 4e-6, 0.0) / ulp
+    exact = float((got == ref).mean())
+    say(f"tree_attn[many rows, B={B}] n_int={n}: exact bf16 match {exact:.4f}, max off {off.max():.2f} ulp")
+    assert off.max() <= 1.0 and exact >= 0.99

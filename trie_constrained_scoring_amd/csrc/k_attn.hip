@@ -9,6 +9,7 @@
 // online-softmax state is merged with the path partial by log-sum-exp at the end,
 // the same combine that "Building an Ultra-High Throughput AI-SQL Engine"
 // (section 3.2.4) applies to its two attention calls for joins.
+#include <algorithm>
 #include <cstdio>
 
 #include "tcs_device.h"
@@ -679,10 +680,10 @@ int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32
 // and writes whole rows through a per-wave LDS tile.
 template <int HD>
 __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
-    int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn, const uint16_t* __restrict__ Kd,
-    const uint16_t* __restrict__ Vd, const int32_t* __restrict__ doc_offsets,
-    const float2* __restrict__ anc_ml, const float* __restrict__ anc_o, float scale,
-    uint16_t* __restrict__ O) {
+    int B, int dpw, int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn,
+    const uint16_t* __restrict__ Kd, const uint16_t* __restrict__ Vd,
+    const int32_t* __restrict__ doc_offsets, const float2* __restrict__ anc_ml,
+    const float* __restrict__ anc_o, float scale, uint16_t* __restrict__ O) {
   constexpr int KT = 64;                       // keys per stage
   constexpr int LDK = HD + 8;                  // sK row (bf16): conflict-free 16-byte reads
   constexpr int LDV = KT + 4;                  // sVt row (bf16): conflict-free 8-byte reads
@@ -702,11 +703,10 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
   const int n_rb = (rows_total + 127) / 128;
   const int rb = blockIdx.x % n_rb;
   const int g = (blockIdx.x / n_rb) % Hkv;
-  const int b = blockIdx.x / (n_rb * Hkv);
+  const int b_lo = blockIdx.x / (n_rb * Hkv) * dpw;
+  const int b_hi = min(B, b_lo + dpw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = rb * 128 + wave * 32;  // this wave's first row
-  const int doc0 = doc_offsets[b];
-  const int L = doc_offsets[b + 1] - doc0;
 
   // Q^T fragments (lane: row l%32, hd 16 ks + 8 (l/32) ..)
   bf16x8 qf[KSTEPS];
@@ -724,6 +724,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
 
   uint4 rk[K_CH];
   uint4 rv[4];
+  int doc0 = 0, L = 0;
   auto load_stage = [&](int key0) {
 #pragma unroll
     for (int i = 0; i < K_CH; ++i) {
@@ -767,13 +768,18 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
     }
   };
 
+  const float qk = scale * LOG2E;
+  // the documents of this workgroup one after another: the query fragments stay in
+  // registers and the rows' path partials stay in cache across them
+  for (int b = b_lo; b < b_hi; ++b) {
+  doc0 = doc_offsets[b];
+  L = doc_offsets[b + 1] - doc0;
   f32x16 acc[NBLK];
 #pragma unroll
   for (int i = 0; i < NBLK; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
   float m = -INFINITY, lsum = 0.f;  // base-2 running max; this lane's share of the sum
-  const float qk = scale * LOG2E;
 
   const int n_it = (L + KT - 1) / KT;
   if (n_it > 0) {
@@ -901,6 +907,8 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
                     anc_o[((size_t)r * Hq + h) * HD + hd] * sf[row * 2 + 1];
     O[(((size_t)b * n_int + r) * Hq + h) * HD + hd] = f32_to_bf16(v);
   }
+  __syncthreads();  // the epilogue's LDS tile is the next document's stage buffer
+  }
 }
 
 int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
@@ -925,11 +933,17 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
     else
       doc_attn_mfma_kernel<64, 1, 4><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   } else {
-    const long grid = long(B) * Hkv * ((rows + 127) / 128);
+    // documents per workgroup: as many as keep >= 4096 workgroups (8 rounds of two
+    // per CU, so the last round's tail stays small); the queries and path partials
+    // are then read once per dpw documents
+    const long blocks = long(Hkv) * ((rows + 127) / 128);
+    const long chunks = std::min(long(B), (4096 + blocks - 1) / blocks);
+    const int dpw = int(std::max(1L, B / chunks));
+    const long grid = blocks * ((B + dpw - 1) / dpw);
     if (hd == 128)
-      doc_attn_rows_kernel<128><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+      doc_attn_rows_kernel<128><<<grid, 256, 0, s>>>(B, dpw, n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
     else
-      doc_attn_rows_kernel<64><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+      doc_attn_rows_kernel<64><<<grid, 256, 0, s>>>(B, dpw, n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   }
   timer_end(TCS_TIMER_DOC_ATTN, stream);
   const hipError_t e = hipGetLastError();
