@@ -79,6 +79,20 @@ def test_prepared_run_equals_classify(dev, name):
     say(f"prepared[{name}]: run == classify on 2 batches")
 
 
+def test_classify_many_rows_projection(dev):
+    """Enough rows (8 documents x 1881 internal nodes, d = 2560, Hq*hd = 4096) that the
+    output projection runs on the ring GEMM: sampled documents against the oracle."""
+    cfg = config(3, V=2000, B=8, L=64, trie=("zipf", 1000, 2, 6, 1.2))
+    inp = make_inputs(cfg, seed=103)
+    label, prob, ll = run_gpu(cfg, inp, prepared=True)
+    n_int = O.build_trie(inp["labels"], inp["root_token"], cfg.V).n_int
+    assert cfg.B * n_int >= 13056, "needs >= 512 output tiles"
+    docs = [0, cfg.B - 1]
+    o = O.classify(inp, docs=docs)
+    check_labels(ll[docs], prob[docs], label[docs], o["ll"], o["prob"], o["label"],
+                 f"classify[ring projection, R={cfg.B * n_int}]")
+
+
 @pytest.fixture(scope="module")
 def cfg2():
     cfg = config(2)

@@ -1,5 +1,6 @@
 // Projection GEMMs of the node input block (q/k/v) and of the output projection
 // (o Wo^T + residual), and the RMSNorm row kernels around them.
+#include <algorithm>
 #include <cstdio>
 
 #include "gemm_core.h"
@@ -291,6 +292,11 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ 
   }
 }
 
+__global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
 // ------------------------------------------------------------------ launchers
 
 static int check_launch(const char* what) {
@@ -388,6 +394,14 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
                                              static_cast<float*>(C), ldc, epi, r);
   }
   return check_launch("gemm_nt");
+}
+
+int launch_zero_fill(void* stream, void* p, size_t bytes) {
+  if (bytes == 0) return TCS_OK;
+  const size_t n = bytes / 16;
+  const int grid = int(std::min<size_t>((n + 255) / 256, 4096));
+  zero_fill_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<uint4*>(p), n);
+  return check_launch("zero_fill");
 }
 
 }  // namespace tcs

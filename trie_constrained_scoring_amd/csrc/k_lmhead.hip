@@ -227,12 +227,34 @@ __device__ __forceinline__ void head_scale_rows(f32x16 (&acc)[4][4], const float
     }
 }
 
-template <bool W8>
+// Plain-product mode of the ring kernel (the output projection y = x + O Wo^T of
+// many rows): C[r][n] = sum_k h[r][k] W[n][k] + E[token[qnode[r % n_int]]][n], fp32.
+struct RingGemmOut {
+  float* C;
+  int ldc;
+  const uint16_t* E;
+  const int32_t* token;
+  const int32_t* qnode;
+  int n_int;
+};
+
+// Tile order of the plain-product mode: linear tile t = 256 w + 32 xcd + slot
+// (row-major over (row tile, column tile)), so each XCD takes 32 consecutive tiles
+// per round and the row tiles they share stay in its L2.
+__device__ __forceinline__ bool gemm_tile_coords(int bid, int n_rt, int n_vt, int& rt, int& vt) {
+  const int xcd = bid & 7, slot = (bid >> 3) & 31, w = bid >> 8;
+  const int t = w * 256 + xcd * 32 + slot;
+  rt = t / n_vt;
+  vt = t - rt * n_vt;
+  return t < n_rt * n_vt;
+}
+
+template <bool W8, bool GEMM>
 __global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
     int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
     const float* __restrict__ w_scale, const int32_t* __restrict__ list_head,
     const int4* __restrict__ rec, float* __restrict__ raw, float2* __restrict__ part,
-    const uint16_t* __restrict__ zero, int rounds_per_wg) {
+    const uint16_t* __restrict__ zero, int rounds_per_wg, RingGemmOut go) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[DMA_SLOT_BYTES], st1[DMA_SLOT_BYTES],
       st2[DMA_SLOT_BYTES], st3[DMA_SLOT_BYTES], st4[DMA_SLOT_BYTES];
   uint8_t* const slot[DMA_SLOTS] = {st0, st1, st2, st3, st4};
@@ -242,7 +264,8 @@ __global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
   // consecutive rounds, so the workgroups that share operand tiles in an XCD's L2
   // stay within a few rounds of each other
   const int w_lo = int(blockIdx.x) / HEAD_WGS * rounds_per_wg;
-  const int rounds = min(head_grid(n_rt, n_vt) / HEAD_WGS, w_lo + rounds_per_wg);
+  const int all_rounds = GEMM ? (n_rt * n_vt + HEAD_WGS - 1) / HEAD_WGS : head_grid(n_rt, n_vt) / HEAD_WGS;
+  const int rounds = min(all_rounds, w_lo + rounds_per_wg);
   const int bslot = int(blockIdx.x) % HEAD_WGS;
   const int nk = d / DMA_BK;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -250,7 +273,8 @@ __global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
   const int wm = wave >> 1, wn = wave & 1;
 
   auto coords = [&](int w, int& rt, int& vt) __attribute__((always_inline)) {
-    return head_tile_coords(w * HEAD_WGS + bslot, n_rt, n_vt, rt, vt);
+    if constexpr (GEMM) return gemm_tile_coords(w * HEAD_WGS + bslot, n_rt, n_vt, rt, vt);
+    else return head_tile_coords(w * HEAD_WGS + bslot, n_rt, n_vt, rt, vt);
   };
   auto next_valid = [&](int w) __attribute__((always_inline)) {
     int rt, vt;
@@ -469,6 +493,33 @@ __global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
     const int r0 = rt * 256, v0 = vt * HEAD_BN;
     // acc[im][jn][e]: vocabulary v0 + vhalf + 32 im + 8 (e>>2) + (e&3); hidden row
     // r0 + rloc + 32 jn
+    if constexpr (GEMM) {
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const int r = r0 + rloc + 32 * jn;
+        if (r >= R) continue;
+        const uint16_t* x = go.E + (size_t)go.token[go.qnode[r % go.n_int]] * V;
+        float* c = go.C + (size_t)r * go.ldc;
+#pragma unroll
+        for (int im = 0; im < 4; ++im)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = v0 + vhalf + 32 * im + 8 * g;
+            if (n + 4 <= V) {
+              const uint2 xr = *reinterpret_cast<const uint2*>(x + n);
+              *reinterpret_cast<float4*>(c + n) = float4{
+                  acc[im][jn][4 * g + 0] + __uint_as_float(xr.x << 16),
+                  acc[im][jn][4 * g + 1] + __uint_as_float(xr.x & 0xFFFF0000u),
+                  acc[im][jn][4 * g + 2] + __uint_as_float(xr.y << 16),
+                  acc[im][jn][4 * g + 3] + __uint_as_float(xr.y & 0xFFFF0000u)};
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                if (n + t < V) c[n + t] = acc[im][jn][4 * g + t] + bf16_to_f32(x[n + t]);
+            }
+          }
+      }
+    } else {
     if constexpr (W8) head_scale_rows(acc, w_scale, v0 + vhalf, V);
     // entries at or past V (last vocabulary tile) drop out of the row sums; the
     // accumulators are only read from here on
@@ -495,6 +546,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
     for (int jn = 0; jn < 4; ++jn) {
       const int r = r0 + rloc + 32 * jn;
       if (lane < 32 && r < R) part[(size_t)(2 * vt + wm) * R + r] = ms[jn];
+    }
     }
     // the next tile's W(0) and h(0) are in slots 0 and 1 (landed at the last barrier)
     read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
@@ -722,9 +774,9 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
     auto wp = static_cast<const uint8_t*>(W);
     auto zp = reinterpret_cast<const uint16_t*>(P.zero);
     if (w_dtype == TCS_FP8_E4M3)
-      lmhead_ring_kernel<true><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per);
+      lmhead_ring_kernel<true, false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per, RingGemmOut{});
     else
-      lmhead_ring_kernel<false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per);
+      lmhead_ring_kernel<false, false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per, RingGemmOut{});
     n_parts = 2 * n_tiles;
   } else {
     dim3 grid(n_tiles, (R + 7) / 8);
@@ -744,6 +796,33 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
                                                              lp);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "lmhead finalize: %s", hipGetErrorString(e));
+  return TCS_OK;
+}
+
+size_t gemm_ring_zero_bytes(int32_t K) {
+  const int nk = K / DMA_BK;
+  return nk % 5 == 0 ? 0 : size_t(256) * K * 2;
+}
+
+bool gemm_ring_ok(int32_t M, int32_t N, int32_t K) {
+  return K % DMA_BK == 0 && K <= 65536 && N % 4 == 0 &&
+         long((M + 255) / 256) * ((N + 255) / 256) >= 512;
+}
+
+int launch_gemm_ring_resid(void* stream, int32_t M, int32_t N, int32_t K, const void* A,
+                           const void* B, float* C, int32_t ldc, const GemmResid& res,
+                           const void* zero) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n_rt = (M + 255) / 256, n_vt = (N + 255) / 256;
+  const int rounds = (n_rt * n_vt + HEAD_WGS - 1) / HEAD_WGS;
+  const int per = head_rounds_per_wg(rounds);
+  const int grid = (rounds + per - 1) / per * HEAD_WGS;
+  const RingGemmOut go{C, ldc, static_cast<const uint16_t*>(res.E), res.token, res.qnode, res.n_int};
+  lmhead_ring_kernel<false, true><<<grid, 256, 0, s>>>(
+      M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(B), nullptr, nullptr,
+      nullptr, nullptr, nullptr, static_cast<const uint16_t*>(zero), per, go);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TCS_EHIP, "gemm ring: %s", hipGetErrorString(e));
   return TCS_OK;
 }
 

@@ -135,7 +135,8 @@ int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie,
 // partials (bf16 models) and the head's gather lists for B documents.
 struct PrepLayout {
   size_t total;
-  void *a_nodes, *Qn, *Kn, *Vn, *anc, *head;
+  void *a_nodes, *Qn, *Kn, *Vn, *anc, *head, *gemm_zero;
+  size_t gemm_zero_bytes;
 };
 
 static PrepLayout prep_layout(const tcs_model* m, const tcs_trie_dev* t, int32_t B, void* buf) {
@@ -150,6 +151,11 @@ static PrepLayout prep_layout(const tcs_model* m, const tcs_trie_dev* t, int32_t
   P.Vn = c.take<char>(n_int * kd * es);
   P.anc = c.take<char>(m->dtype == TCS_BF16 ? anc_bytes(t->n_int, m->Hq, m->hd) : 0);
   P.head = c.take<char>(lmhead_prep_bytes(m->dtype, B, t->n_int, t->n_nodes, m->d, m->V));
+  // zero block of the output projection's ring GEMM (padding k-steps)
+  const int32_t R = int32_t(size_t(B) * n_int);
+  P.gemm_zero_bytes = m->dtype == TCS_BF16 && gemm_ring_ok(R, m->d, int32_t(qd))
+                          ? gemm_ring_zero_bytes(int32_t(qd)) : 0;
+  P.gemm_zero = c.take<char>(P.gemm_zero_bytes);
   P.total = c.used;
   return P;
 }
@@ -236,6 +242,7 @@ static int prepare_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t,
     float* ao = c.take<float>(size_t(n_int) * m->Hq * m->hd);
     if ((rc = launch_anc_attn(stream, dt, n_int, m->Hq, m->Hkv, m->hd, P.Qn, P.Kn, P.Vn, t->qparent, scale, ml, ao))) return rc;
   }
+  if ((rc = launch_zero_fill(stream, P.gemm_zero, P.gemm_zero_bytes))) return rc;
   return launch_lmhead_prep(stream, dt, B, n_int, t->n_nodes, m->d, m->V, t->e_tok, t->e_qrow,
                             t->e_child, t->n_nodes - 1, P.head);
 }
@@ -273,7 +280,11 @@ static int run_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, con
   if (rc) return rc;
   // y = x + O Wo^T ; h = RMSNorm(y)
   GemmResid res{m->E, t->token, t->qnode, n_int};
-  if ((rc = launch_gemm_nt(stream, dt, GEMM_RESID, R, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d, &res))) return rc;
+  if (dt == TCS_BF16 && gemm_ring_ok(R, m->d, qd))
+    rc = launch_gemm_ring_resid(stream, R, m->d, qd, L.O, m->Wo, L.y, m->d, res, P.gemm_zero);
+  else
+    rc = launch_gemm_nt(stream, dt, GEMM_RESID, R, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d, &res);
+  if (rc) return rc;
   if ((rc = launch_rownorm(stream, dt, L.y, R, m->d, gemm_resid_splits(dt, R, m->d, qd), m->eps,
                            L.h))) return rc;
   if ((rc = launch_lmhead_run(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,

@@ -63,6 +63,18 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
                    const void* A, int32_t lda, const void* B, int32_t ldb, void* C, int32_t ldc,
                    const GemmResid* resid);
 
+// Output projection of many rows on the output head's LDS-DMA ring:
+// C[r][n] = sum_k A[r][k] B[n][k] + E[tok(r)][n] (bf16 operands, fp32 C), for shapes
+// with gemm_ring_ok; `zero` holds gemm_ring_zero_bytes(K) zero bytes (none needed
+// when K / 64 is a multiple of 5).
+bool gemm_ring_ok(int32_t M, int32_t N, int32_t K);
+size_t gemm_ring_zero_bytes(int32_t K);
+int launch_gemm_ring_resid(void* stream, int32_t M, int32_t N, int32_t K, const void* A,
+                           const void* B, float* C, int32_t ldc, const GemmResid& res,
+                           const void* zero);
+// Zero `bytes` (a multiple of 16) of device memory with a fill kernel.
+int launch_zero_fill(void* stream, void* p, size_t bytes);
+
 // Output head, see tcs_lmhead_lse_gather.  Its workspace is a per-label-set part
 // (lmhead_prep_bytes: edge segments, zero block, gather lists for batches of B
 // documents; written by launch_lmhead_prep) followed by the per-batch (max, sum exp)
