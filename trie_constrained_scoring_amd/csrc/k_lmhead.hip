@@ -161,42 +161,36 @@ __device__ __forceinline__ void head_pick(int t, const f32x16 (&acc)[4][4], floa
 
 // Max and sum of exp of each of the lane's four rows (jn) over its 64 entries
 // plus the partner lane's (l ^ 32); entries at or past `vlim` are excluded when
-// MASK.  Rows are innermost, so each entry's mask is used as soon as it is made.
+// MASK.  One row at a time, so only that row's 64 values are live.
 // exp2 is the hardware instruction: arguments are <= 0, and terms below 2^-126
 // of the row maximum, which it flushes, are far below fp32 resolution of the sum.
 template <bool MASK>
 __device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][4], int vlim,
                                               float2 (&out)[4]) {
   constexpr float LOG2E = 1.4426950408889634f;
-  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-  for (int im = 0; im < 4; ++im)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const bool ok = !MASK || 32 * im + 8 * (e >> 2) + (e & 3) < vlim;
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) m[jn] = fmaxf(m[jn], ok ? acc[im][jn][e] : -INFINITY);
-    }
-  float ml[4], sum[4];
 #pragma unroll
   for (int jn = 0; jn < 4; ++jn) {
-    m[jn] = fmaxf(m[jn], __shfl_xor(m[jn], 32, 64));
-    ml[jn] = m[jn] == -INFINITY ? 0.f : m[jn] * LOG2E;
-    sum[jn] = 0.f;
-  }
+    float m = -INFINITY;
 #pragma unroll
-  for (int im = 0; im < 4; ++im)
+    for (int im = 0; im < 4; ++im)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const bool ok = !MASK || 32 * im + 8 * (e >> 2) + (e & 3) < vlim;
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) {
-        const float x = __builtin_amdgcn_exp2f(fmaf(acc[im][jn][e], LOG2E, -ml[jn]));
-        sum[jn] += ok ? x : 0.f;
+      for (int e = 0; e < 16; ++e) {
+        const bool ok = !MASK || 32 * im + 8 * (e >> 2) + (e & 3) < vlim;
+        m = fmaxf(m, ok ? acc[im][jn][e] : -INFINITY);
       }
-    }
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const float ml = m == -INFINITY ? 0.f : m * LOG2E;
+    float sum = 0.f;
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn) out[jn] = float2{m[jn], sum[jn] + __shfl_xor(sum[jn], 32, 64)};
+    for (int im = 0; im < 4; ++im)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool ok = !MASK || 32 * im + 8 * (e >> 2) + (e & 3) < vlim;
+        const float x = __builtin_amdgcn_exp2f(fmaf(acc[im][jn][e], LOG2E, -ml));
+        sum += ok ? x : 0.f;
+      }
+    out[jn] = float2{m, sum + __shfl_xor(sum, 32, 64)};
+  }
 }
 
 // acc[im][jn][e] *= scale of vocabulary entry vb + 32 im + 8 (e>>2) + (e&3) (fp8
