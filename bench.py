@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
                     [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
+    python bench.py --head-probe --config 3  # head alone: workload-like vs constant operands
 
 One step is one ``tcs_classify_run`` call over one batch of synthetic documents:
 ancestor-masked tree attention over the documents, output projection + RMSNorm,
@@ -44,7 +45,7 @@ METRIC = "documents classified/sec at 10/255/5000 labels; % of HBM/MFMA roofline
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 HEAD_SOURCES = ["gemm_core.h", "k_lmhead.hip", "tcs_device.h"]
-HEAD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lmhead_bf16_running_example_B64_traffic.md")
+HEAD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lmhead_ring_bf16_running_example_B64_traffic.md")
 COPY_BYTES = 1 << 30
 
 
@@ -154,6 +155,30 @@ def doc_attn_bytes(S):
     return kv + q + anc + o
 
 
+def doc_attn_flops(S):
+    """Algorithmic FLOP of one document-attention launch: q.k and p.v for every
+    (document, internal node, query head) over the document's keys, 4 hd FLOP per key
+    (the path keys are reduced once per label set, in the prepare step)."""
+    cfg, td = S["cfg"], S["td"]
+    B, n_int, T = S["docs"].B, td.trie.n_int, int(S["inp"]["doc_offsets"][-1])
+    return 4.0 * n_int * cfg.Hq * cfg.hd * T
+
+
+def doc_attn_roofline(S, ms):
+    """Roofline of the document attention: HBM-bound below the bf16 ridge
+    (2.5 PFLOP/s / 8 TB/s = 312 FLOP/B), matrix-core-bound above it."""
+    by, fl = doc_attn_bytes(S), doc_attn_flops(S)
+    if fl / by > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        tf = fl / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_launch": fl, "bytes_per_launch": by,
+                "ms_per_launch": round(ms, 4)}
+    gbs = by / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": by, "flops_per_launch": fl,
+            "ms_per_launch": round(ms, 4)}
+
+
 def cpu_baseline(S, budget_s=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of documents."""
     import oracle as O
@@ -175,6 +200,48 @@ def cpu_baseline(S, budget_s=15.0):
                       f"(BLAS threads = visible cores), {dt:.1f}s"}
 
 
+def head_probe(cid: int, reps: int = 5):
+    """The output head alone (tcs_lmhead_lse_gather) at a workload's shape, on operands
+    drawn like the workload's (unit-RMS rows h, W ~ N(0, 0.02), bf16) and on constant
+    operands of the same shape: the gap between the two is the part of the head's
+    time that depends on the operand values (matrix-core power), not on the schedule."""
+    import torch
+    import trie_constrained_scoring_amd as tcs
+    from synth import config, make_inputs
+    cfg = config(cid)
+    inp = make_inputs(cfg, weights=False)
+    trie = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(trie)
+    B, R = cfg.B, cfg.B * trie.n_int
+    g = torch.Generator(device="cuda").manual_seed(cid)
+    out = {}
+    for kind in ("random", "constant"):
+        if kind == "random":
+            h = torch.randn(R, cfg.d, device="cuda", generator=g).to(torch.bfloat16)
+            W = (torch.randn(cfg.V, cfg.d, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        else:
+            h = torch.ones(R, cfg.d, device="cuda", dtype=torch.bfloat16)
+            W = torch.full((cfg.V, cfg.d), 0.02, device="cuda", dtype=torch.bfloat16)
+        ws = torch.empty(tcs.lmhead_workspace_bytes(B, trie.n_int, trie.n_nodes, cfg.d, cfg.V),
+                         dtype=torch.uint8, device="cuda")
+        tcs.lmhead_lse_gather(h, W, td, B, ws=ws)
+        torch.cuda.synchronize()
+        tcs.timing_enable(True)
+        for _ in range(reps):
+            tcs.lmhead_lse_gather(h, W, td, B, ws=ws)
+        torch.cuda.synchronize()
+        ms, n = tcs.timing_read(tcs.TCS_TIMER_HEAD)
+        tcs.timing_enable(False)
+        ms /= n
+        tf = 2.0 * R * cfg.d * cfg.V / (ms * 1e-3) / 1e12
+        out[kind] = {"ms_per_launch": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del h, W, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"head_probe": {"config": cid, "rows": R, "d": cfg.d, "V": cfg.V, **out}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +252,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (3 launches) and exit")
+    ap.add_argument("--head-probe", action="store_true",
+                    help="only time the output head alone on workload-like vs constant operands")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); documents shard across GPUs "
@@ -201,6 +270,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return
+
+    if args.head_probe:
+        head_probe(args.config)
         return
 
     S = setup(args.config)
@@ -235,11 +308,7 @@ def main():
                        "timing": "HIP events around each head launch of a second pass of the same steps"}
     res["head_share_of_step"] = round(kern["head"] / (sec * 1e3), 4)
     if kern["doc_attn"]:
-        by = doc_attn_bytes(S)
-        gbs = by / (kern["doc_attn"] * 1e-3) / 1e9
-        res["doc_attn_roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                    "bytes_per_launch": by, "ms_per_launch": round(kern["doc_attn"], 4)}
+        res["doc_attn_roofline"] = doc_attn_roofline(S, kern["doc_attn"])
     extra = {}
     for c in [int(x) for x in args.extra.split(",") if x.strip()]:
         if c == args.config:
@@ -256,9 +325,8 @@ def main():
              "head_tflops": round(tf, 2), "head_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
              "head_ms": round(k2["head"], 4), "prepare_ms": round(S2["prep_ms"], 3)}
         if k2["doc_attn"]:
-            gbs = doc_attn_bytes(S2) / (k2["doc_attn"] * 1e-3) / 1e9
             e["doc_attn_ms"] = round(k2["doc_attn"], 4)
-            e["doc_attn_gbs"] = round(gbs, 1)
+            e["doc_attn_roofline"] = doc_attn_roofline(S2, k2["doc_attn"])
         extra[str(S2["trie"].n_labels)] = e
         S = S2
     if extra:

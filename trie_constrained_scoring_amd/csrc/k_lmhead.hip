@@ -244,11 +244,11 @@ __device__ __forceinline__ bool gemm_tile_coords(int bid, int n_rt, int n_vt, in
 }
 
 template <bool W8, bool GEMM>
-__global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
+__device__ __forceinline__ void ring_body(
     int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
     const float* __restrict__ w_scale, const int32_t* __restrict__ list_head,
     const int4* __restrict__ rec, float* __restrict__ raw, float2* __restrict__ part,
-    const uint16_t* __restrict__ zero, int rounds_per_wg, RingGemmOut go) {
+    const uint16_t* __restrict__ zero, int rounds_per_wg, const RingGemmOut& go) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[DMA_SLOT_BYTES], st1[DMA_SLOT_BYTES],
       st2[DMA_SLOT_BYTES], st3[DMA_SLOT_BYTES], st4[DMA_SLOT_BYTES];
   uint8_t* const slot[DMA_SLOTS] = {st0, st1, st2, st3, st4};
@@ -556,6 +556,27 @@ __global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
   wait_vmcnt<0>();  // loads past the last tile: nothing may still target LDS at exit
 }
 
+// The output head (bf16 or fp8 weights).
+template <bool W8>
+__global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
+    int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
+    const float* __restrict__ w_scale, const int32_t* __restrict__ list_head,
+    const int4* __restrict__ rec, float* __restrict__ raw, float2* __restrict__ part,
+    const uint16_t* __restrict__ zero, int rounds_per_wg) {
+  ring_body<W8, false>(R, V, d, h, W, w_scale, list_head, rec, raw, part, zero, rounds_per_wg,
+                       RingGemmOut{});
+}
+
+// The output projection of many rows (plain products plus the embedding residual).
+__global__ __launch_bounds__(256, 1) void proj_ring_kernel(int M, int N, int K,
+                                                           const uint16_t* __restrict__ A,
+                                                           const uint8_t* __restrict__ B,
+                                                           const uint16_t* __restrict__ zero,
+                                                           int rounds_per_wg, RingGemmOut go) {
+  ring_body<false, true>(M, N, K, A, B, nullptr, nullptr, nullptr, nullptr, nullptr, zero,
+                         rounds_per_wg, go);
+}
+
 // fp32 head: one thread per vocabulary entry of a 256-entry tile, 8 rows per block.
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(
     int R, int V, int d, int n_int, int n_nodes, const float* __restrict__ h,
@@ -768,9 +789,9 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
     auto wp = static_cast<const uint8_t*>(W);
     auto zp = reinterpret_cast<const uint16_t*>(P.zero);
     if (w_dtype == TCS_FP8_E4M3)
-      lmhead_ring_kernel<true, false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per, RingGemmOut{});
+      lmhead_ring_kernel<true><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per);
     else
-      lmhead_ring_kernel<false, false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per, RingGemmOut{});
+      lmhead_ring_kernel<false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per);
     n_parts = 2 * n_tiles;
   } else {
     dim3 grid(n_tiles, (R + 7) / 8);
@@ -812,9 +833,9 @@ int launch_gemm_ring_resid(void* stream, int32_t M, int32_t N, int32_t K, const 
   const int per = head_rounds_per_wg(rounds);
   const int grid = (rounds + per - 1) / per * HEAD_WGS;
   const RingGemmOut go{C, ldc, static_cast<const uint16_t*>(res.E), res.token, res.qnode, res.n_int};
-  lmhead_ring_kernel<false, true><<<grid, 256, 0, s>>>(
-      M, N, K, static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(B), nullptr, nullptr,
-      nullptr, nullptr, nullptr, static_cast<const uint16_t*>(zero), per, go);
+  proj_ring_kernel<<<grid, 256, 0, s>>>(M, N, K, static_cast<const uint16_t*>(A),
+                                        static_cast<const uint8_t*>(B),
+                                        static_cast<const uint16_t*>(zero), per, go);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "gemm ring: %s", hipGetErrorString(e));
   return TCS_OK;
