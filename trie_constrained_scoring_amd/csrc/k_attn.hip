@@ -616,31 +616,48 @@ __global__ __launch_bounds__(256) void doc_attn_stream_kernel(
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < 32 * HD; idx += 256) {
-    const int row = idx / HD, hd = idx % HD;
+  {
+    // thread t writes row t/8, hd [16 (t%8), +16): its path-partial loads are all
+    // issued before any is used
+    constexpr int SEG = HD / 8;
+    const int row = tid >> 3, h0 = (tid & 7) * SEG;
     const int j = j0 + row;
-    if (j >= rows_total) continue;
-    const int r = j / G, h = g * G + j % G;
-    float M = -INFINITY;
+    if (j < rows_total) {
+      const int r = j / G, h = g * G + j % G;
+      const float4* ao = reinterpret_cast<const float4*>(anc_o + ((size_t)r * Hq + h) * HD + h0);
+      float4 av[SEG / 4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) M = fmaxf(M, sml[(k * 32 + row) * 2]);
-    float Ls = 0.f, Os = 0.f;
-    if (M != -INFINITY) {
+      for (int i = 0; i < SEG / 4; ++i) av[i] = ao[i];
+      const float2 a = anc_ml[(size_t)r * Hq + h];
+      float M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) M = fmaxf(M, sml[(k * 32 + row) * 2]);
+      float f[4], Ls = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float f = exp2f(sml[(k * 32 + row) * 2] - M);
-        Ls += f * sml[(k * 32 + row) * 2 + 1];
-        Os += f * so[((size_t)k * 32 + row) * OUT_LD + hd];
+        f[k] = M == -INFINITY ? 0.f : exp2f(sml[(k * 32 + row) * 2] - M);
+        Ls += f[k] * sml[(k * 32 + row) * 2 + 1];
       }
+      const float ma = a.x * LOG2E;
+      const float Mt = fmaxf(M, ma);
+      const float fd = M == -INFINITY ? 0.f : exp2f(M - Mt);
+      const float fa = exp2f(ma - Mt);
+      const float inv = 1.0f / (Ls * fd + a.y * fa);
+      float v[SEG];
+#pragma unroll
+      for (int e = 0; e < SEG; ++e) {
+        float Os = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) Os += f[k] * so[((size_t)k * 32 + row) * OUT_LD + h0 + e];
+        const float an = (&av[e / 4].x)[e % 4];
+        v[e] = (Os * fd + an * fa) * inv;
+      }
+      uint4* op = reinterpret_cast<uint4*>(O + (((size_t)b * n_int + r) * Hq + h) * HD + h0);
+#pragma unroll
+      for (int i = 0; i < SEG / 8; ++i)
+        op[i] = uint4{pack_bf16(v[8 * i], v[8 * i + 1]), pack_bf16(v[8 * i + 2], v[8 * i + 3]),
+                      pack_bf16(v[8 * i + 4], v[8 * i + 5]), pack_bf16(v[8 * i + 6], v[8 * i + 7])};
     }
-    const float2 a = anc_ml[(size_t)r * Hq + h];
-    const float ma = a.x * LOG2E;
-    const float Mt = fmaxf(M, ma);
-    const float fd = M == -INFINITY ? 0.f : exp2f(M - Mt);
-    const float fa = exp2f(ma - Mt);
-    const float num = Os * fd + anc_o[((size_t)r * Hq + h) * HD + hd] * fa;
-    const float den = Ls * fd + a.y * fa;
-    O[(((size_t)b * n_int + r) * Hq + h) * HD + hd] = f32_to_bf16(num / den);
   }
 }
 
@@ -898,14 +915,31 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
     }
   }
   __syncthreads();
-  for (int idx = lane; idx < 32 * HD; idx += 64) {
-    const int row = idx / HD, hd = idx % HD;
-    const int j = j0 + row;
-    if (j >= rows_total) continue;
-    const int r = j / G, h = g * G + j % G;
-    const float v = so[row * OUT_LD + hd] * sf[row * 2] +
-                    anc_o[((size_t)r * Hq + h) * HD + hd] * sf[row * 2 + 1];
-    O[(((size_t)b * n_int + r) * Hq + h) * HD + hd] = f32_to_bf16(v);
+  {
+    // lane pair (2 rr, 2 rr + 1) writes row rr, one half of hd each: all of the
+    // half-row's path-partial loads are issued before any is used
+    constexpr int HH = HD / 2;
+    const int rr = lane >> 1, half = lane & 1;
+    const int j = j0 + rr;
+    if (j < rows_total) {
+      const int r = j / G, h = g * G + j % G;
+      const float4* ao = reinterpret_cast<const float4*>(anc_o + ((size_t)r * Hq + h) * HD + half * HH);
+      float4 av[HH / 4];
+#pragma unroll
+      for (int i = 0; i < HH / 4; ++i) av[i] = ao[i];
+      const float sd = sf[rr * 2], sa = sf[rr * 2 + 1];
+      const float* sr = so + rr * OUT_LD + half * HH;
+      uint4* op = reinterpret_cast<uint4*>(O + (((size_t)b * n_int + r) * Hq + h) * HD + half * HH);
+#pragma unroll
+      for (int i = 0; i < HH / 8; ++i) {
+        const float4 a0 = av[2 * i], a1 = av[2 * i + 1];
+        const float* x = sr + 8 * i;
+        op[i] = uint4{pack_bf16(x[0] * sd + a0.x * sa, x[1] * sd + a0.y * sa),
+                      pack_bf16(x[2] * sd + a0.z * sa, x[3] * sd + a0.w * sa),
+                      pack_bf16(x[4] * sd + a1.x * sa, x[5] * sd + a1.y * sa),
+                      pack_bf16(x[6] * sd + a1.z * sa, x[7] * sd + a1.w * sa)};
+      }
+    }
   }
   __syncthreads();  // the epilogue's LDS tile is the next document's stage buffer
   }
