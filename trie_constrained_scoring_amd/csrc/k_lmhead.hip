@@ -656,9 +656,16 @@ __global__ __launch_bounds__(256) void lse_finalize_wave_kernel(int R, int n_par
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   float m = -INFINITY, s = 0.f;
-  for (int t = lane; t < n_parts; t += 64) {
-    const float2 p = part[(size_t)t * R + r];
-    lse_merge(m, s, p.x, p.y);
+  // eight loads in flight per lane before they are merged
+  for (int t0 = lane; t0 < n_parts; t0 += 64 * 8) {
+    float2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + 64 * u;
+      p[u] = t < n_parts ? part[(size_t)t * R + r] : float2{-INFINITY, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) lse_merge(m, s, p[u].x, p[u].y);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
