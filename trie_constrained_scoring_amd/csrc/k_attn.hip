@@ -945,6 +945,232 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
   }
 }
 
+// Document part for tries with many query rows per (document, KV head), hd 128:
+// 128 query rows (32 per wave) of one KV head against the documents
+// [b_lo, b_hi) one after another.  64-key stages of K and V go through a two-slot
+// LDS ring filled by buffer-to-LDS loads (natural [key][hd] layout, chunk-swizzled
+// like the key-streaming kernel), shared by the four waves; the ring runs on
+// across documents.  Per stage each wave computes S^T = K Q^T for two 32-key
+// blocks, one online-softmax update, and O^T += V^T P^T with V^T from transposing
+// LDS reads and P split into bf16 high and low parts.  At a document's end each
+// lane merges its row with the row's path partial and writes its half of the row
+// straight from the accumulators, so the ring keeps loading meanwhile.  Two
+// workgroups fit on a CU (64 KB of LDS each).
+__global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
+    int B, int dpw, int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn,
+    const uint16_t* __restrict__ Kd, const uint16_t* __restrict__ Vd,
+    const int32_t* __restrict__ doc_offsets, const float2* __restrict__ anc_ml,
+    const float* __restrict__ anc_o, float scale, uint16_t* __restrict__ O) {
+  constexpr int HD = 128;
+  constexpr int KT = 64;                 // keys per stage
+  constexpr int ROW = HD * 2;            // bytes per key row
+  constexpr int OPB = KT * ROW;          // bytes per operand per stage (16 KB)
+  constexpr int SLOT = 2 * OPB;          // K then V
+  constexpr int NBLK = HD / 32, KSTEPS = HD / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
+
+  const int G = Hq / Hkv;
+  const int rows_total = n_int * G;
+  const int n_rb = (rows_total + 127) / 128;
+  const int rb = blockIdx.x % n_rb;
+  const int g = (blockIdx.x / n_rb) % Hkv;
+  const int b_lo = blockIdx.x / (n_rb * Hkv) * dpw;
+  const int b_hi = min(B, b_lo + dpw);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j0 = rb * 128 + wave * 32;   // this wave's first row
+  const int RS = Hkv * HD * 2;           // bytes between consecutive keys of one head
+
+  // slots start as zeros, so a key past a document's end that no load writes
+  // still holds finite values (its weight is 0)
+#pragma unroll
+  for (int i = 0; i < 2 * SLOT / (256 * 16); ++i)
+    *reinterpret_cast<uint4*>(lds + (i * 256 + tid) * 16) = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();  // every wave's zeros are in place before any load can land
+
+  // Q^T fragments: lane holds row l%32, hd 16 ks + 8 (l/32) ..
+  const int kr = lane & 31, c = lane >> 5;
+  const int jrow = j0 + kr;
+  const bool row_ok = jrow < rows_total;
+  const int r = row_ok ? jrow / G : 0, h = g * G + (row_ok ? jrow % G : 0);
+  bf16x8 qf[KSTEPS];
+  {
+    const uint16_t* qp = Qn + ((size_t)r * Hq + h) * HD + 8 * c;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : uint4{0, 0, 0, 0};
+      qf[ks] = *reinterpret_cast<bf16x8*>(&v);
+    }
+  }
+
+  // DMA: load j (0..15) of an operand fills stage rows 4j .. 4j+3; this wave issues
+  // loads 4 wave .. 4 wave + 3 of K and of V.  Lane i writes row 4j + i/16 at
+  // position i%16, which holds chunk (i%16) ^ kv_swz(row).
+  int vo[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int row = 4 * (4 * wave + jj) + (lane >> 4);
+    vo[jj] = row * RS + (((lane & 15) ^ kv_swz(row & 15)) << 4);
+  }
+  auto n_stages = [&](int b) { return (doc_offsets[b + 1] - doc_offsets[b] + KT - 1) / KT; };
+  // stage t of document b into slot sl
+  auto issue = [&](int b, int t, int sl) __attribute__((always_inline)) {
+    const int doc0 = doc_offsets[b], L = doc_offsets[b + 1] - doc0;
+    const int nkeys = min(KT, L - t * KT);
+    const int bytes = (nkeys - 1) * RS + ROW;
+    const size_t off = ((size_t)(doc0 + t * KT) * Hkv + g) * HD;
+    uint8_t* dst = lds + sl * SLOT + wave * 4 * 1024;
+    kv_issue<4>(Kd + off, bytes, dst, vo);
+    kv_issue<4>(Vd + off, bytes, dst + OPB, vo);
+  };
+
+  // fragment offsets inside a slot (key block kb adds kb * 32 rows)
+  int ko[KSTEPS];  // K: row kr, chunk 2 ks + c
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) ko[ks] = kr * ROW + (((2 * ks + c) ^ kv_swz(kr & 15)) << 4);
+  int vof[2][2][NBLK];  // V^T, as in the key-streaming kernel
+  {
+    const int sidx = lane & 15, hsel = (lane >> 4) & 1;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int key = 16 * st + 8 * q + 4 * c + (sidx >> 2);
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+          const int chunk = 4 * blk + 2 * hsel + ((sidx & 3) >> 1);
+          vof[st][q][blk] = OPB + key * ROW + ((chunk ^ kv_swz(key & 15)) << 4) + 8 * (sidx & 1);
+        }
+      }
+  }
+  const float qk = scale * LOG2E;
+
+  // prefetch cursor: the next stage to load (documents without keys are skipped)
+  int pb = b_lo, pt = 0;
+  while (pb < b_hi && n_stages(pb) == 0) ++pb;
+  int kc = 0;  // stages computed so far (slot kc & 1)
+  if (pb < b_hi) issue(pb, 0, 0);
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (++pt >= n_stages(pb)) {
+      pt = 0;
+      do ++pb; while (pb < b_hi && n_stages(pb) == 0);
+    }
+  };
+  advance();
+
+  for (int b = b_lo; b < b_hi; ++b) {
+    const int L = doc_offsets[b + 1] - doc_offsets[b];
+    const int nst = (L + KT - 1) / KT;
+    f32x16 acc[NBLK];
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    float m = -INFINITY, lsum = 0.f;  // base-2 running max; this lane's share of the sum
+    for (int t = 0; t < nst; ++t, ++kc) {
+      wait_vmcnt<0>();       // this wave's part of stage kc has landed
+      wait_lgkmcnt0();       // and its reads of stage kc - 1 are done
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (pb < b_hi) {       // stage kc + 1 into the slot stage kc - 1 used
+        issue(pb, pt, (kc + 1) & 1);
+        advance();
+      }
+      const uint8_t* sl = lds + (kc & 1) * SLOT;
+      f32x16 sc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + kb * 32 * ROW + ko[ks]);
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
+        }
+      }
+      // online softmax (base 2) over the 64 keys; keys past the document end are masked
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = t * KT + kb * 32 + 8 * (e >> 2) + 4 * c + (e & 3);
+          sc[kb][e] = key < L ? sc[kb][e] * qk : -INFINITY;
+          tmax = fmaxf(tmax, sc[kb][e]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m, tmax);  // finite: every stage has a valid key
+      const float cf = exp2f(m - mn);
+      m = mn;
+      lsum *= cf;
+#pragma unroll
+      for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] *= cf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          p[e] = exp2f(sc[kb][e] - mn);
+          lsum += p[e];
+        }
+        bf16x8 ph[2], pl[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          uint32_t wh[4], wl[4];
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            const float a = p[8 * st + 2 * q2], a2 = p[8 * st + 2 * q2 + 1];
+            wh[q2] = pack_bf16(a, a2);
+            wl[q2] = pack_bf16(a - __uint_as_float(wh[q2] << 16), a2 - __uint_as_float(wh[q2] & 0xFFFF0000u));
+          }
+          uint4 uh{wh[0], wh[1], wh[2], wh[3]}, ul{wl[0], wl[1], wl[2], wl[3]};
+          ph[st] = *reinterpret_cast<bf16x8*>(&uh);
+          pl[st] = *reinterpret_cast<bf16x8*>(&ul);
+        }
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const bf16x8 vf = lds_read_tr_x2(sl + kb * 32 * ROW + vof[st][0][blk],
+                                             sl + kb * 32 * ROW + vof[st][1][blk]);
+            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[st], acc[blk], 0, 0, 0);
+            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[st], acc[blk], 0, 0, 0);
+          }
+      }
+    }
+    // merge with the row's path partial; lane writes hd blk*32 + 8 e4 + 4 c + 0..3
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (row_ok) {
+      const float* ao = anc_o + ((size_t)r * Hq + h) * HD + 4 * c;
+      float4 av[NBLK][4];
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) av[blk][e4] = *reinterpret_cast<const float4*>(ao + blk * 32 + 8 * e4);
+      const float2 a = anc_ml[(size_t)r * Hq + h];
+      const float ma = a.x * LOG2E;
+      const float Mt = fmaxf(m, ma);
+      const float fd = m == -INFINITY ? 0.f : exp2f(m - Mt);
+      const float fa = exp2f(ma - Mt);
+      const float inv = 1.0f / (lsum * fd + a.y * fa);
+      const float sd = fd * inv, sa = fa * inv;
+      uint16_t* op = O + (((size_t)b * n_int + r) * Hq + h) * HD + 4 * c;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const float4 an = av[blk][e4];
+          *reinterpret_cast<uint2*>(op + blk * 32 + 8 * e4) =
+              uint2{pack_bf16(acc[blk][4 * e4] * sd + an.x * sa, acc[blk][4 * e4 + 1] * sd + an.y * sa),
+                    pack_bf16(acc[blk][4 * e4 + 2] * sd + an.z * sa, acc[blk][4 * e4 + 3] * sd + an.w * sa)};
+        }
+    }
+  }
+  wait_vmcnt<0>();  // nothing may still target LDS at exit
+}
+
 int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
                     int32_t hd, const void* Qn, const void* Kd, const void* Vd,
                     const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
@@ -975,7 +1201,7 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
     const int dpw = int(std::max(1L, B / chunks));
     const long grid = blocks * ((B + dpw - 1) / dpw);
     if (hd == 128)
-      doc_attn_rows_kernel<128><<<grid, 256, 0, s>>>(B, dpw, n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+      doc_attn_rows_dma_kernel<<<grid, 256, 0, s>>>(B, dpw, n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
     else
       doc_attn_rows_kernel<64><<<grid, 256, 0, s>>>(B, dpw, n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   }
