@@ -250,6 +250,55 @@ __global__ __launch_bounds__(256) void rownorm_any_kernel(const float* __restric
   for (int i = threadIdx.x; i < d; i += 256) out[(size_t)r * d + i] = from_f32<T>(val(i) * rs);
 }
 
+// Few rows: one workgroup per row, each thread holding up to RB4 float4 chunks of
+// it (the n_part partials' loads all issued before the sums), one block reduction.
+template <typename T, int RB4>
+__global__ __launch_bounds__(256) void rownorm_block_kernel(const float* __restrict__ y, int n, int d,
+                                                            int n_part, float eps, T* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const int d4 = d / 4;
+  float4 v[RB4];
+#pragma unroll
+  for (int i = 0; i < RB4; ++i) {
+    const int c = t + 256 * i;
+    v[i] = c < d4 ? reinterpret_cast<const float4*>(y + (size_t)r * d)[c] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int p = 1; p < n_part; ++p) {
+    float4 w[RB4];
+#pragma unroll
+    for (int i = 0; i < RB4; ++i) {
+      const int c = t + 256 * i;
+      w[i] = c < d4 ? reinterpret_cast<const float4*>(y + ((size_t)p * n + r) * d)[c]
+                    : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < RB4; ++i) {
+      v[i].x += w[i].x; v[i].y += w[i].y; v[i].z += w[i].z; v[i].w += w[i].w;
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < RB4; ++i) {
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = block_sum256<T>(ss, red);
+  const float rs = 1.0f / sqrtf(ss / float(d) + eps);
+#pragma unroll
+  for (int i = 0; i < RB4; ++i) {
+    const int c = t + 256 * i;
+    if (c >= d4) continue;
+    T* o = out + (size_t)r * d + 4 * c;
+    o[0] = from_f32<T>(v[i].x * rs);
+    o[1] = from_f32<T>(v[i].y * rs);
+    o[2] = from_f32<T>(v[i].z * rs);
+    o[3] = from_f32<T>(v[i].w * rs);
+  }
+}
+
 // One wave per row, the row held in registers: lane l takes the float4 chunks
 // l, l + 64, ... (at most RN4 of them, so d <= 256 RN4), summed over the n_part
 // partials in a fixed order; one read of y, one write of h.
@@ -328,6 +377,11 @@ int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_
       rownorm_any_kernel<bf16_t><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
     else
       rownorm_any_kernel<float><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+  } else if (n <= 2048 && n_part > 1) {  // few rows, split-K partials: a workgroup per row
+    if (dt == TCS_BF16)
+      rownorm_block_kernel<bf16_t, 4><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+    else
+      rownorm_block_kernel<float, 4><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
   } else if (dt == TCS_BF16) {
     if (d <= 256 * 10)
       rownorm_kernel<bf16_t, 10><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));

@@ -19,6 +19,8 @@ namespace tcs {
 constexpr int HEAD_BN = 256;   // vocabulary entries per tile
 constexpr int HEAD_SEG = 128;  // vocabulary entries per edge segment (and bf16 partial)
 constexpr int HEAD_WGS = 256;  // persistent bf16 head: one workgroup per CU
+// below this many rows the matrix-core head stores its (max, sum) partials row-major
+constexpr int LSE_ROWMAJOR_MAX_ROWS = 4096;
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t* __restrict__ a, int n, int key) {
   int lo = 0, hi = n;
@@ -539,7 +541,11 @@ __device__ __forceinline__ void ring_body(
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
       const int r = r0 + rloc + 32 * jn;
-      if (lane < 32 && r < R) part[(size_t)(2 * vt + wm) * R + r] = ms[jn];
+      // few rows: partials [row][half-tile], so each row's are contiguous for the
+      // finalisation; else [half-tile][row]
+      const size_t pi = R < LSE_ROWMAJOR_MAX_ROWS ? (size_t)r * (2 * n_vt) + 2 * vt + wm
+                                                  : (size_t)(2 * vt + wm) * R + r;
+      if (lane < 32 && r < R) part[pi] = ms[jn];
     }
     }
     // the next tile's W(0) and h(0) are in slots 0 and 1 (landed at the last barrier)
@@ -675,6 +681,39 @@ __global__ __launch_bounds__(256) void lse_finalize_wave_kernel(int R, int n_par
   if (lane == 0) lse[r] = m + logf(s);
 }
 
+// Few rows (partials stored row-major by the matrix-core head): one workgroup per
+// row, every thread with its own strided share of the row's partials (all loads
+// issued before the merges), then a workgroup merge.
+__global__ __launch_bounds__(256) void lse_finalize_block_kernel(int R, int n_parts,
+                                                                 const float2* __restrict__ part,
+                                                                 float* __restrict__ lse) {
+  __shared__ float2 red[4];
+  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float m = -INFINITY, s = 0.f;
+  const float2* pr = part + (size_t)r * n_parts;  // this row's partials, contiguous
+  for (int t0 = t; t0 < n_parts; t0 += 256 * 8) {
+    float2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = t0 + 256 * u;
+      p[u] = k < n_parts ? pr[k] : float2{-INFINITY, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) lse_merge(m, s, p[u].x, p[u].y);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    lse_merge(m, s, m2, s2);
+  }
+  if (lane == 0) red[wave] = float2{m, s};
+  __syncthreads();
+  if (t == 0) {
+    for (int w = 1; w < 4; ++w) lse_merge(m, s, red[w].x, red[w].y);
+    lse[r] = m + logf(s);
+  }
+}
+
 // lp[b, c] = logit - lse[row of the edge's parent]; lp[b, root] = 0.
 __global__ void lp_finalize_kernel(int B, int n_int, int n_nodes, const int32_t* __restrict__ e_qrow,
                                    const int32_t* __restrict__ e_child, const float* __restrict__ lse,
@@ -776,7 +815,8 @@ int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int
 int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
                       int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                       const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
-                      const int32_t* e_child, float* lse, float* lp, const void* prep, void* part) {
+                      const int32_t* e_child, float* lse, float* lp, const void* prep, void* part,
+                      bool finalize_lp) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = B * n_int;
   if (R <= 0) return TCS_OK;
@@ -809,13 +849,17 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
   timer_end(TCS_TIMER_HEAD, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "lmhead: %s", hipGetErrorString(e));
-  if (R < 16384)
+  if (h_dtype == TCS_BF16 && R < LSE_ROWMAJOR_MAX_ROWS)
+    lse_finalize_block_kernel<<<R, 256, 0, s>>>(R, n_parts, p, lse);
+  else if (R < 16384)
     lse_finalize_wave_kernel<<<(R + 3) / 4, 256, 0, s>>>(R, n_parts, p, lse);
   else
     lse_finalize_kernel<<<(R + 255) / 256, 256, 0, s>>>(R, n_parts, p, lse);
-  const long nlp = long(B) * n_nodes;
-  lp_finalize_kernel<<<int((nlp + 255) / 256), 256, 0, s>>>(B, n_int, n_nodes, e_qrow, e_child, lse,
-                                                             lp);
+  if (finalize_lp) {
+    const long nlp = long(B) * n_nodes;
+    lp_finalize_kernel<<<int((nlp + 255) / 256), 256, 0, s>>>(B, n_int, n_nodes, e_qrow, e_child,
+                                                               lse, lp);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "lmhead finalize: %s", hipGetErrorString(e));
   return TCS_OK;

@@ -136,6 +136,7 @@ int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie,
 struct PrepLayout {
   size_t total;
   void *a_nodes, *Qn, *Kn, *Vn, *anc, *head, *gemm_zero;
+  int32_t* node_qrow;
   size_t gemm_zero_bytes;
 };
 
@@ -156,6 +157,7 @@ static PrepLayout prep_layout(const tcs_model* m, const tcs_trie_dev* t, int32_t
   P.gemm_zero_bytes = m->dtype == TCS_BF16 && gemm_ring_ok(R, m->d, int32_t(qd))
                           ? gemm_ring_zero_bytes(int32_t(qd)) : 0;
   P.gemm_zero = c.take<char>(P.gemm_zero_bytes);
+  P.node_qrow = c.take<int32_t>(t->n_nodes);
   P.total = c.used;
   return P;
 }
@@ -243,6 +245,7 @@ static int prepare_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t,
     if ((rc = launch_anc_attn(stream, dt, n_int, m->Hq, m->Hkv, m->hd, P.Qn, P.Kn, P.Vn, t->qparent, scale, ml, ao))) return rc;
   }
   if ((rc = launch_zero_fill(stream, P.gemm_zero, P.gemm_zero_bytes))) return rc;
+  if ((rc = launch_node_qrow(stream, t, P.node_qrow))) return rc;
   return launch_lmhead_prep(stream, dt, B, n_int, t->n_nodes, m->d, m->V, t->e_tok, t->e_qrow,
                             t->e_child, t->n_nodes - 1, P.head);
 }
@@ -287,10 +290,12 @@ static int run_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, con
   if (rc) return rc;
   if ((rc = launch_rownorm(stream, dt, L.y, R, m->d, gemm_resid_splits(dt, R, m->d, qd), m->eps,
                            L.h))) return rc;
+  // the head leaves raw child logits in lp; the path sum subtracts lse itself
   if ((rc = launch_lmhead_run(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,
                               m->W_scale, t->e_tok, t->e_qrow, t->e_child, L.lse, L.lp, P.head,
-                              L.part))) return rc;
-  return launch_path_sum(stream, B, t, L.lp, ll ? ll : static_cast<float*>(L.ll), prob, label);
+                              L.part, false))) return rc;
+  return launch_path_sum(stream, B, t, L.lp, ll ? ll : static_cast<float*>(L.ll), prob, label,
+                         L.lse, P.node_qrow);
 }
 
 size_t tcs_classify_prepared_bytes(const tcs_model* model, const tcs_trie_dev* trie, int32_t B) {

@@ -88,10 +88,12 @@ size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_no
 int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
                        int32_t d, int32_t V, const int32_t* e_tok, const int32_t* e_qrow,
                        const int32_t* e_child, int32_t n_edges, void* prep);
+// finalize_lp = false leaves the raw child logits in lp (for a fused path sum).
 int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
                       int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                       const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
-                      const int32_t* e_child, float* lse, float* lp, const void* prep, void* part);
+                      const int32_t* e_child, float* lse, float* lp, const void* prep, void* part,
+                      bool finalize_lp = true);
 int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
                   int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                   const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
@@ -106,7 +108,13 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
                     const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
                     float scale, void* O);
 
+// Path sums, label softmax and argmax.  lp: edge log-probs [B, n_nodes]; or, with
+// lse and node_qrow set, the raw child logits, each edge's log-prob being
+// lp - lse[b n_int + node_qrow[node]].
 int launch_path_sum(void* stream, int32_t B, const tcs_trie_dev* trie, const float* lp,
-                    float* ll, float* prob, int32_t* label);
+                    float* ll, float* prob, int32_t* label, const float* lse = nullptr,
+                    const int32_t* node_qrow = nullptr);
+// node_qrow[v] = query row of v's parent, for every non-root node v.
+int launch_node_qrow(void* stream, const tcs_trie_dev* trie, int32_t* node_qrow);
 
 }  // namespace tcs
