@@ -192,7 +192,6 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 constexpr int DMA_BK = 64;
 constexpr int DMA_SLOT_BYTES = 256 * DMA_BK * 2;  // one operand tile, bf16: 32 KB
 constexpr int DMA_SLOTS = 5;
-constexpr int DMA_LOADS_PER_OPERAND = 8;          // per wave (per thread) per tile
 
 __device__ __forceinline__ int dma_swz(int r) { return (r ^ (r >> 3)) & 7; }  // r in [0, 16)
 

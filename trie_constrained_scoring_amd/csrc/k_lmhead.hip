@@ -75,7 +75,11 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
 // workgroup per CU walks its own sequence of 256 x 256 tiles (head_tile_coords),
 // and the LDS ring of five 32 KB operand slots runs on across tile boundaries, so
 // the first k-tiles of the next tile load while the current one finishes and while
-// its epilogue runs.
+// its epilogue runs.  The workgroup has 8 waves, two per SIMD, each owning 128
+// vocabulary entries x 64 rows (4 x 2 blocks of v_mfma_f32_32x32x16_bf16): while
+// one wave of a SIMD waits on LDS reads, DMA issue or the step barrier, the other
+// keeps the matrix core fed (measured on MI355X: 9% faster than 4 waves of
+// 128 x 128 on a 97k-row head, at the cost of 1.5x the LDS reads).
 //
 // Global k-step g (over all tiles of this workgroup) keeps W's k-tile in slot
 // 2g mod 5 and h's in slot 2g+1 mod 5; while step g is multiplied, h(g+1) and
@@ -100,31 +104,36 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
 // permuted the same way on both operands (lane half c supplies k 32m + 16c + 8s +
 // 0..7 in step 2m+s), which leaves the dot products unchanged.
 
-// One operand k-tile of this wave into an LDS slot: load j (0..7) fills slot rows
-// wave*64 + 8j .. +7 (1 KB), lane i writing 16 bytes at row i/8, position i%8;
+// The ring kernel runs 8 waves (two per SIMD); each owns 128 vocabulary entries x
+// 64 rows of the 256 x 256 tile and loads 1/8 of every operand k-tile.
+constexpr int RING_WAVES = 8;
+constexpr int RING_LOADS = 4;   // bf16 operand: 1 KB loads per wave per k-tile
+constexpr int RING_LOADS8 = 2;  // fp8 W: 1 KB loads per wave per k-tile
+
+// One bf16 operand k-tile of this wave into an LDS slot: load j (0..3) fills slot
+// rows wave*32 + 8j .. +7 (1 KB), lane i writing 16 bytes at row i/8, position i%8;
 // `vo` holds each load's lane byte offset, `k` the k-tile (scalar offset).
 __device__ __forceinline__ void head_issue(const void* base, int bytes, int k, uint8_t* sl,
-                                           int wave, const int (&vo)[DMA_LOADS_PER_OPERAND]) {
+                                           int wave, const int (&vo)[RING_LOADS]) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
   const int so = k * DMA_BK * 2;
 #pragma unroll
-  for (int j = 0; j < DMA_LOADS_PER_OPERAND; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 64 + j * 8) * 128), 16, vo[j],
+  for (int j = 0; j < RING_LOADS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 32 + j * 8) * 128), 16, vo[j],
                                              so, 0, 0);
 }
 
-// fp8 W k-tile (256 rows x 64 bytes, 16 KB) of this wave: load j (0..3) fills slot
-// rows wave*64 + 16j .. +15, lane i writing 16 bytes at row i/4, position i%4.
-constexpr int DMA8_LOADS = 4;
+// fp8 W k-tile (256 rows x 64 bytes, 16 KB) of this wave: load j (0..1) fills slot
+// rows wave*32 + 16j .. +15, lane i writing 16 bytes at row i/4, position i%4.
 __device__ __forceinline__ void head_issue8(const void* base, int bytes, int k, uint8_t* sl,
-                                            int wave, const int (&vo)[DMA8_LOADS]) {
+                                            int wave, const int (&vo)[RING_LOADS8]) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
   const int so = k * DMA_BK;
 #pragma unroll
-  for (int j = 0; j < DMA8_LOADS; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 64 + j * 16) * 64), 16, vo[j],
+  for (int j = 0; j < RING_LOADS8; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 32 + j * 16) * 64), 16, vo[j],
                                              so, 0, 0);
 }
 // fp8 W slot: row r (64 bytes) keeps its 16-byte chunk c at position c ^ dma8_swz(r),
@@ -144,9 +153,9 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // v[jn] = acc[t / 16][jn][t % 16] for a wave-uniform t in [0, 64): a binary
 // select tree on the six bits of t (63 selects per jn, six lane masks), so the
 // accumulators are only read in place.
-__device__ __forceinline__ void head_pick(int t, const f32x16 (&acc)[4][4], float (&v)[4]) {
+__device__ __forceinline__ void head_pick(int t, const f32x16 (&acc)[4][2], float (&v)[2]) {
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn) {
+  for (int jn = 0; jn < 2; ++jn) {
     float x[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -161,17 +170,17 @@ __device__ __forceinline__ void head_pick(int t, const f32x16 (&acc)[4][4], floa
   }
 }
 
-// Max and sum of exp of each of the lane's four rows (jn) over its 64 entries
+// Max and sum of exp of each of the lane's two rows (jn) over its 64 entries
 // plus the partner lane's (l ^ 32); entries at or past `vlim` are excluded when
 // MASK.  One row at a time, so only that row's 64 values are live.
 // exp2 is the hardware instruction: arguments are <= 0, and terms below 2^-126
 // of the row maximum, which it flushes, are far below fp32 resolution of the sum.
 template <bool MASK>
-__device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][4], int vlim,
-                                              float2 (&out)[4]) {
+__device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][2], int vlim,
+                                              float2 (&out)[2]) {
   constexpr float LOG2E = 1.4426950408889634f;
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn) {
+  for (int jn = 0; jn < 2; ++jn) {
     float m = -INFINITY;
 #pragma unroll
     for (int im = 0; im < 4; ++im)
@@ -197,7 +206,7 @@ __device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][4], int vli
 
 // acc[im][jn][e] *= scale of vocabulary entry vb + 32 im + 8 (e>>2) + (e&3) (fp8
 // head); entries at or past V are left alone (the row sums exclude them).
-__device__ __forceinline__ void head_scale_rows(f32x16 (&acc)[4][4], const float* __restrict__ w_scale,
+__device__ __forceinline__ void head_scale_rows(f32x16 (&acc)[4][2], const float* __restrict__ w_scale,
                                                 int vb, int V) {
 #pragma unroll
   for (int im = 0; im < 4; ++im)
@@ -214,7 +223,7 @@ __device__ __forceinline__ void head_scale_rows(f32x16 (&acc)[4][4], const float
         sc.w = 1.f;
       }
 #pragma unroll
-      for (int jn = 0; jn < 4; ++jn) {
+      for (int jn = 0; jn < 2; ++jn) {
         acc[im][jn][4 * g + 0] *= sc.x;
         acc[im][jn][4 * g + 1] *= sc.y;
         acc[im][jn][4 * g + 2] *= sc.z;
@@ -266,7 +275,7 @@ __device__ __forceinline__ void ring_body(
   const int nk = d / DMA_BK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave & 1, wr = wave >> 1;  // vocabulary half, row quarter
 
   auto coords = [&](int w, int& rt, int& vt) __attribute__((always_inline)) {
     if constexpr (GEMM) return gemm_tile_coords(w * HEAD_WGS + bslot, n_rt, n_vt, rt, vt);
@@ -296,23 +305,23 @@ __device__ __forceinline__ void ring_body(
     return Span{W, h, 0, 0};
   };
 
-  // Load j (0..7) of this wave fills slot rows wave*64 + 8j .. +7 (1 KB): lane i
+  // Load j (0..3) of this wave fills slot rows wave*32 + 8j .. +7 (1 KB): lane i
   // writes row i/8, position i%8, which holds global chunk (i%8) ^ swz(row % 16);
   // row % 16 = 8*(j&1) + i/8.  The k offset goes in the scalar offset.
   const int lr = lane >> 3, lp = lane & 7;
-  int vo[DMA_LOADS_PER_OPERAND];
+  int vo[RING_LOADS];
 #pragma unroll
-  for (int j = 0; j < DMA_LOADS_PER_OPERAND; ++j)
-    vo[j] = ((wave * 64 + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
-  // fp8 W: load j (0..3) fills rows wave*64 + 16j + i/4, position i%4, which holds
+  for (int j = 0; j < RING_LOADS; ++j)
+    vo[j] = ((wave * 32 + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
+  // fp8 W: load j (0..1) fills rows wave*32 + 16j + i/4, position i%4, which holds
   // chunk (i%4) ^ dma8_swz(row % 16)
-  int vo8[DMA8_LOADS];
+  int vo8[RING_LOADS8];
 #pragma unroll
-  for (int j = 0; j < DMA8_LOADS; ++j) {
-    const int row = wave * 64 + j * 16 + (lane >> 2);
+  for (int j = 0; j < RING_LOADS8; ++j) {
+    const int row = wave * 32 + j * 16 + (lane >> 2);
     vo8[j] = row * d + (((lane & 3) ^ dma8_swz(row & 15)) << 4);
   }
-  constexpr int W_LOADS = W8 ? DMA8_LOADS : DMA_LOADS_PER_OPERAND;
+  constexpr int W_LOADS = W8 ? RING_LOADS8 : RING_LOADS;
   int w = next_valid(w_lo);
   if (w >= rounds) return;
   // A tile runs nk5 = nk rounded up to a multiple of 5 steps, so every tile starts
@@ -361,11 +370,11 @@ __device__ __forceinline__ void ring_body(
   int fo8[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) fo8[m] = (lane & 31) * 64 + (((2 * m + (lane >> 5)) ^ dma8_swz(lane & 15)) << 4);
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][4], fb[2][2];
   uint4 wraw[4];  // fp8 W codes of the current pair of k-steps
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
   auto read_frags = [&](const uint8_t* sa, const uint8_t* sb, int ks, bf16x8 (&xa)[4],
-                        bf16x8 (&xb)[4]) {
+                        bf16x8 (&xb)[2]) {
     if constexpr (W8) {
       if ((ks & 1) == 0) {
 #pragma unroll
@@ -373,43 +382,44 @@ __device__ __forceinline__ void ring_body(
           wraw[i] = *reinterpret_cast<const uint4*>(sa + (wm * 128 + i * 32) * 64 + fo8[ks >> 1]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
+      for (int j = 0; j < 2; ++j)
+        xb[j] = *reinterpret_cast<const bf16x8*>(sb + (wr * 64 + j * 32) * 128 + fo[ks]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         xa[i] = (ks & 1) ? e4m3x8_to_bf16(wraw[i].z, wraw[i].w) : e4m3x8_to_bf16(wraw[i].x, wraw[i].y);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
         xa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + fo[ks]);
-        xb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * 128 + i * 32) * 128 + fo[ks]);
-      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xb[j] = *reinterpret_cast<const bf16x8*>(sb + (wr * 64 + j * 32) * 128 + fo[ks]);
     }
   };
-  auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[4]) {
+  auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
   };
   auto interleave_ds = [&]() __attribute__((always_inline)) {
     if constexpr (W8) {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (code conversion)
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU (code conversion)
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
     } else {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < 6; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
     }
   };
@@ -427,11 +437,11 @@ __device__ __forceinline__ void ring_body(
       read_frags(slot[sA], slot[sB], 1, fa[1], fb[1]);
       mfma_step(fa[0], fb[0]);
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        if (g < DMA_LOADS_PER_OPERAND + W_LOADS)
+      for (int g = 0; g < 8; ++g) {
+        if (g < RING_LOADS + W_LOADS)
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
-        if (W8) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
-        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+        if (W8) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        else if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
       read_frags(slot[sA], slot[sB], 2, fa[0], fb[0]);
@@ -460,12 +470,12 @@ __device__ __forceinline__ void ring_body(
   read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
 
   const int vhalf = wm * 128 + 4 * (lane >> 5);  // + 32 im + 8 (e>>2) + (e&3)
-  const int rloc = wn * 128 + (lane & 31);       // + 32 jn
+  const int rloc = wr * 64 + (lane & 31);        // + 32 jn
   for (; w < rounds;) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     using F = std::false_type;
@@ -491,7 +501,7 @@ __device__ __forceinline__ void ring_body(
     // r0 + rloc + 32 jn
     if constexpr (GEMM) {
 #pragma unroll
-      for (int jn = 0; jn < 4; ++jn) {
+      for (int jn = 0; jn < 2; ++jn) {
         const int r = r0 + rloc + 32 * jn;
         if (r >= R) continue;
         const uint16_t* x = go.E + (size_t)go.token[go.qnode[r % go.n_int]] * V;
@@ -524,22 +534,21 @@ __device__ __forceinline__ void ring_body(
     for (int k = list_head[(2 * vt + wm) * n_rt + rt]; k >= 0;) {
       const int4 q = rec[k];
       const int t = q.z & 63, hh = (q.z >> 6) & 1, rit = q.z >> 7;
-      if ((rit >> 7) == wn) {  // row r0 + rit is in this wave's half of the rows
-        float v[4];
+      if ((rit >> 6) == wr) {  // row r0 + rit is in this wave's quarter of the rows
+        float v[2];
         head_pick(t, acc, v);
-        const int jn = (rit >> 5) & 3;
-        const float x = jn == 0 ? v[0] : jn == 1 ? v[1] : jn == 2 ? v[2] : v[3];
+        const float x = ((rit >> 5) & 1) ? v[1] : v[0];
         if (lane == (rit & 31) + 32 * hh) raw[q.y] = x;
       }
       k = q.x;
     }
     // per hidden row: max and sum of exp over this wave's 128 vocabulary entries
     // (only the last vocabulary tile has entries at or past V)
-    float2 ms[4];
+    float2 ms[2];
     if (v0 + HEAD_BN <= V) head_rows_lse<false>(acc, vlim, ms);
     else head_rows_lse<true>(acc, vlim, ms);
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
+    for (int jn = 0; jn < 2; ++jn) {
       const int r = r0 + rloc + 32 * jn;
       // few rows: partials [row][half-tile], so each row's are contiguous for the
       // finalisation; else [half-tile][row]
@@ -564,7 +573,7 @@ __device__ __forceinline__ void ring_body(
 
 // The output head (bf16 or fp8 weights).
 template <bool W8>
-__global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
+__global__ __launch_bounds__(64 * RING_WAVES, 1) void lmhead_ring_kernel(
     int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
     const float* __restrict__ w_scale, const int32_t* __restrict__ list_head,
     const int4* __restrict__ rec, float* __restrict__ raw, float2* __restrict__ part,
@@ -574,7 +583,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_ring_kernel(
 }
 
 // The output projection of many rows (plain products plus the embedding residual).
-__global__ __launch_bounds__(256, 1) void proj_ring_kernel(int M, int N, int K,
+__global__ __launch_bounds__(64 * RING_WAVES, 1) void proj_ring_kernel(int M, int N, int K,
                                                            const uint16_t* __restrict__ A,
                                                            const uint8_t* __restrict__ B,
                                                            const uint16_t* __restrict__ zero,
@@ -836,9 +845,9 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
     auto wp = static_cast<const uint8_t*>(W);
     auto zp = reinterpret_cast<const uint16_t*>(P.zero);
     if (w_dtype == TCS_FP8_E4M3)
-      lmhead_ring_kernel<true><<<grid, 256, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per);
+      lmhead_ring_kernel<true><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per);
     else
-      lmhead_ring_kernel<false><<<grid, 256, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per);
+      lmhead_ring_kernel<false><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per);
     n_parts = 2 * n_tiles;
   } else {
     dim3 grid(n_tiles, (R + 7) / 8);
@@ -884,7 +893,7 @@ int launch_gemm_ring_resid(void* stream, int32_t M, int32_t N, int32_t K, const 
   const int per = head_rounds_per_wg(rounds);
   const int grid = (rounds + per - 1) / per * HEAD_WGS;
   const RingGemmOut go{C, ldc, static_cast<const uint16_t*>(res.E), res.token, res.qnode, res.n_int};
-  proj_ring_kernel<<<grid, 256, 0, s>>>(M, N, K, static_cast<const uint16_t*>(A),
+  proj_ring_kernel<<<grid, 64 * RING_WAVES, 0, s>>>(M, N, K, static_cast<const uint16_t*>(A),
                                         static_cast<const uint8_t*>(B),
                                         static_cast<const uint16_t*>(zero), per, go);
   const hipError_t e = hipGetLastError();
