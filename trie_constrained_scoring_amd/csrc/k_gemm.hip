@@ -20,15 +20,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
   int mt, nt;
   tile_coords<8>(nbm, nbn, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  // split-K (RESID only): split z takes k in [z K, (z+1) K) and writes its fp32
-  // partial to C + z M ldc; the residual goes with split 0
-  const int z = blockIdx.y;
-  if (z > 0) {
-    A += (size_t)z * K;
-    B += (size_t)z * K;
-    C = static_cast<float*>(C) + (size_t)z * M * ldc;
-    epi = GEMM_PART;
-  }
   f32x4 acc[S::MB][S::NB];
   gemm_mainloop<BM, BN, WM, WN>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
 
@@ -52,8 +43,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
         const float v = acc[i][j][r];
         if (epi == GEMM_RESID) {
           static_cast<float*>(C)[(size_t)row * ldc + col] = v + bf16_to_f32(xres[col]);
-        } else if (epi == GEMM_PART) {
-          static_cast<float*>(C)[(size_t)row * ldc + col] = v;
         } else {
           static_cast<uint16_t*>(C)[(size_t)row * ldc + col] = f32_to_bf16(v);
         }
@@ -135,6 +124,169 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(
       static_cast<uint16_t*>(C)[(size_t)row * ldc + col] = f32_to_bf16(v);
     }
   }
+}
+
+// ------------------------------------------------------------------ bf16 split-K, few rows
+//
+// The output projection of a few hundred to a few thousand rows (e.g. 512 x 2560 x
+// 4096) has too few output tiles to fill the chip, so K is split as well: work item
+// (tile, z) multiplies k-tiles [z nkt / s, (z + 1) nkt / s) of a BM x 128 output
+// tile and writes an fp32 partial (the residual goes with z = 0).  Such a product
+// is bound by how fast each CU pulls operand bytes out of L2 (measured on MI355X:
+// ~16 GB/s per wave for buffer-to-LDS loads, so a CU needs many waves loading), and
+// the partials cost HBM traffic in proportion to s; split_plan picks BM and s from
+// both.  Both operands stream through an NST-stage LDS ring filled by
+// buffer-to-LDS loads: 128 contiguous bytes per operand row and k-tile (whole cache
+// lines), the 16-byte chunk c of row r stored at position c ^ dma_swz(r mod 16), so
+// the fragment reads spread over the banks.  Loads run NST - 1 k-tiles ahead and
+// hold no registers; one barrier per k-tile.  Eight waves split the tile 4 x 2,
+// each (BM/4) x 64 in v_mfma_f32_32x32x16_bf16 blocks (measured on MI355X, the
+// 16x16x32 form delivers half the FLOP rate).
+template <int BM>
+struct SplitShape {
+  static constexpr int BN = 128;
+  static constexpr int NST = BM == 128 ? 4 : 3;  // 128 KB / 144 KB of LDS
+  static constexpr int STAGE = (BM + BN) * 128;  // bytes per k-tile
+  static constexpr int WM = 4, WN = 2;           // waves across the rows / columns
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile: 64 x 64 or 32 x 64
+  static constexpr int MI = TM / 32, NJ = TN / 32;  // 32 x 32 blocks per wave
+  static constexpr int LA = BM / 64;             // 1 KB loads per wave and stage, A
+  static constexpr int LB = BN / 64;             //   and B
+};
+
+// NL 1 KB buffer-to-LDS loads: load j writes dst + 1 KB j (lane i at 16 i) from
+// byte vo[j] + so of a resource over [base, base + bytes).
+template <int NL>
+__device__ __forceinline__ void split_issue(const uint16_t* base, int bytes, int so, uint8_t* dst,
+                                            const int* vo) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NL; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(dst + j * 1024), 16, vo[j], so, 0, 0);
+}
+
+template <int BM>
+__global__ __launch_bounds__(512, 1) void gemm_split_kernel(
+    int M, int N, int K, int s, const uint16_t* __restrict__ A, int lda,
+    const uint16_t* __restrict__ B, int ldb, float* __restrict__ C, int ldc, GemmResid resid) {
+  using S = SplitShape<BM>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::NST * S::STAGE];
+  const int nbm = (M + BM - 1) / BM, nbn = (N + S::BN - 1) / S::BN;
+  // items in order (split, column tile, row tile); XCD x (block i runs on XCD
+  // i % 8) takes a contiguous range of them, which shares operand rows in its L2
+  const int items = nbm * nbn * s;
+  const int per = items / 8, rem = items % 8;
+  const int xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  const int mt = item % nbm, nt = (item / nbm) % nbn, z = item / (nbm * nbn);
+  const int nkt = K / 64;
+  const int kt0 = int(long(z) * nkt / s), nkz = int(long(z + 1) * nkt / s) - kt0;
+  const int m0 = mt * BM, n0 = nt * S::BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int wm = wave % S::WM, wn = wave / S::WM;
+
+  // Rows past M / N lie outside the resources' ranges: their loads are dropped,
+  // and the outputs they feed are not stored.
+  const uint16_t* const abase = A + (size_t)m0 * lda;
+  const uint16_t* const bbase = B + (size_t)n0 * ldb;
+  const int abytes = min(BM, M - m0) * lda * 2, bbytes = min(S::BN, N - n0) * ldb * 2;
+  // load j of an operand: slot row wave * rows/8 + 8 j + lane/8, position lane%8
+  // (holding chunk (lane%8) ^ dma_swz(row mod 16))
+  const int lr = lane >> 3, lp = lane & 7;
+  int voa[S::LA], vob[S::LB];
+#pragma unroll
+  for (int j = 0; j < S::LA; ++j) {
+    const int row = wave * (BM / 8) + 8 * j + lr;
+    voa[j] = (row * lda + (lp ^ dma_swz(row & 15)) * 8) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < S::LB; ++j) {
+    const int row = wave * (S::BN / 8) + 8 * j + lr;
+    vob[j] = (row * ldb + (lp ^ dma_swz(row & 15)) * 8) * 2;
+  }
+  auto slot = [&](int q) { return lds + (q % S::NST) * S::STAGE; };
+  auto issue = [&](int q) __attribute__((always_inline)) {
+    uint8_t* sl = slot(q);
+    const int so = (kt0 + q) * 128;
+    split_issue<S::LA>(abase, abytes, so, sl + wave * (BM / 8) * 128, voa);
+    split_issue<S::LB>(bbase, bbytes, so, sl + (BM + wave * (S::BN / 8)) * 128, vob);
+  };
+
+  // fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32
+  int fo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) fo[ks] = (lane & 31) * 128 + (((2 * ks + (lane >> 5)) ^ dma_swz(lane & 15)) << 4);
+  const int arow = wm * S::TM, brow = BM + wn * S::TN;
+  bf16x8 fa[2][S::MI], fb[2][S::NJ];
+  auto read_frags = [&](const uint8_t* sl, int ks, bf16x8 (&xa)[S::MI], bf16x8 (&xb)[S::NJ]) {
+#pragma unroll
+    for (int i = 0; i < S::MI; ++i)
+      xa[i] = *reinterpret_cast<const bf16x8*>(sl + (arow + 32 * i) * 128 + fo[ks]);
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j)
+      xb[j] = *reinterpret_cast<const bf16x8*>(sl + (brow + 32 * j) * 128 + fo[ks]);
+  };
+  f32x16 acc[S::MI][S::NJ];
+#pragma unroll
+  for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto mfma = [&](const bf16x8 (&xa)[S::MI], const bf16x8 (&xb)[S::NJ]) {
+#pragma unroll
+    for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < S::NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int q = 0; q < S::NST - 1; ++q)
+    if (q < nkz) issue(q);
+  for (int kt = 0; kt < nkz; ++kt) {
+    // this wave's loads of k-tile kt have landed (later ones may be in flight) and
+    // its reads of k-tile kt - 1, whose slot is refilled next, are done
+    if (kt + S::NST - 2 < nkz) wait_vmcnt<(S::NST - 2) * (S::LA + S::LB)>();
+    else wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    if (kt + S::NST - 1 < nkz) issue(kt + S::NST - 1);
+    const uint8_t* sl = slot(kt);
+    // the last k-step's MFMAs of the previous k-tile run under this one's first reads
+    read_frags(sl, 0, fa[0], fb[0]);
+    if (kt > 0) mfma(fa[1], fb[1]);
+    read_frags(sl, 1, fa[1], fb[1]);
+    mfma(fa[0], fb[0]);
+    read_frags(sl, 2, fa[0], fb[0]);
+    mfma(fa[1], fb[1]);
+    read_frags(sl, 3, fa[1], fb[1]);
+    mfma(fa[0], fb[0]);
+  }
+  if (nkz > 0) mfma(fa[1], fb[1]);
+
+  // lane l holds column n0 + brow - BM + 32 j + l%32 of rows
+  // m0 + arow + 32 i + 8 (e/4) + 4 (l/32) + e%4
+  float* const Cz = C + (size_t)z * M * ldc;
+#pragma unroll
+  for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + arow + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (m >= M) continue;
+      const uint16_t* xres = nullptr;
+      if (z == 0) xres = static_cast<const uint16_t*>(resid.E) + (size_t)resid.token[resid.qnode[m % resid.n_int]] * N;
+#pragma unroll
+      for (int j = 0; j < S::NJ; ++j) {
+        const int n = n0 + wn * S::TN + 32 * j + (lane & 31);
+        if (n >= N) continue;
+        float v = acc[i][j][e];
+        if (z == 0) v += bf16_to_f32(xres[n]);
+        Cz[(size_t)m * ldc + n] = v;
+      }
+    }
 }
 
 // ------------------------------------------------------------------ fp32 SIMT
@@ -398,21 +550,36 @@ int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_
 
 template <int BM, int BN, int WM, int WN>
 static void launch_bf16_cfg(hipStream_t s, int M, int N, int K, const void* A, int lda,
-                            const void* B, int ldb, void* C, int ldc, int epi, GemmResid r,
-                            int splits = 1) {
+                            const void* B, int ldb, void* C, int ldc, int epi, GemmResid r) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  gemm_nt_bf16_kernel<BM, BN, WM, WN><<<dim3(tiles, splits), 64 * WM * WN, 0, s>>>(
-      M, N, K / splits, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb,
-      C, ldc, epi, r);
+  gemm_nt_bf16_kernel<BM, BN, WM, WN><<<tiles, 64 * WM * WN, 0, s>>>(
+      M, N, K, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
+      epi, r);
+}
+
+// Tile rows and K split of gemm_split_kernel for an M x N product: BM x 128 tiles
+// (BM = 256 past ~640 rows, for fewer operand bytes per FLOP), and as many K
+// splits as keep the items within one per CU.
+static void split_plan(int M, int N, int K, int& bm, int& s) {
+  bm = M <= 640 ? 128 : 256;
+  const long tiles = long((M + bm - 1) / bm) * ((N + 127) / 128);
+  s = tiles >= 256 ? 1 : int(256 / tiles);
+  s = std::min(s, std::min(8, K / GEMM_BK));
+}
+
+// Few-row bf16 products with a residual go to gemm_split_kernel (K-split partials);
+// larger ones to the generic tiles, one partial.
+static bool use_split(tcs_dtype dt, int M, int N) {
+  if (dt != TCS_BF16 || M <= 64) return false;
+  const long t256 = long((M + 255) / 256) * ((N + 255) / 256);
+  const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
+  return t256 < 512 && t128 < 512;
 }
 
 int gemm_resid_splits(tcs_dtype dt, int32_t M, int32_t N, int32_t K) {
-  if (dt != TCS_BF16 || M <= 64) return 1;
-  const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
-  if (long((M + 255) / 256) * ((N + 255) / 256) >= 512 || t128 >= 512) return 1;
-  const long tiles = long((M + 63) / 64) * ((N + 63) / 64);
-  int s = 1;
-  while (s < 8 && tiles * s * 2 <= 2048 && (K / GEMM_BK) % (s * 2) == 0) s *= 2;
+  if (!use_split(dt, M, N)) return 1;
+  int bm, s;
+  split_plan(M, N, K, bm, s);
   return s;
 }
 
@@ -426,7 +593,20 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
     if (K % GEMM_BK != 0) return fail(TCS_EUNSUPPORTED, "gemm: K=%d is not a multiple of 64", K);
     const long t256 = long((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
-    if (M <= 64 && long(M) * lda < (1L << 30) && long(N) * ldb < (1L << 30)) {
+    if (epi == GEMM_RESID && use_split(dt, M, N)) {
+      // 16-byte operand chunks; a tile's rows span < 2^31 bytes
+      if (lda % 8 != 0 || ldb % 8 != 0 || long(std::min(M, 256)) * lda >= (1L << 30) ||
+          long(std::min(N, 128)) * ldb >= (1L << 30))
+        return fail(TCS_EUNSUPPORTED, "gemm: row strides %d, %d unsupported", lda, ldb);
+      int bm, sp;
+      split_plan(M, N, K, bm, sp);
+      const int grid = ((M + bm - 1) / bm) * ((N + 127) / 128) * sp;
+      auto a = static_cast<const uint16_t*>(A);
+      auto b = static_cast<const uint16_t*>(B);
+      auto c = static_cast<float*>(C);
+      if (bm == 128) gemm_split_kernel<128><<<grid, 512, 0, s>>>(M, N, K, sp, a, lda, b, ldb, c, ldc, r);
+      else gemm_split_kernel<256><<<grid, 512, 0, s>>>(M, N, K, sp, a, lda, b, ldb, c, ldc, r);
+    } else if (M <= 64 && long(M) * lda < (1L << 30) && long(N) * ldb < (1L << 30)) {
       const int g = (N + 15) / 16;
       auto a = static_cast<const uint16_t*>(A);
       auto b = static_cast<const uint16_t*>(B);
@@ -439,8 +619,7 @@ int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N
     else if (t128 >= 512)
       launch_bf16_cfg<128, 128, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
     else
-      launch_bf16_cfg<64, 64, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r,
-                                    epi == GEMM_RESID ? gemm_resid_splits(dt, M, N, K) : 1);
+      launch_bf16_cfg<64, 64, 2, 2>(s, M, N, K, A, lda, B, ldb, C, ldc, epi, r);
   } else {
     dim3 grid((N + 63) / 64, (M + 63) / 64);
     gemm_nt_f32_kernel<<<grid, 256, 0, s>>>(M, N, K, static_cast<const float*>(A), lda,

@@ -49,9 +49,9 @@ int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_
 //   STORE: C stored in dtype dt (rounded) with leading dimension ldc.
 //   RESID: C + E[tok(row)] stored as fp32, tok(row) = token[qnode[row % n_int]]; may
 //          be split over K into gemm_resid_splits(...) fp32 partials [splits][M][ldc]
-//          (the residual in the first), to be summed by launch_rownorm.
-//   PART:  (internal) one split's fp32 partial.
-enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_PART = 2 };
+//          (the residual in the first), to be summed by launch_rownorm.  lda and ldb
+//          must then be multiples of 8.
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1 };
 int gemm_resid_splits(tcs_dtype dt, int32_t M, int32_t N, int32_t K);
 struct GemmResid {
   const void* E;
