@@ -5,7 +5,10 @@
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
     python bench.py --head-probe --config 3  # head alone: workload-like vs constant operands
 
-One step is one ``tcs_classify_run`` call over one batch of synthetic documents:
+One step is one ``tcs_classify_run`` call over one batch of synthetic documents
+(consecutive steps alternate over ``--streams`` HIP streams, default 2, each with its
+own run workspace, so one batch's attention and projection can use the CUs the
+previous batch's output head leaves idle in its last partial round of tiles):
 ancestor-masked tree attention over the documents, output projection + RMSNorm,
 the full-vocabulary output head with fused log-sum-exp and child gather, and the
 path sums / label softmax / argmax.  Inputs are resident in HBM before timing.
@@ -76,7 +79,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup(cid: int):
+def setup(cid: int, streams: int = 1):
     import torch
     import trie_constrained_scoring_amd as tcs
     from synth import config, make_inputs
@@ -95,38 +98,48 @@ def setup(cid: int):
     prep = tcs.Prepared(model, td, docs.B)
     torch.cuda.synchronize()
     prep_ms = (time.perf_counter() - t0) * 1e3
-    ws = torch.empty(tcs.classify_run_workspace_bytes(model, td, docs), dtype=torch.uint8, device="cuda")
     B, M = docs.B, trie.n_labels
-    out = dict(label=torch.empty(B, dtype=torch.int32, device="cuda"),
-               prob=torch.empty((B, M), dtype=torch.float32, device="cuda"),
-               ll=torch.empty((B, M), dtype=torch.float32, device="cuda"))
+    # one run workspace and output set per batch in flight
+    ws, out = [], []
+    for _ in range(max(1, streams)):
+        ws.append(torch.empty(tcs.classify_run_workspace_bytes(model, td, docs), dtype=torch.uint8,
+                              device="cuda"))
+        out.append(dict(label=torch.empty(B, dtype=torch.int32, device="cuda"),
+                        prob=torch.empty((B, M), dtype=torch.float32, device="cuda"),
+                        ll=torch.empty((B, M), dtype=torch.float32, device="cuda")))
     torch.cuda.synchronize()
     return dict(cfg=cfg, inp=inp, trie=trie, td=td, model=model, docs=docs, ws=ws, out=out,
                 trie_ms=trie_ms, prep=prep, prep_ms=prep_ms)
 
 
 def run_steps(S, steps, warmup):
-    """Seconds per step over `steps` timed steps (after `warmup` untimed ones), then
-    the mean duration (ms) of the head and document-attention kernel launches over a
-    second pass of `steps` identical steps in which the library brackets those
-    launches with HIP events on their stream (recording events costs host time per
-    launch, so that pass is kept out of the throughput figure)."""
+    """Seconds per step over `steps` timed steps (after `warmup` untimed ones; step i
+    runs on stream i mod len(S["ws"]) with workspace i mod len(S["ws"])), then the mean
+    duration (ms) of the head and document-attention kernel launches over a second
+    pass of `steps` identical steps, all on one stream, in which the library brackets
+    those launches with HIP events on their stream (recording events costs host time
+    per launch, so that pass is kept out of the throughput figure)."""
     import torch
     import trie_constrained_scoring_amd as tcs
 
-    def step():
-        tcs.classify(S["model"], S["td"], S["docs"], ws=S["ws"], prepared=S["prep"], **S["out"])
-    for _ in range(warmup):
-        step()
+    n = len(S["ws"])
+    streams = [torch.cuda.current_stream()] if n == 1 else [torch.cuda.Stream() for _ in range(n)]
+
+    def step(i, k=None):
+        k = i % n if k is None else k
+        tcs.classify(S["model"], S["td"], S["docs"], ws=S["ws"][k], prepared=S["prep"],
+                     stream=streams[k], **S["out"][k])
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(i)
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
     tcs.timing_enable(True)
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(i, 0)
     torch.cuda.synchronize()
     kern = {}
     for name, timer in (("head", tcs.TCS_TIMER_HEAD), ("doc_attn", tcs.TCS_TIMER_DOC_ATTN)):
@@ -250,6 +263,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--extra", default="3,4", help="other label-set sizes to report (config ids)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="batches in flight: consecutive steps alternate over this many HIP streams, "
+                         "each with its own run workspace")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (3 launches) and exit")
     ap.add_argument("--head-probe", action="store_true",
@@ -276,7 +292,7 @@ def main():
         head_probe(args.config)
         return
 
-    S = setup(args.config)
+    S = setup(args.config, args.streams)
     cfg, trie = S["cfg"], S["trie"]
     sec, kern = run_steps(S, args.steps, args.warmup)
     B = S["docs"].B
@@ -292,7 +308,8 @@ def main():
                                f"({trie.n_int} internal), d={cfg.d}, Hq/Hkv/hd={cfg.Hq}/{cfg.Hkv}/{cfg.hd}, "
                                f"V={cfg.V}",
                    "labels": trie.n_labels, "trie_nodes": trie.n_nodes, "global_batch": B,
-                   "seq_len": cfg.L, "parallelism": "none (1 GPU)"},
+                   "seq_len": cfg.L, "parallelism": "none (1 GPU)",
+                   "batches_in_flight": len(S["ws"])},
         "trie_nodes_per_s": round(B * trie.n_nodes / sec, 1),
         "trie_build_ms": round(S["trie_ms"], 3),
         "prepare_ms": round(S["prep_ms"], 3),
@@ -315,7 +332,7 @@ def main():
             continue
         del S
         torch.cuda.empty_cache()
-        S2 = setup(c)
+        S2 = setup(c, args.streams)
         s2, k2 = run_steps(S2, max(3, args.steps // 2), 2)
         f2, _ = head_flops(S2)
         tf = f2 / (k2["head"] * 1e-3) / 1e12

@@ -413,7 +413,9 @@ def classify_run_workspace_bytes(model: Model, trie_dev: TrieDevice, docs: Docs)
 def classify(model: Model, trie_dev: TrieDevice, docs: Docs, label=None, prob=None, ll=None,
              with_prob=True, ws=None, stream=None, prepared: Prepared = None):
     """The whole trie_tree pass (tcs_classify), or with `prepared` one batch on
-    per-label-set state (tcs_classify_run).  Returns (label [B], prob [B, M], ll [B, M])."""
+    per-label-set state (tcs_classify_run).  Returns (label [B], prob [B, M], ll [B, M]).
+    With `stream`, the work is queued on that torch stream; the results are ready once
+    it has finished.  Runs on different streams need their own `ws`."""
     torch = _torch()
     B, M = docs.B, trie_dev.trie.n_labels
     dev = docs.offsets.device
@@ -430,6 +432,12 @@ def classify(model: Model, trie_dev: TrieDevice, docs: Docs, label=None, prob=No
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _need_cuda(label, prob, ll, ws)
+    if stream is not None:
+        # the kernels use these on `stream`: keep the caching allocator from handing
+        # their memory to other work before that stream is done with it
+        for x in (label, prob, ll, ws):
+            if x is not None:
+                x.record_stream(stream)
     if prepared is None:
         _check(lib().tcs_classify(_stream(stream), C.byref(model.struct), C.byref(trie_dev.struct),
                                   C.byref(docs.struct), _ptr(label), _ptr(prob), _ptr(ll), _ptr(ws),
