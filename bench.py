@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
                     [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
-    python bench.py --head-probe --config 3  # head alone: workload-like vs constant operands
+    python bench.py --head-probe --config 3 [--power]  # head alone: workload-like vs constant
+                                                       # operands (+ socket power and clocks)
 
 One step is one ``tcs_classify_run`` call over one batch of synthetic documents
 (consecutive steps alternate over ``--streams`` HIP streams, default 2, each with its
@@ -36,6 +37,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -213,11 +215,30 @@ def cpu_baseline(S, budget_s=15.0):
                       f"(BLAS threads = visible cores), {dt:.1f}s"}
 
 
-def head_probe(cid: int, reps: int = 5):
+def smi_sample(stop, samples, period=0.3):
+    """Append (socket power W, mean GFX clock MHz) read by `amd-smi metric` (a child
+    process) until `stop` is set."""
+    import subprocess
+    while not stop.is_set():
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], capture_output=True,
+                               text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired):
+            return
+        pw = re.findall(r"SOCKET_POWER: (\d+) W", r.stdout)
+        clk = [float(x) for x in re.findall(r"GFX_\d+:\s+CLK: (\d+) MHz", r.stdout)]
+        if pw and clk:
+            samples.append((float(pw[0]), sum(clk) / len(clk)))
+        stop.wait(period)
+
+
+def head_probe(cid: int, reps: int = 5, power: bool = False):
     """The output head alone (tcs_lmhead_lse_gather) at a workload's shape, on operands
     drawn like the workload's (unit-RMS rows h, W ~ N(0, 0.02), bf16) and on constant
     operands of the same shape: the gap between the two is the part of the head's
-    time that depends on the operand values (matrix-core power), not on the schedule."""
+    time that depends on the operand values (matrix-core power), not on the schedule.
+    With `power`, the head then runs back to back for ~4 s per operand kind while
+    amd-smi samples the socket power and the GFX clocks."""
     import torch
     import trie_constrained_scoring_amd as tcs
     from synth import config, make_inputs
@@ -249,6 +270,22 @@ def head_probe(cid: int, reps: int = 5):
         tf = 2.0 * R * cfg.d * cfg.V / (ms * 1e-3) / 1e12
         out[kind] = {"ms_per_launch": round(ms, 4), "tflops": round(tf, 1),
                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if power:
+            import threading
+            n_launch = max(20, int(4.0 / (ms * 1e-3)))
+            samples, stop = [], threading.Event()
+            for _ in range(n_launch):
+                tcs.lmhead_lse_gather(h, W, td, B, ws=ws)
+            time.sleep(0.5)  # past the ramp
+            th = threading.Thread(target=smi_sample, args=(stop, samples))
+            th.start()
+            torch.cuda.synchronize()
+            stop.set()
+            th.join()
+            if samples:
+                out[kind]["socket_power_w"] = round(statistics.mean(p for p, _ in samples), 1)
+                out[kind]["gfx_clock_mhz"] = round(statistics.mean(c for _, c in samples), 1)
+                out[kind]["power_samples"] = len(samples)
         del h, W, ws
         torch.cuda.empty_cache()
     print(json.dumps({"head_probe": {"config": cid, "rows": R, "d": cfg.d, "V": cfg.V, **out}}),
@@ -270,6 +307,8 @@ def main():
                     help="only run a plain device copy of 1 GiB (3 launches) and exit")
     ap.add_argument("--head-probe", action="store_true",
                     help="only time the output head alone on workload-like vs constant operands")
+    ap.add_argument("--power", action="store_true",
+                    help="with --head-probe: also sample socket power and GFX clocks (amd-smi)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); documents shard across GPUs "
@@ -289,7 +328,7 @@ def main():
         return
 
     if args.head_probe:
-        head_probe(args.config)
+        head_probe(args.config, power=args.power)
         return
 
     S = setup(args.config, args.streams)
