@@ -390,6 +390,27 @@ __global__ __launch_bounds__(256) void doc_attn_mfma_kernel(
 // The four waves' key slices and the row's path partial are merged by log-sum-exp
 // in the epilogue.
 
+// Online-softmax update of a wave's rows for a new block of keys whose scaled
+// row maximum (base 2) is `smax`.  The running maximum m is raised only when some
+// row of the wave would exceed it by more than 8 (a factor 256): the block's
+// weights exp2(s - m) then stay at most 256, which fp32 sums and the bf16
+// high/low split of the weights carry without loss, and the accumulators are
+// rescaled a few times per document instead of at every block.  Every quantity
+// is relative to the same m, so the normalised result does not depend on when m
+// was raised.  m = -inf before the first block (which always raises it).
+template <int NB>
+__device__ __forceinline__ void lazy_rescale(float& m, float smax, float& lsum, f32x16 (&acc)[NB]) {
+  if (__builtin_amdgcn_ballot_w64(smax > m + 8.f) == 0) return;  // wave-uniform
+  const float mn = fmaxf(m, smax);
+  const float cf = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf, 1 where m stays
+  m = mn;
+  lsum *= cf;
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] *= cf;
+}
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
@@ -532,28 +553,24 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + ko[ks]);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
     }
-    // online softmax (base 2); keys past the document end are masked
-    const int kb0 = t * KB + 4 * c;
+    // online softmax (base 2); only the document's last stage has keys past its
+    // end, which are masked (the empty asm keeps this a branch)
+    if (t * KB + KB > L) {
+      asm volatile("");
+      const int kb0 = t * KB + 4 * c;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kb0 + 8 * (e >> 2) + (e & 3) >= L) sc[e] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kb0 + 8 * (e >> 2) + (e & 3);
-      sc[e] = key < L ? sc[e] * qk : -INFINITY;
-      tmax = fmaxf(tmax, sc[e]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);  // finite: every stage has a valid key
-    const float cf = exp2f(m - mn);
-    m = mn;
-    lsum *= cf;
-#pragma unroll
-    for (int i = 0; i < NBLK; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][e] *= cf;
+    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sc[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk;  // finite: every stage has a valid key
+    lazy_rescale(m, tmax, lsum, acc);
     float p[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      p[e] = exp2f(sc[e] - mn);
+      p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], qk, -m));
       lsum += p[e];
     }
     // P^T fragments: step st takes keys {16 st + 4c + 0..3, 16 st + 8 + 4c + 0..3}
@@ -1101,31 +1118,32 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
         }
       }
-      // online softmax (base 2) over the 64 keys; keys past the document end are masked
+      // online softmax (base 2) over the 64 keys; only a document's last stage has
+      // keys past its end, which are masked (the empty asm keeps this a branch
+      // rather than selects on every stage)
+      if (L - t * KT < KT) {
+        asm volatile("");
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = t * KT + kb * 32 + 8 * (e >> 2) + 4 * c + (e & 3);
+            sc[kb][e] = key < L ? sc[kb][e] : -INFINITY;
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = t * KT + kb * 32 + 8 * (e >> 2) + 4 * c + (e & 3);
-          sc[kb][e] = key < L ? sc[kb][e] * qk : -INFINITY;
-          tmax = fmaxf(tmax, sc[kb][e]);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m, tmax);  // finite: every stage has a valid key
-      const float cf = exp2f(m - mn);
-      m = mn;
-      lsum *= cf;
-#pragma unroll
-      for (int i = 0; i < NBLK; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][e] *= cf;
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sc[kb][e]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk;  // finite: every stage has a valid key
+      lazy_rescale(m, tmax, lsum, acc);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float p[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          p[e] = exp2f(sc[kb][e] - mn);
+          p[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], qk, -m));
           lsum += p[e];
         }
         bf16x8 ph[2], pl[2];
