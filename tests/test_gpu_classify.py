@@ -43,6 +43,11 @@ SMALL = {
     "prefix-bf16-small": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=64, B=5, L=40,
                                 trie=("explicit", [[3], [3, 4], [3, 4, 5], [3, 6], [9, 9, 9], [9, 9], [1]])),
     "fp8-small": config(5, V=2500, d=192, Hq=4, Hkv=1, B=4, L=300),
+    # one label (probability 1, always chosen); a 40-token chain beside short labels
+    "single-label-bf16": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=64, B=3, L=20,
+                                trie=("explicit", [[4, 2, 7]])),
+    "deep-chain-bf16": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=128, B=3, L=30,
+                              trie=("explicit", [list(range(100, 140)), [5], [100, 101, 7]])),
     # few-row output projection on the K-split kernel: ragged row and column tiles,
     # 128- and 256-row tiles, even and uneven K splits (R = B x 8 internal nodes)
     "proj-split-bm128": config(2, V=2000, d=320, Hq=4, Hkv=2, hd=128, B=25, L=24),
