@@ -20,7 +20,9 @@ separately: the trie, built on the host (``trie_build_ms``), and
 
 Prints ONE JSON line.  ``value`` is documents classified per second at the
 primary workload (default: the running-example shape, 10 labels); the 255- and
-5000-label workloads are reported under ``at_labels``.  ``roofline`` is for the
+5000-label workloads are reported under ``at_labels``, and ``path_roofline`` times the
+path-sum kernel alone on 4096 documents of the 5000-label trie (enough bytes to hold
+it against HBM).  ``roofline`` is for the
 dominant kernel (the output head): after the timed steps, the same steps run
 again with the head launches bracketed by HIP events on the stream they run on
 (the library's tcs_timing_enable hook), and achieved = algorithmic FLOP per
@@ -215,6 +217,43 @@ def cpu_baseline(S, budget_s=15.0):
                       f"(BLAS threads = visible cores), {dt:.1f}s"}
 
 
+def path_stress(cid: int = 4, B: int = 4096, reps: int = 10):
+    """tcs_path_sum_softmax alone on many documents of one label set (the 5,000-label
+    trie by default), so that the path kernel streams enough bytes to be measured
+    against HBM: it reads lp [B, n_nodes] once and writes ll and prob [B, M] and
+    label [B].  lp holds edge log-probs drawn in [-12, -2] (the root's is 0)."""
+    import torch
+    import trie_constrained_scoring_amd as tcs
+    from synth import config, make_inputs
+    cfg = config(cid)
+    inp = make_inputs(cfg, weights=False)
+    trie = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(trie)
+    N, M = trie.n_nodes, trie.n_labels
+    g = torch.Generator(device="cuda").manual_seed(cid)
+    lp = torch.rand(B, N, device="cuda", generator=g) * -10.0 - 2.0
+    lp[:, 0] = 0.0
+    ll = torch.empty(B, M, device="cuda")
+    prob = torch.empty(B, M, device="cuda")
+    label = torch.empty(B, dtype=torch.int32, device="cuda")
+    tcs.path_sum_softmax(lp, td, ll, prob, label)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tcs.path_sum_softmax(lp, td, ll, prob, label)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = B * (N * 4 + 2 * M * 4 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "path_sum_kernel",
+            "workload": f"{B} documents on the {M}-label trie of config {cid} ({N} nodes)",
+            "bytes_per_launch": nbytes, "ms_per_launch": round(ms, 4),
+            "timing": "torch.cuda.Event around 10 launches on the current stream"}
+
+
 def smi_sample(stop, samples, period=0.3):
     """Append (socket power W, mean GFX clock MHz) read by `amd-smi metric` (a child
     process) until `stop` is set."""
@@ -307,6 +346,10 @@ def main():
                     help="only run a plain device copy of 1 GiB (3 launches) and exit")
     ap.add_argument("--head-probe", action="store_true",
                     help="only time the output head alone on workload-like vs constant operands")
+    ap.add_argument("--path-stress", action="store_true",
+                    help="only time tcs_path_sum_softmax on 4096 documents of the 5000-label trie")
+    ap.add_argument("--no-path-stress", action="store_true",
+                    help="leave the path-sum stress measurement (path_roofline) out")
     ap.add_argument("--power", action="store_true",
                     help="with --head-probe: also sample socket power and GFX clocks (amd-smi)")
     args = ap.parse_args()
@@ -329,6 +372,9 @@ def main():
 
     if args.head_probe:
         head_probe(args.config, power=args.power)
+        return
+    if args.path_stress:
+        print(json.dumps({"path_roofline": path_stress()}), flush=True)
         return
 
     S = setup(args.config, args.streams)
@@ -387,6 +433,11 @@ def main():
         S = S2
     if extra:
         res["at_labels"] = extra
+    if not args.no_path_stress:
+        del S
+        torch.cuda.empty_cache()
+        res["path_roofline"] = path_stress()
+        S = None
     if not args.no_cpu_baseline:
         del S
         torch.cuda.empty_cache()

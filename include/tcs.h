@@ -99,6 +99,10 @@ typedef struct {
   int32_t* e_tok;
   int32_t* e_qrow;       /* query row of the edge's parent */
   int32_t* e_child;      /* node id of the edge's child */
+  /* optional (may be NULL): derived arrays for the level-by-level path sums */
+  int32_t* row_level_offsets; /* [cap_levels] first query row of each depth, then n_int */
+  int32_t* label_row;    /* [M] row whose prefix sum a label's score starts from: its
+                            node's row if the node is internal, else its parent's */
 } tcs_trie;
 
 /*
@@ -124,6 +128,10 @@ typedef struct {
   const int32_t* e_tok;        /* [n_nodes-1] sorted */
   const int32_t* e_qrow;       /* [n_nodes-1] */
   const int32_t* e_child;      /* [n_nodes-1] */
+  /* optional (NULL: the path sums walk each label's path instead) */
+  const int32_t* qrow;               /* [n_nodes] */
+  const int32_t* row_level_offsets;  /* [max_depth + 2] */
+  const int32_t* label_row;          /* [n_labels] */
 } tcs_trie_dev;
 
 /* --------------------------------------------------------- tree attention ---- */
@@ -190,9 +198,13 @@ int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtyp
  * Per-label log score, label softmax and argmax (section 3.2).
  *   ll[b, m]  = sum of lp[b, .] over the path root -> label_node[m], plus
  *               log(1 - sum_{children c} exp(lp[b, c])) when label_node[m] has
- *               children (accumulated in fp64; -inf if the children take all mass)
+ *               children (-inf if the children take all mass).  Path sums are
+ *               carried in fp64, or as a pair of fp32 values (about 2^-33 relative
+ *               error per step) when the trie arrays for level-by-level sums are
+ *               given; the prefix term in fp64.
  *   prob[b,.] = softmax over m of ll[b, .]            (optional: prob may be NULL)
- *   label[b]  = argmax_m ll[b, m], lowest label id among equal maxima
+ *   label[b]  = argmax_m ll[b, m] of the returned (fp32) ll, lowest label id among
+ *               equal maxima
  * lp is [B, n_nodes] fp32 with lp[b, 0] = 0; ll and prob are [B, M] fp32.
  */
 int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie, const float* lp,

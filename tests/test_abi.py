@@ -39,6 +39,14 @@ def assert_same_trie(t, o):
     assert (t.n_nodes, t.n_int, t.n_labels, t.max_depth) == (o.n_nodes, o.n_int, o.n_labels, o.max_depth)
     for n in ARRAYS:
         np.testing.assert_array_equal(t.arrays[n], getattr(o, n), err_msg=n)
+    # derived arrays for the level-by-level path sums, from their definitions:
+    # rows at depth < d, and the row a label's score starts from
+    row_depth = o.depth[o.qnode]
+    np.testing.assert_array_equal(
+        t.arrays["row_level_offsets"], [int(np.sum(row_depth < d)) for d in range(o.max_depth + 2)])
+    u = o.label_node
+    np.testing.assert_array_equal(
+        t.arrays["label_row"], np.where(o.child_count[u] > 0, o.qrow[u], o.qrow[o.parent[u]]))
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])

@@ -84,6 +84,23 @@ def test_path_sum_vs_oracle(dev, case, with_prob):
     check_labels(ll, prob, label, o_ll, o_p, o_lab, f"path_sum[{case}]")
 
 
+@pytest.mark.parametrize("cid,B", [(4, 300), (3, 600)])
+def test_path_sum_many_docs_per_workgroup(dev, cid, B):
+    """More documents than workgroups (the 5000-label trie takes one 1024-thread
+    workgroup per CU, the 255-label trie two), so workgroups score several
+    documents in turn, each loaded while the previous one is scored."""
+    inp = make_inputs(config(cid), weights=False)
+    labels, root, V = inp["labels"], inp["root_token"], config(cid).V
+    trie = O.build_trie(labels, root, V)
+    lp = _proper_lp(trie, B, np.random.default_rng(cid))
+    ll, prob, label = _run_path_sum(labels, root, V, lp)
+    o_ll = O.path_log_likelihoods(trie, lp.astype(np.float64))
+    o_p, o_lab = O.label_softmax(o_ll)
+    assert np.abs(ll - o_ll).max() < 1e-4
+    assert np.abs(prob - o_p).max() < 1e-5
+    check_labels(ll, prob, label, o_ll, o_p, o_lab, f"path_sum[config {cid}, B={B}]")
+
+
 def test_path_sum_ties_take_lowest_label(dev):
     labels = [[1], [2], [3], [4]]
     trie = O.build_trie(labels, 0, 8)

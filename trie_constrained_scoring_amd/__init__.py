@@ -40,11 +40,12 @@ class tcs_trie(C.Structure):
                 ("n_nodes", C.c_int32), ("n_int", C.c_int32), ("n_labels", C.c_int32),
                 ("max_depth", C.c_int32)] + [(n, P32) for n in (
                     "parent", "token", "depth", "child_begin", "child_count", "node_label", "qrow",
-                    "qnode", "qparent", "label_node", "level_offsets", "e_tok", "e_qrow", "e_child")]
+                    "qnode", "qparent", "label_node", "level_offsets", "e_tok", "e_qrow", "e_child",
+                    "row_level_offsets", "label_row")]
 
 
 TRIE_DEV_ARRAYS = ("parent", "token", "child_begin", "child_count", "qnode", "qparent", "label_node",
-                   "e_tok", "e_qrow", "e_child")
+                   "e_tok", "e_qrow", "e_child", "qrow", "row_level_offsets", "label_row")
 
 
 class tcs_trie_dev(C.Structure):
@@ -219,7 +220,9 @@ def trie_build(label_offsets, label_tokens, root_token: int, V: int) -> Trie:
             "parent", "token", "depth", "child_begin", "child_count", "node_label", "qrow", "qnode",
             "qparent", "e_tok", "e_qrow", "e_child")}
         arrays["label_node"] = np.zeros(max(M, 1), dtype=np.int32)
+        arrays["label_row"] = np.zeros(max(M, 1), dtype=np.int32)
         arrays["level_offsets"] = np.zeros(cap + 1, dtype=np.int32)
+        arrays["row_level_offsets"] = np.zeros(cap + 1, dtype=np.int32)
         t = tcs_trie(cap_nodes=cap, cap_levels=cap + 1)
         for n, a in arrays.items():
             setattr(t, n, a.ctypes.data_as(P32))
@@ -231,7 +234,7 @@ def trie_build(label_offsets, label_tokens, root_token: int, V: int) -> Trie:
         _check(rc)
         N, n_int, D = t.n_nodes, t.n_int, t.max_depth
         cut = {"qnode": n_int, "qparent": n_int, "e_tok": N - 1, "e_qrow": N - 1, "e_child": N - 1,
-               "label_node": M, "level_offsets": D + 2}
+               "label_node": M, "label_row": M, "level_offsets": D + 2, "row_level_offsets": D + 2}
         out = {n: a[:cut.get(n, N)].copy() for n, a in arrays.items()}
         return Trie(N, n_int, M, D, out)
     raise TcsError(TCS_ECAPACITY, "trie capacity")

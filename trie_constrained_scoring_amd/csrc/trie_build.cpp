@@ -164,5 +164,18 @@ extern "C" int tcs_trie_build(const int32_t* label_offsets, const int32_t* label
     out->e_qrow[i] = out->qrow[out->parent[c]];
     out->e_child[i] = c;
   }
+  // rows follow node order, so the rows of one depth are contiguous
+  if (out->row_level_offsets) {
+    for (int32_t dd = 0, r = 0; dd <= D + 1; ++dd) {
+      while (r < n_int && depth_c[out->qnode[r]] < dd) ++r;
+      out->row_level_offsets[dd] = r;
+    }
+  }
+  if (out->label_row) {
+    for (int32_t m = 0; m < M; ++m) {
+      const int32_t u = out->label_node[m];
+      out->label_row[m] = out->child_count[u] > 0 ? out->qrow[u] : out->qrow[out->parent[u]];
+    }
+  }
   return TCS_OK;
 }
