@@ -460,9 +460,11 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   const int G = Hq / Hkv;
   const int rows_total = n_int * G;
   const int n_rb = (rows_total + 31) / 32;
-  const int rb = blockIdx.x % n_rb;
-  const int g = (blockIdx.x / n_rb) % Hkv;
-  const int b = blockIdx.x / (n_rb * Hkv);
+  // block i -> document i mod B: block i runs on XCD i mod 8, so each XCD reads whole
+  // key rows (all KV heads) of its documents
+  const int Bn = int(gridDim.x) / (n_rb * Hkv);
+  const int b = blockIdx.x % Bn, rest = blockIdx.x / Bn;
+  const int rb = rest % n_rb, g = rest / n_rb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = rb * 32;
