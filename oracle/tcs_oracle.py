@@ -33,7 +33,12 @@ reason in the design notes):
       and the final hidden state h.  The residual sum y is not rounded;
   R7  the fp8 head holds E4M3FN codes with one fp32 scale per vocabulary row; the
       scale multiplies the dot product;
-  R8  argmax ties go to the lowest label id.
+  R8  argmax ties go to the lowest label id;
+  R9  decision-word form ([CT] 3.2): a word is a token plus the tokens after it that
+      carry a word-continuation flag (a per-vocabulary input); a label "leaves all
+      others" at its first token k such that no other label starts with its first
+      k tokens; a label that never does (it is the start of another label) is
+      scored over all its tokens, with the prefix rule of R3.
 
 Parity status: every function below is pinned by the non-GPU oracle tests
 (library routines, closed forms, the worked example, brute-force scoring).
@@ -50,6 +55,7 @@ __all__ = [
     "node_layer", "doc_kv_from_tokens", "tree_attention", "hidden_states",
     "lm_head_lse", "head_logits_at", "edge_logprobs", "log1mexp", "path_log_likelihoods",
     "label_softmax", "classify", "bruteforce_ll", "label_ll_on_paths",
+    "decision_depths", "truncate_labels",
 ]
 
 TCS_OK = 0
@@ -413,7 +419,8 @@ def classify(inp: dict, docs=None, model: OracleModel | None = None, trie: Trie 
                 ll=ll, prob=prob, label=label, docs=docs)
 
 
-def bruteforce_ll(inp: dict, doc: int, label_ids=None, model: OracleModel | None = None):
+def bruteforce_ll(inp: dict, doc: int, label_ids=None, model: OracleModel | None = None,
+                  upto=None):
     """Score labels one at a time by running the whole sequence causally.
 
     The direct definition of [CT] 3.2: P(m) = prod_k P(x_k | prompt, x_<k).  For
@@ -422,6 +429,10 @@ def bruteforce_ll(inp: dict, doc: int, label_ids=None, model: OracleModel | None
     log P(t_{j+1}) = logit_j[t_{j+1}] - logsumexp(logit_j).  When other labels
     continue label m, the log-probability of not taking any of their next tokens
     is added ([CT] 3.2 prefix rule).  No trie is built.
+
+    `upto` [M] (optional) scores only the first upto[m] tokens of label m: the
+    decision-word score of [CT] 3.2 with upto = decision_depths(...).  The prefix
+    rule is applied only when the whole label is scored.
     """
     model = model or OracleModel(inp)
     labels = [list(map(int, l)) for l in inp["labels"]]
@@ -438,7 +449,8 @@ def bruteforce_ll(inp: dict, doc: int, label_ids=None, model: OracleModel | None
     label_ids = range(len(labels)) if label_ids is None else label_ids
     out = []
     for m in label_ids:
-        seq = [root] + labels[m]
+        k_m = len(labels[m]) if upto is None else int(upto[m])
+        seq = [root] + labels[m][:k_m]
         n = len(seq)
         x, q, k, v = node_layer(model, seq)
         keys = np.concatenate([Kb, k], axis=0)            # [L + n, Hkv, hd]
@@ -461,8 +473,9 @@ def bruteforce_ll(inp: dict, doc: int, label_ids=None, model: OracleModel | None
         mx = z.max(axis=1)
         lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
         ll = sum(z[j, seq[j + 1]] - lse[j] for j in range(n - 1))
-        cont = sorted({l[len(labels[m])] for l in labels
-                       if len(l) > len(labels[m]) and l[:len(labels[m])] == labels[m]})
+        cont = [] if k_m < len(labels[m]) else \
+            sorted({l[len(labels[m])] for l in labels
+                    if len(l) > len(labels[m]) and l[:len(labels[m])] == labels[m]})
         if cont:
             pstop = 1.0 - np.exp(z[n - 1, cont] - lse[n - 1]).sum()
             ll += np.log(pstop) if pstop > 0 else -np.inf
@@ -528,3 +541,42 @@ def label_ll_on_paths(inp: dict, doc: int, label_ids, model: OracleModel | None 
     with np.errstate(all="ignore"):
         ll = path_log_likelihoods(trie, lp)[0]
     return ll[list(label_ids)], dict(rows=rows, lse=lse, h=h)
+
+
+# =========================================================================== decision words ([CT] 3.2)
+
+def decision_depths(labels, word_cont):
+    """d_m for every label: the number of its tokens the decision-word form scores.
+
+    [CT] 3.2: a label is scored up to the last token of the word in which it leaves
+    every other label.  Count, for every token prefix, how many labels start with
+    it.  Label m leaves the others at the first k whose prefix of length k is
+    counted once (only m has it).  The word holding token k runs on while the
+    next token carries the continuation flag (word_cont[t] != 0), so d_m is k
+    plus that run.  When no prefix of m is its own (m is the start of another
+    label), d_m is the whole length (reading R9).  Duplicate labels are an error.
+    """
+    labels = [list(map(int, l)) for l in labels]
+    if len({tuple(l) for l in labels}) != len(labels):
+        raise TrieError(TCS_EDUPLICATE, "two labels are equal")
+    count: dict = {}
+    for lab in labels:
+        for k in range(1, len(lab) + 1):
+            count[tuple(lab[:k])] = count.get(tuple(lab[:k]), 0) + 1
+    out = np.zeros(len(labels), dtype=np.int64)
+    for m, lab in enumerate(labels):
+        n = len(lab)
+        k = n
+        for j in range(1, n + 1):
+            if count[tuple(lab[:j])] == 1:
+                k = j
+                break
+        while k < n and word_cont[lab[k]]:
+            k += 1
+        out[m] = k
+    return out
+
+
+def truncate_labels(labels, depths):
+    """Label m cut to its first depths[m] tokens."""
+    return [list(map(int, l[:int(d)])) for l, d in zip(labels, depths)]

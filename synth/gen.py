@@ -15,7 +15,9 @@ Storage formats produced here:
     vocabulary row, ``s_v = max|W_v| / 448``, codes rounded to nearest-even and
     saturated at +-448.
 
-Random sub-streams, in spawn order: trie, root token, E, Wq, Wk, Wv, Wo, W, doc.
+Random sub-streams, in spawn order: trie, root token, E, Wq, Wk, Wv, Wo, W, doc,
+word (the word-continuation flags; spawned last so the earlier streams are the
+same with or without it).
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-STREAMS = ("trie", "root", "E", "Wq", "Wk", "Wv", "Wo", "W", "doc")
+STREAMS = ("trie", "root", "E", "Wq", "Wk", "Wv", "Wo", "W", "doc", "word")
 
 
 @dataclass(frozen=True)
@@ -91,11 +93,34 @@ _RUNNING_SHAPE = [
     [15],              # praise
     [16],              # other
 ]
+# "-factor" carries no leading space: it continues the word "two".
+_RUNNING_CONTINUATION = {12}
+
+# Share of vocabulary tokens that continue the previous token's word (no leading
+# space) in the synthetic tokenizer.
+WORD_CONT_P = 0.25
 
 
 def running_example_labels(rng: np.random.Generator, V: int):
     ids = rng.choice(V, size=17, replace=False)
     return [[int(ids[s]) for s in lab] for lab in _RUNNING_SHAPE]
+
+
+def word_continuation_flags(cfg: "Config", labels, rng: np.random.Generator):
+    """uint8 [V]: 1 where a vocabulary token continues the previous token's word.
+
+    Words decide how far a label is scored in the decision-word form of trie_tree
+    ("To Classify, Try a Trie Tree", section 3.2: up to the end of the word where
+    the label leaves all others).  Each token is a continuation with probability
+    WORD_CONT_P; in the running example the label tokens are set by hand so that
+    only "-factor" continues a word.
+    """
+    flags = (rng.random(cfg.V) < WORD_CONT_P).astype(np.uint8)
+    if cfg.trie[0] == "running":
+        for lab, shape in zip(labels, _RUNNING_SHAPE):
+            for t, sym in zip(lab, shape):
+                flags[t] = 1 if sym in _RUNNING_CONTINUATION else 0
+    return flags
 
 
 def zipf_copy_prefix_labels(rng: np.random.Generator, V: int, M: int, lo: int, hi: int, s: float):
@@ -233,7 +258,8 @@ def _fp8_head(rng, V, d, std, chunk_rows=8192):
 def make_inputs(cfg: Config, seed: int | None = None, *, weights: bool = True):
     """Draw one workload.  Returns a dict of numpy arrays plus the label lists.
 
-    Keys: labels (list of lists), label_offsets, label_tokens, root_token, E, Wq, Wk,
+    Keys: labels (list of lists), label_offsets, label_tokens, root_token, word_cont
+    (uint8 [V] word-continuation flags), E, Wq, Wk,
     Wv, Wo, W, W_scale (fp8 head only, else None), doc_offsets, and either Kd/Vd
     ([sum L, Hkv, hd]) or doc_tokens ([sum L]).
     """
@@ -245,6 +271,7 @@ def make_inputs(cfg: Config, seed: int | None = None, *, weights: bool = True):
     out["labels"] = labels
     out["label_offsets"], out["label_tokens"] = labels_to_csr(labels)
     out["root_token"] = int(rngs["root"].integers(0, cfg.V))
+    out["word_cont"] = word_continuation_flags(cfg, labels, rngs["word"])
     d, Hq, Hkv, hd, V = cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, cfg.V
     if weights:
         out["E"] = _weight(rngs["E"], (V, d), cfg.std, cfg.dtype)
