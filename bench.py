@@ -1,7 +1,7 @@
 """Throughput of the trie_tree label-scoring pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-path-stress] [--no-decision-word]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
     python bench.py --head-probe --config 3 [--power]  # head alone: workload-like vs constant
                                                        # operands (+ socket power and clocks)
@@ -22,7 +22,10 @@ Prints ONE JSON line.  ``value`` is documents classified per second at the
 primary workload (default: the running-example shape, 10 labels); the 255- and
 5000-label workloads are reported under ``at_labels``, and ``path_roofline`` times the
 path-sum kernel alone on 4096 documents of the 5000-label trie (enough bytes to hold
-it against HBM).  ``roofline`` is for the
+it against HBM).  ``decision_word`` runs the same documents and weights with every
+label cut to the end of the word where it leaves the others (the decision-word form
+of trie_tree: fewer query rows, same kernels); the headline scores every label over
+its full root-to-leaf path.  ``roofline`` is for the
 dominant kernel (the output head): after the timed steps, the same steps run
 again with the head launches bracketed by HIP events on the stream they run on
 (the library's tcs_timing_enable hook), and achieved = algorithmic FLOP per
@@ -102,8 +105,16 @@ def setup(cid: int, streams: int = 1):
     prep = tcs.Prepared(model, td, docs.B)
     torch.cuda.synchronize()
     prep_ms = (time.perf_counter() - t0) * 1e3
-    B, M = docs.B, trie.n_labels
-    # one run workspace and output set per batch in flight
+    ws, out = run_buffers(model, td, docs, streams)
+    return dict(cfg=cfg, inp=inp, trie=trie, td=td, model=model, docs=docs, ws=ws, out=out,
+                trie_ms=trie_ms, prep=prep, prep_ms=prep_ms)
+
+
+def run_buffers(model, td, docs, streams):
+    """One run workspace and output set per batch in flight."""
+    import torch
+    import trie_constrained_scoring_amd as tcs
+    B, M = docs.B, td.trie.n_labels
     ws, out = [], []
     for _ in range(max(1, streams)):
         ws.append(torch.empty(tcs.classify_run_workspace_bytes(model, td, docs), dtype=torch.uint8,
@@ -112,8 +123,37 @@ def setup(cid: int, streams: int = 1):
                         prob=torch.empty((B, M), dtype=torch.float32, device="cuda"),
                         ll=torch.empty((B, M), dtype=torch.float32, device="cuda")))
     torch.cuda.synchronize()
-    return dict(cfg=cfg, inp=inp, trie=trie, td=td, model=model, docs=docs, ws=ws, out=out,
-                trie_ms=trie_ms, prep=prep, prep_ms=prep_ms)
+    return ws, out
+
+
+def decision_word(S, steps, warmup, streams):
+    """The same documents and weights scored in the decision-word form: every label
+    cut to the end of the word where it leaves the others (tcs_decision_truncate),
+    then the unchanged classify pass on the cut trie."""
+    import torch
+    import trie_constrained_scoring_amd as tcs
+    cfg, inp = S["cfg"], S["inp"]
+    t0 = time.perf_counter()
+    offs, toks, _ = tcs.decision_truncate(inp["label_offsets"], inp["label_tokens"], cfg.V,
+                                          inp["word_cont"])
+    trie = tcs.trie_build(offs, toks, inp["root_token"], cfg.V)
+    cut_ms = (time.perf_counter() - t0) * 1e3
+    td = tcs.TrieDevice(trie)
+    prep = tcs.Prepared(S["model"], td, S["docs"].B)
+    ws, out = run_buffers(S["model"], td, S["docs"], streams)
+    C = dict(S, trie=trie, td=td, prep=prep, ws=ws, out=out)
+    sec, kern = run_steps(C, steps, warmup)
+    f, R = head_flops(C)
+    tf = f / (kern["head"] * 1e-3) / 1e12
+    B = S["docs"].B
+    e = {"config": cfg.id, "docs_per_s": round(B / sec, 2), "ms_per_step": round(sec * 1e3, 4),
+         "query_rows": trie.n_int, "query_rows_full_labels": S["trie"].n_int,
+         "trie_nodes": trie.n_nodes, "cut_and_build_ms": round(cut_ms, 3),
+         "head_tflops": round(tf, 2), "head_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+         "head_ms": round(kern["head"], 4)}
+    del C, prep, ws, out, td
+    torch.cuda.empty_cache()
+    return e
 
 
 def run_steps(S, steps, warmup):
@@ -350,6 +390,8 @@ def main():
                     help="only time tcs_path_sum_softmax on 4096 documents of the 5000-label trie")
     ap.add_argument("--no-path-stress", action="store_true",
                     help="leave the path-sum stress measurement (path_roofline) out")
+    ap.add_argument("--no-decision-word", action="store_true",
+                    help="leave the decision-word measurements (labels cut to their deciding word) out")
     ap.add_argument("--power", action="store_true",
                     help="with --head-probe: also sample socket power and GFX clocks (amd-smi)")
     args = ap.parse_args()
@@ -411,6 +453,9 @@ def main():
     res["head_share_of_step"] = round(kern["head"] / (sec * 1e3), 4)
     if kern["doc_attn"]:
         res["doc_attn_roofline"] = doc_attn_roofline(S, kern["doc_attn"])
+    decision = {}
+    if not args.no_decision_word:
+        decision[cfg.name] = decision_word(S, args.steps, args.warmup, args.streams)
     extra = {}
     for c in [int(x) for x in args.extra.split(",") if x.strip()]:
         if c == args.config:
@@ -430,9 +475,13 @@ def main():
             e["doc_attn_ms"] = round(k2["doc_attn"], 4)
             e["doc_attn_roofline"] = doc_attn_roofline(S2, k2["doc_attn"])
         extra[str(S2["trie"].n_labels)] = e
+        if not args.no_decision_word:
+            decision[S2["cfg"].name] = decision_word(S2, max(3, args.steps // 2), 2, args.streams)
         S = S2
     if extra:
         res["at_labels"] = extra
+    if decision:
+        res["decision_word"] = decision
     if not args.no_path_stress:
         del S
         torch.cuda.empty_cache()

@@ -115,6 +115,33 @@ typedef struct {
 int tcs_trie_build(const int32_t* label_offsets, const int32_t* label_tokens, int32_t M,
                    int32_t root_token, int32_t V, tcs_trie* out);
 
+/*
+ * Decision-word cut of a label set ("To Classify, Try a Trie Tree", section 3.2):
+ * trie_tree scores a label only up to the end of the word in which it leaves every
+ * other label.  For label m, k is the first position whose token prefix (tokens
+ * 1..k) no other label shares; the word holding token k goes on while the next
+ * token is a word continuation (word_cont[token] != 0), and d_m is the position of
+ * its last token.  A label that shares all its prefixes -- it is the start of
+ * another label -- keeps every token (d_m = its length) and is scored with the
+ * prefix rule.  Label m of the output is label m cut to its first d_m tokens.
+ *
+ * Running tcs_trie_build and tcs_classify on the cut labels gives exactly the
+ * decision-word scores: the cut labels are distinct, and one is the start of
+ * another only where the labels were, with the same next tokens, so the prefix
+ * rule is unchanged.  Label ids keep their order.
+ *
+ * label_offsets [M+1], label_tokens [label_offsets[M]]: labels as for
+ * tcs_trie_build.  word_cont [V]: one byte per vocabulary token, nonzero for a
+ * token that continues the previous token's word.  out_offsets [M+1] and
+ * out_tokens [label_offsets[M]] (never more than that is written) receive the cut
+ * labels as CSR; depth [M] (may be NULL) receives d_m.  All host memory, caller
+ * owned.  Errors: TCS_EINVAL (a null pointer, M < 1, an empty label, a token
+ * outside [0,V)), TCS_EDUPLICATE (two equal labels).  Host only; no GPU needed.
+ */
+int tcs_decision_truncate(const int32_t* label_offsets, const int32_t* label_tokens, int32_t M,
+                          int32_t V, const uint8_t* word_cont, int32_t* out_offsets,
+                          int32_t* out_tokens, int32_t* depth);
+
 /* Device copy of the trie arrays needed by the kernels (all device pointers). */
 typedef struct {
   int32_t n_nodes, n_int, n_labels, max_depth;

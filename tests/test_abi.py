@@ -127,3 +127,67 @@ def test_timing_api_without_launches():
     lib = tcs.lib()
     assert lib.tcs_timing_read(0, None, None) == tcs.TCS_EINVAL
     tcs.timing_enable(False)
+
+
+# ------------------------------------------------------------ decision-word cut
+
+def assert_same_cut(labels, flags, V):
+    offs, toks = labels_to_csr(labels)
+    c_offs, c_toks, c_depth = tcs.decision_truncate(offs, toks, V, flags)
+    d = O.decision_depths(labels, flags)
+    np.testing.assert_array_equal(c_depth, d)
+    cut_o, cut_t = labels_to_csr(O.truncate_labels(labels, d))
+    np.testing.assert_array_equal(c_offs, cut_o)
+    np.testing.assert_array_equal(c_toks, cut_t)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_decision_truncate_matches_oracle_on_configs(cid):
+    inp = make_inputs(config(cid), weights=False)
+    assert_same_cut(inp["labels"], inp["word_cont"], config(cid).V)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.lists(st.integers(0, 6), min_size=1, max_size=7), min_size=1, max_size=30),
+       st.lists(st.integers(0, 1), min_size=10, max_size=10))
+def test_decision_truncate_matches_oracle_random(raw, flags):
+    V = 10
+    flags = np.array(flags, dtype=np.uint8)
+    try:
+        O.decision_depths(raw, flags)
+    except O.TrieError as e:
+        offs, toks = labels_to_csr(raw)
+        with pytest.raises(tcs.TcsError) as ei:
+            tcs.decision_truncate(offs, toks, V, flags)
+        assert ei.value.code == e.code
+        return
+    assert_same_cut(raw, flags, V)
+
+
+def test_decision_truncate_errors():
+    lib = tcs.lib()
+    z = np.zeros(10, np.uint8)
+
+    def code(labels, offs=None, toks=None, V=10):
+        if offs is None:
+            offs, toks = labels_to_csr(labels)
+        with pytest.raises(tcs.TcsError) as e:
+            tcs.decision_truncate(offs, toks, V, np.zeros(V, np.uint8))
+        return e.value.code
+    assert code([[1, 2], [3], [1, 2]]) == tcs.TCS_EDUPLICATE
+    assert code([[1, 10]]) == tcs.TCS_EINVAL
+    assert code(None, offs=np.array([0, 1, 1], np.int32), toks=np.array([3], np.int32)) == tcs.TCS_EINVAL
+    assert code(None, offs=np.array([0], np.int32), toks=np.zeros(0, np.int32)) == tcs.TCS_EINVAL
+    offs, toks = labels_to_csr([[1, 2]])
+    out = np.zeros(3, np.int32)
+    P = lambda a: a.ctypes.data_as(tcs.P32)
+    assert lib.tcs_decision_truncate(P(offs), P(toks), 1, 10, None, P(out), P(out), None) == \
+        tcs.TCS_EINVAL
+    assert b"null" in lib.tcs_last_error()
+    flags = z.ctypes.data_as(C.POINTER(C.c_uint8))
+    assert lib.tcs_decision_truncate(P(offs), P(toks), 1, 10, flags, None, P(out), None) == \
+        tcs.TCS_EINVAL
+    # depth may be NULL
+    o2, t2 = np.zeros(2, np.int32), np.zeros(2, np.int32)
+    assert lib.tcs_decision_truncate(P(offs), P(toks), 1, 10, flags, P(o2), P(t2), None) == tcs.TCS_OK
+    assert list(o2) == [0, 1] and t2[0] == 1

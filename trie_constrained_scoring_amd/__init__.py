@@ -84,6 +84,8 @@ def lib():
         L.tcs_last_error.restype = C.c_char_p
         L.tcs_version.restype = C.c_char_p
         L.tcs_trie_build.argtypes = [P32, P32, i32, i32, i32, C.POINTER(tcs_trie)]
+        L.tcs_decision_truncate.argtypes = [P32, P32, i32, i32, C.POINTER(C.c_uint8), P32, P32,
+                                            P32]
         L.tcs_tree_attn_workspace_bytes.restype = sz
         L.tcs_tree_attn_workspace_bytes.argtypes = [i32, i32, i32]
         L.tcs_tree_attn.argtypes = [vp, C.c_int, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
@@ -238,6 +240,29 @@ def trie_build(label_offsets, label_tokens, root_token: int, V: int) -> Trie:
         out = {n: a[:cut.get(n, N)].copy() for n, a in arrays.items()}
         return Trie(N, n_int, M, D, out)
     raise TcsError(TCS_ECAPACITY, "trie capacity")
+
+
+def decision_truncate(label_offsets, label_tokens, V: int, word_cont):
+    """Decision-word cut of the labels (tcs_decision_truncate, host library call).
+
+    Returns (offsets [M+1], tokens, depth [M]) as numpy int32: label m cut to its
+    first depth[m] tokens.  Feed the result to trie_build to score labels in the
+    decision-word form."""
+    L = lib()
+    offs = np.ascontiguousarray(label_offsets, dtype=np.int32)
+    toks = np.ascontiguousarray(label_tokens, dtype=np.int32)
+    flags = np.ascontiguousarray(word_cont, dtype=np.uint8)
+    M = len(offs) - 1
+    if flags.shape != (V,):
+        raise TcsError(TCS_EINVAL, f"decision_truncate: word_cont has shape {flags.shape}, need ({V},)")
+    out_offs = np.zeros(max(M, 0) + 1, dtype=np.int32)
+    out_toks = np.zeros(max(len(toks), 1), dtype=np.int32)
+    depth = np.zeros(max(M, 1), dtype=np.int32)
+    _check(L.tcs_decision_truncate(offs.ctypes.data_as(P32), toks.ctypes.data_as(P32), M, V,
+                                   flags.ctypes.data_as(C.POINTER(C.c_uint8)),
+                                   out_offs.ctypes.data_as(P32), out_toks.ctypes.data_as(P32),
+                                   depth.ctypes.data_as(P32)))
+    return out_offs, out_toks[:out_offs[-1]].copy(), depth[:M].copy()
 
 
 class TrieDevice:

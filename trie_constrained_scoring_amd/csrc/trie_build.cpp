@@ -20,29 +20,44 @@ struct Edge {
   int32_t child;   // provisional id
 };
 
+// Shared argument checks of the label-set entry points (CSR labels over [0, V)).
+int check_labels(const char* fn, const int32_t* label_offsets, const int32_t* label_tokens,
+                 int32_t M, int32_t V) {
+  using tcs::fail;
+  if (!label_offsets) return fail(TCS_EINVAL, "%s: null label_offsets", fn);
+  if (M < 1) return fail(TCS_EINVAL, "%s: need at least one label (M=%d)", fn, M);
+  if (V < 1) return fail(TCS_EINVAL, "%s: vocabulary size %d", fn, V);
+  if (label_offsets[0] != 0) return fail(TCS_EINVAL, "%s: label_offsets[0] must be 0", fn);
+  for (int32_t m = 0; m < M; ++m) {
+    if (label_offsets[m + 1] <= label_offsets[m])
+      return fail(TCS_EINVAL, "%s: label %d is empty", fn, m);
+  }
+  const int64_t T = label_offsets[M];
+  if (T > 0 && !label_tokens) return fail(TCS_EINVAL, "%s: null label_tokens", fn);
+  for (int64_t i = 0; i < T; ++i) {
+    if (label_tokens[i] < 0 || label_tokens[i] >= V)
+      return fail(TCS_EINVAL, "%s: token %d at position %lld outside [0,%d)", fn,
+                  label_tokens[i], (long long)i, V);
+  }
+  return TCS_OK;
+}
+
+inline uint64_t edge_key(int32_t node, int32_t token) {
+  return (static_cast<uint64_t>(static_cast<uint32_t>(node)) << 32) |
+         static_cast<uint32_t>(token);
+}
+
 }  // namespace
 
 extern "C" int tcs_trie_build(const int32_t* label_offsets, const int32_t* label_tokens,
                               int32_t M, int32_t root_token, int32_t V, tcs_trie* out) {
   using tcs::fail;
   tcs::clear_error();
-  if (!label_offsets || !out) return fail(TCS_EINVAL, "trie_build: null pointer");
-  if (M < 1) return fail(TCS_EINVAL, "trie_build: need at least one label (M=%d)", M);
-  if (V < 1) return fail(TCS_EINVAL, "trie_build: vocabulary size %d", V);
+  if (!out) return fail(TCS_EINVAL, "trie_build: null pointer");
+  if (int rc = check_labels("trie_build", label_offsets, label_tokens, M, V)) return rc;
   if (root_token < 0 || root_token >= V)
     return fail(TCS_EINVAL, "trie_build: root token %d outside [0,%d)", root_token, V);
-  if (label_offsets[0] != 0) return fail(TCS_EINVAL, "trie_build: label_offsets[0] must be 0");
-  for (int32_t m = 0; m < M; ++m) {
-    if (label_offsets[m + 1] <= label_offsets[m])
-      return fail(TCS_EINVAL, "trie_build: label %d is empty", m);
-  }
   const int64_t T = label_offsets[M];
-  if (T > 0 && !label_tokens) return fail(TCS_EINVAL, "trie_build: null label_tokens");
-  for (int64_t i = 0; i < T; ++i) {
-    if (label_tokens[i] < 0 || label_tokens[i] >= V)
-      return fail(TCS_EINVAL, "trie_build: token %d at position %lld outside [0,%d)",
-                  label_tokens[i], (long long)i, V);
-  }
 
   // 1. insert: provisional ids in creation order, root = 0
   std::unordered_map<uint64_t, int32_t> child_of;
@@ -54,8 +69,7 @@ extern "C" int tcs_trie_build(const int32_t* label_offsets, const int32_t* label
   for (int32_t m = 0; m < M; ++m) {
     int32_t node = 0;
     for (int32_t i = label_offsets[m]; i < label_offsets[m + 1]; ++i) {
-      const uint64_t key = (static_cast<uint64_t>(static_cast<uint32_t>(node)) << 32) |
-                           static_cast<uint32_t>(label_tokens[i]);
+      const uint64_t key = edge_key(node, label_tokens[i]);
       auto it = child_of.find(key);
       if (it == child_of.end()) {
         const int32_t id = static_cast<int32_t>(label_at.size());
@@ -176,6 +190,62 @@ extern "C" int tcs_trie_build(const int32_t* label_offsets, const int32_t* label
       const int32_t u = out->label_node[m];
       out->label_row[m] = out->child_count[u] > 0 ? out->qrow[u] : out->qrow[out->parent[u]];
     }
+  }
+  return TCS_OK;
+}
+
+// Decision-word cut of every label ("To Classify, Try a Trie Tree", section 3.2).
+// One pass inserts the labels into a (node, token) map and counts, per node, the
+// labels that pass through it; label m leaves all others at the first node on its
+// path that it alone passes, and its word then runs on over the continuation tokens.
+extern "C" int tcs_decision_truncate(const int32_t* label_offsets, const int32_t* label_tokens,
+                                     int32_t M, int32_t V, const uint8_t* word_cont,
+                                     int32_t* out_offsets, int32_t* out_tokens, int32_t* depth) {
+  using tcs::fail;
+  tcs::clear_error();
+  if (int rc = check_labels("decision_truncate", label_offsets, label_tokens, M, V)) return rc;
+  if (!word_cont || !out_offsets || !out_tokens)
+    return fail(TCS_EINVAL, "decision_truncate: null pointer");
+  const int64_t T = label_offsets[M];
+
+  std::unordered_map<uint64_t, int32_t> child_of;
+  child_of.reserve(static_cast<size_t>(T) * 2 + 1);
+  std::vector<int32_t> through(1, M);   // labels passing each node (root: all)
+  std::vector<int32_t> ends(1, -1);     // label ending at each node
+  std::vector<int32_t> path(T);         // node reached after each label token
+  for (int32_t m = 0; m < M; ++m) {
+    int32_t node = 0;
+    for (int32_t i = label_offsets[m]; i < label_offsets[m + 1]; ++i) {
+      auto ins = child_of.emplace(edge_key(node, label_tokens[i]),
+                                  static_cast<int32_t>(through.size()));
+      if (ins.second) {
+        through.push_back(0);
+        ends.push_back(-1);
+      }
+      node = ins.first->second;
+      ++through[node];
+      path[i] = node;
+    }
+    if (ends[node] >= 0)
+      return fail(TCS_EDUPLICATE, "decision_truncate: label %d duplicates label %d", m,
+                  ends[node]);
+    ends[node] = m;
+  }
+
+  out_offsets[0] = 0;
+  for (int32_t m = 0; m < M; ++m) {
+    const int32_t b = label_offsets[m], n = label_offsets[m + 1] - b;
+    int32_t k = n;  // a label that is the start of another keeps every token
+    for (int32_t j = 0; j < n; ++j) {
+      if (through[path[b + j]] == 1) {
+        k = j + 1;
+        break;
+      }
+    }
+    while (k < n && word_cont[label_tokens[b + k]]) ++k;
+    if (depth) depth[m] = k;
+    std::memcpy(out_tokens + out_offsets[m], label_tokens + b, sizeof(int32_t) * k);
+    out_offsets[m + 1] = out_offsets[m] + k;
   }
   return TCS_OK;
 }
