@@ -120,6 +120,12 @@ HEAD_CASES = {
     "small-fp8": dict(V=777, d=192, labels=("zipf", 40, 2, 6, 1.2), B=9, head="fp8"),
     "small-f32": dict(V=1000, d=64, labels=("running",), B=4, head="f32"),
     "ragged-vocab": dict(V=257, d=64, labels=("zipf", 12, 1, 4, 1.0), B=3, head="bf16"),
+    # row-tile counts (72 rows per document) for the head's tile order: 16 tiles (two
+    # strips of 8), 39 (one group of 32 + a 7-row strip), 73 (two groups + strips of
+    # 5 and 4)
+    "rows-16-tiles": dict(V=1000, d=128, labels=("zipf", 40, 2, 6, 1.2), B=56, head="bf16"),
+    "rows-39-tiles": dict(V=1000, d=128, labels=("zipf", 40, 2, 6, 1.2), B=138, head="bf16"),
+    "rows-73-tiles-fp8": dict(V=777, d=192, labels=("zipf", 40, 2, 6, 1.2), B=259, head="fp8"),
 }
 
 
@@ -163,7 +169,8 @@ def test_lmhead_vs_oracle(dev, name):
     o_lp = O.edge_logprobs(model, trie, h.reshape(B, trie.n_int, -1), o_lse.reshape(B, trie.n_int))
     e1 = np.abs(lse - o_lse).max()
     e2 = np.abs(lp - o_lp).max()
-    say(f"lmhead[{name}] R={B * trie.n_int} V={cfg.V}: max |dlse| {e1:.2e} max |dlp| {e2:.2e}")
+    say(f"lmhead[{name}] R={B * trie.n_int} ({-(-B * trie.n_int // 256)} row tiles) V={cfg.V}: "
+        f"max |dlse| {e1:.2e} max |dlp| {e2:.2e}")
     assert e1 < 2e-4 and e2 < 2e-4
     assert np.all(lp[:, 0] == 0)
 

@@ -197,38 +197,39 @@ __device__ __forceinline__ int dma_swz(int r) { return (r ^ (r >> 3)) & 7; }  //
 
 
 // Output-head tile order: tile slot `bid` = 256 w + b is the w-th tile of the
-// persistent workgroup b (one per CU; b runs on XCD b % 8).  The 256 slots of one
-// round w cover a GM x GN block of tiles; each XCD takes an MX x NX sub-block so
-// its L2 serves both operands, and all XCDs share the block's other operand
-// through the MALL.  Returns false for slots past the matrix edge.
+// persistent workgroup b (one per CU; b runs on XCD b % 8).  Row tiles go in full
+// groups of 32 while they last: a round covers a 32 x 8 block of (row, column)
+// tiles, each XCD a 4 x 8 sub-block, so its L2 serves both operands and all XCDs
+// share the block's 8 weight tiles through the MALL.  The rem = nbm mod 32 row
+// tiles left over (all of them when nbm < 32) are cut into strips of at most 8
+// rows and enumerated densely, tile u of a strip of h rows at (u mod h, u / h):
+// every round but the last is full, and an XCD's 32 consecutive tiles span h rows
+// by about 32/h columns.  Returns false for slots past the matrix edge.
 __device__ __forceinline__ bool head_tile_coords(int bid, int nbm, int nbn, int& mt, int& nt) {
   const int xcd = bid & 7, slot = (bid >> 3) & 31, w = bid >> 8;
-  int MX, NX, GM, GN, m_local, n_local;
-  if (nbm >= 32) {          // XCDs split the rows: per XCD 4 x 8
-    MX = 4; NX = 8; GM = 32; GN = 8;
-    m_local = xcd * MX + slot % MX;
-    n_local = slot / MX;
-  } else {                  // XCDs split the columns: per XCD MX x (32/MX)
-    MX = nbm >= 16 ? 16 : nbm >= 8 ? 8 : nbm >= 4 ? 4 : nbm >= 2 ? 2 : 1;
-    NX = 32 / MX; GM = MX; GN = 8 * NX;
-    m_local = slot % MX;
-    n_local = xcd * NX + slot / MX;
+  const int G = nbm >> 5, nbc = (nbn + 7) >> 3;  // full row groups, 8-column blocks
+  if (w < G * nbc) {
+    const int g = w / nbc, nb = w - g * nbc;
+    mt = g * 32 + xcd * 4 + (slot & 3);
+    nt = nb * 8 + (slot >> 2);
+    return nt < nbn;
   }
-  const int nb_count = (nbn + GN - 1) / GN;
-  const int g = w / nb_count, nb = w % nb_count;
-  mt = g * GM + m_local;
-  nt = nb * GN + n_local;
-  return mt < nbm && nt < nbn;
+  const int rem = nbm - G * 32;
+  if (rem <= 0) return false;
+  const int u = (w - G * nbc) * 256 + xcd * 32 + slot;
+  const int ns = (rem + 7) >> 3, hs = (rem + ns - 1) / ns;  // strips, rows per strip
+  const int s = min(u / (hs * nbn), ns - 1);
+  const int h = min(hs, rem - s * hs);  // the last strip may be shorter
+  const int loc = u - s * hs * nbn;
+  mt = G * 32 + s * hs + loc % h;
+  nt = loc / h;
+  return nt < nbn;
 }
 
+// Slots (a multiple of 256) that head_tile_coords spreads the nbm x nbn tiles over.
 __host__ __device__ inline int head_grid(int nbm, int nbn) {
-  int GM, GN;
-  if (nbm >= 32) { GM = 32; GN = 8; }
-  else {
-    const int MX = nbm >= 16 ? 16 : nbm >= 8 ? 8 : nbm >= 4 ? 4 : nbm >= 2 ? 2 : 1;
-    GM = MX; GN = 8 * (32 / MX);
-  }
-  return ((nbm + GM - 1) / GM) * ((nbn + GN - 1) / GN) * 256;
+  const int G = nbm >> 5, nbc = (nbn + 7) >> 3, rem = nbm - G * 32;
+  return (G * nbc + (rem * nbn + 255) / 256) * 256;
 }
 
 }  // namespace tcs
