@@ -14,6 +14,9 @@ Sources (cited by page title and section):
        refund 0.8 x 0.6 = 0.48 against praise 0.3).
   [QI] "Building an Ultra-High Throughput AI-SQL Engine", section 3.2.4 (partial
        attention results merged by their log-sum-exp / online softmax).
+  [CT] also section 3.3 (letters: one letter token per label, read at the ANSWER:
+       position and rescaled over the letters) and section 4.1 (when every label is
+       one token only the label tokens' head rows are computed).
   [TA] "Trie Automata for Constrained Decoding over Large Finite Sets",
        Proposition 1 (the trie is the minimal automaton: one state per distinct
        prefix).
@@ -38,7 +41,11 @@ reason in the design notes):
       carry a word-continuation flag (a per-vocabulary input); a label "leaves all
       others" at its first token k such that no other label starts with its first
       k tokens; a label that never does (it is the start of another label) is
-      scored over all its tokens, with the prefix rule of R3.
+      scored over all its tokens, with the prefix rule of R3;
+  R10 letters ([CT] 3.3): the letter tokens are M distinct vocabulary ids (an
+      input); the one answer position is the root, attending to the document and
+      itself as in R4; the returned scores are the letter logits (log scores up to a
+      per-document constant, as the vocabulary log-sum-exp is never formed).
 
 Parity status: every function below is pinned by the non-GPU oracle tests
 (library routines, closed forms, the worked example, brute-force scoring).
@@ -55,7 +62,7 @@ __all__ = [
     "node_layer", "doc_kv_from_tokens", "tree_attention", "hidden_states",
     "lm_head_lse", "head_logits_at", "edge_logprobs", "log1mexp", "path_log_likelihoods",
     "label_softmax", "classify", "bruteforce_ll", "label_ll_on_paths",
-    "decision_depths", "truncate_labels",
+    "decision_depths", "truncate_labels", "letters_classify",
 ]
 
 TCS_OK = 0
@@ -580,3 +587,40 @@ def decision_depths(labels, word_cont):
 def truncate_labels(labels, depths):
     """Label m cut to its first depths[m] tokens."""
     return [list(map(int, l[:int(d)])) for l, d in zip(labels, depths)]
+
+
+# =========================================================================== letters ([CT] 3.3)
+
+def letters_classify(inp: dict, letters, docs=None, model: OracleModel | None = None):
+    """letters: one answer position (the root, ANSWER:) per document; the logits of
+    the M letter tokens are read there and rescaled over the letters.
+
+    [CT] 3.3: P_hat(m) = P(letter_m) / sum_m' P(letter_m'); the vocabulary
+    normaliser of P cancels, so only the M letter rows of the head are used
+    ([CT] 4.1, V_out = M).  Returns dict(z [B, M] letter logits, prob, label).
+    """
+    model = model or OracleModel(inp)
+    letters = [int(t) for t in letters]
+    root = int(inp["root_token"])
+    offs = inp["doc_offsets"]
+    docs = list(range(len(offs) - 1)) if docs is None else list(docs)
+    x, q, k, v = node_layer(model, [root])
+    group = model.Hq // model.Hkv
+    z = np.zeros((len(docs), len(letters)))
+    for i, b in enumerate(docs):
+        if inp["cfg"].doc_mode == "tokens":
+            Kb, Vb = doc_kv_from_tokens(model, inp["doc_tokens"][offs[b]:offs[b + 1]])
+        else:
+            dec = decode_bf16 if model.bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+            Kb, Vb = dec(inp["Kd"][offs[b]:offs[b + 1]]), dec(inp["Vd"][offs[b]:offs[b + 1]])
+        keys = np.concatenate([Kb, k], axis=0)      # the document, then the answer position
+        vals = np.concatenate([Vb, v], axis=0)
+        O = np.zeros((model.Hq, model.hd))
+        for h in range(model.Hq):
+            s = keys[:, h // group, :] @ q[0, h, :] * model.scale
+            p = np.exp(s - s.max())
+            O[h] = (p / p.sum()) @ vals[:, h // group, :]
+        hid = hidden_states(model, x[None], model.rnd(O)[None, None])[0, 0]
+        z[i] = head_logits_at(model, hid[None], cols=letters)[0]
+    prob, label = label_softmax(z)
+    return dict(z=z, prob=prob, label=label, docs=docs)

@@ -16,8 +16,8 @@ Storage formats produced here:
     saturated at +-448.
 
 Random sub-streams, in spawn order: trie, root token, E, Wq, Wk, Wv, Wo, W, doc,
-word (the word-continuation flags; spawned last so the earlier streams are the
-same with or without it).
+word (the word-continuation flags), letters (the letter token ids); streams are
+only ever appended, so the earlier ones do not change.
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-STREAMS = ("trie", "root", "E", "Wq", "Wk", "Wv", "Wo", "W", "doc", "word")
+STREAMS = ("trie", "root", "E", "Wq", "Wk", "Wv", "Wo", "W", "doc", "word", "letters")
 
 
 @dataclass(frozen=True)
@@ -259,7 +259,7 @@ def make_inputs(cfg: Config, seed: int | None = None, *, weights: bool = True):
     """Draw one workload.  Returns a dict of numpy arrays plus the label lists.
 
     Keys: labels (list of lists), label_offsets, label_tokens, root_token, word_cont
-    (uint8 [V] word-continuation flags), E, Wq, Wk,
+    (uint8 [V] word-continuation flags), letters (int32 [M] letter token ids), E, Wq, Wk,
     Wv, Wo, W, W_scale (fp8 head only, else None), doc_offsets, and either Kd/Vd
     ([sum L, Hkv, hd]) or doc_tokens ([sum L]).
     """
@@ -272,6 +272,9 @@ def make_inputs(cfg: Config, seed: int | None = None, *, weights: bool = True):
     out["label_offsets"], out["label_tokens"] = labels_to_csr(labels)
     out["root_token"] = int(rngs["root"].integers(0, cfg.V))
     out["word_cont"] = word_continuation_flags(cfg, labels, rngs["word"])
+    # letters ("To Classify, Try a Trie Tree", section 3.3): one answer token per
+    # label, M distinct vocabulary ids standing in for "A", "B", ...
+    out["letters"] = rngs["letters"].choice(cfg.V, size=len(labels), replace=False).astype(np.int32)
     d, Hq, Hkv, hd, V = cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, cfg.V
     if weights:
         out["E"] = _weight(rngs["E"], (V, d), cfg.std, cfg.dtype)
