@@ -1,7 +1,7 @@
 """Throughput of the trie_tree label-scoring pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
-                    [--no-cpu-baseline] [--no-path-stress] [--no-decision-word]
+                    [--no-cpu-baseline] [--no-path-stress] [--no-decision-word] [--no-letters]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
     python bench.py --head-probe --config 3 [--power]  # head alone: workload-like vs constant
                                                        # operands (+ socket power and clocks)
@@ -25,7 +25,8 @@ path-sum kernel alone on 4096 documents of the 5000-label trie (enough bytes to 
 it against HBM).  ``decision_word`` runs the same documents and weights with every
 label cut to the end of the word where it leaves the others (the decision-word form
 of trie_tree: fewer query rows, same kernels); the headline scores every label over
-its full root-to-leaf path.  ``roofline`` is for the
+its full root-to-leaf path.  ``letters`` runs them under the letters method (one
+answer position per document, only the letter rows of the head).  ``roofline`` is for the
 dominant kernel (the output head): after the timed steps, the same steps run
 again with the head launches bracketed by HIP events on the stream they run on
 (the library's tcs_timing_enable hook), and achieved = algorithmic FLOP per
@@ -171,8 +172,12 @@ def run_steps(S, steps, warmup):
 
     def step(i, k=None):
         k = i % n if k is None else k
-        tcs.classify(S["model"], S["td"], S["docs"], ws=S["ws"][k], prepared=S["prep"],
-                     stream=streams[k], **S["out"][k])
+        if S.get("letters"):
+            tcs.letters(S["model"], S["td"], S["docs"], S["prep"], ws=S["ws"][k], stream=streams[k],
+                        **S["out"][k])
+        else:
+            tcs.classify(S["model"], S["td"], S["docs"], ws=S["ws"][k], prepared=S["prep"],
+                         stream=streams[k], **S["out"][k])
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -234,6 +239,32 @@ def doc_attn_roofline(S, ms):
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": by, "flops_per_launch": fl,
             "ms_per_launch": round(ms, 4)}
+
+
+def letters_measure(S, steps, warmup, streams):
+    """The same documents and weights under the letters method (tcs_letters_run): one
+    answer position per document and the M letter rows of the head; the document
+    attention is then the dominant kernel."""
+    import torch
+    import trie_constrained_scoring_amd as tcs
+    cfg, inp = S["cfg"], S["inp"]
+    letters = np.asarray(inp["letters"], dtype=np.int32)
+    trie = tcs.trie_build(np.arange(len(letters) + 1, dtype=np.int32), letters, inp["root_token"],
+                          cfg.V)
+    td = tcs.TrieDevice(trie)
+    prep = tcs.Prepared(S["model"], td, S["docs"].B)
+    ws, out = run_buffers(S["model"], td, S["docs"], streams)
+    C = dict(S, trie=trie, td=td, prep=prep, ws=ws, out=out, letters=True)
+    sec, kern = run_steps(C, steps, warmup)
+    B = S["docs"].B
+    e = {"config": cfg.id, "letters": len(letters), "docs_per_s": round(B / sec, 2),
+         "ms_per_step": round(sec * 1e3, 4)}
+    if kern["doc_attn"]:
+        e["doc_attn_roofline"] = doc_attn_roofline(C, kern["doc_attn"])
+        e["doc_attn_share_of_step"] = round(kern["doc_attn"] / (sec * 1e3), 4)
+    del C, prep, ws, out, td
+    torch.cuda.empty_cache()
+    return e
 
 
 def cpu_baseline(S, budget_s=15.0):
@@ -392,6 +423,8 @@ def main():
                     help="leave the path-sum stress measurement (path_roofline) out")
     ap.add_argument("--no-decision-word", action="store_true",
                     help="leave the decision-word measurements (labels cut to their deciding word) out")
+    ap.add_argument("--no-letters", action="store_true",
+                    help="leave the letters measurements (one answer position, letter rows only) out")
     ap.add_argument("--power", action="store_true",
                     help="with --head-probe: also sample socket power and GFX clocks (amd-smi)")
     args = ap.parse_args()
@@ -453,9 +486,11 @@ def main():
     res["head_share_of_step"] = round(kern["head"] / (sec * 1e3), 4)
     if kern["doc_attn"]:
         res["doc_attn_roofline"] = doc_attn_roofline(S, kern["doc_attn"])
-    decision = {}
+    decision, letters = {}, {}
     if not args.no_decision_word:
         decision[cfg.name] = decision_word(S, args.steps, args.warmup, args.streams)
+    if not args.no_letters:
+        letters[cfg.name] = letters_measure(S, args.steps, args.warmup, args.streams)
     extra = {}
     for c in [int(x) for x in args.extra.split(",") if x.strip()]:
         if c == args.config:
@@ -477,11 +512,15 @@ def main():
         extra[str(S2["trie"].n_labels)] = e
         if not args.no_decision_word:
             decision[S2["cfg"].name] = decision_word(S2, max(3, args.steps // 2), 2, args.streams)
+        if not args.no_letters:
+            letters[S2["cfg"].name] = letters_measure(S2, max(3, args.steps // 2), 2, args.streams)
         S = S2
     if extra:
         res["at_labels"] = extra
     if decision:
         res["decision_word"] = decision
+    if letters:
+        res["letters"] = letters
     if not args.no_path_stress:
         del S
         torch.cuda.empty_cache()

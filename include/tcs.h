@@ -321,6 +321,29 @@ int tcs_classify_run(tcs_stream stream, const tcs_model* model, const tcs_trie_d
                      const tcs_docs* docs, const tcs_prepared* prep, int32_t* label, float* prob,
                      float* ll, void* ws, size_t ws_bytes);
 
+/*
+ * letters ("To Classify, Try a Trie Tree", section 3.3): the prompt shows each
+ * label behind its own letter and the answer is one letter token.  The model runs
+ * at one answer position per document, the ANSWER: position (the trie's root,
+ * attending to the document and to itself); the M letter logits are read there,
+ * rescaled to sum to 1 over the letters and the best letter's label is returned.
+ * Since every label is one token, the output head computes only the M letter rows
+ * (section 4.1): the vocabulary log-sum-exp would cancel in the rescale and is
+ * never formed.
+ *
+ * `trie` is tcs_trie_build's trie of the M letter tokens as one-token labels
+ * (label m = letter token m; max_depth 1, one query row), with root_token the
+ * ANSWER: token.  `prep` comes from tcs_classify_prepare for that trie and B,
+ * `ws` holds tcs_classify_run_workspace_bytes(model, trie, docs) bytes.
+ * Outputs (device): label [B]; prob [B, M] (may be NULL): the rescaled
+ * probabilities; ll [B, M] (may be NULL): the letter logits, i.e. log scores up to
+ * a per-document constant.  Errors as tcs_classify_run, and TCS_EINVAL for a trie
+ * with a label longer than one token.
+ */
+int tcs_letters_run(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* trie,
+                    const tcs_docs* docs, const tcs_prepared* prep, int32_t* label, float* prob,
+                    float* ll, void* ws, size_t ws_bytes);
+
 /* ----------------------------------------------------------- measurement ---- */
 /*
  * Per-kernel timing, for measuring a kernel against its roofline from inside a

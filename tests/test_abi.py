@@ -191,3 +191,21 @@ def test_decision_truncate_errors():
     o2, t2 = np.zeros(2, np.int32), np.zeros(2, np.int32)
     assert lib.tcs_decision_truncate(P(offs), P(toks), 1, 10, flags, P(o2), P(t2), None) == tcs.TCS_OK
     assert list(o2) == [0, 1] and t2[0] == 1
+
+
+def test_letters_rejects_deeper_tries_without_gpu():
+    """tcs_letters_run checks the trie before touching any device memory: a label of
+    two tokens is refused (the pointers below are never dereferenced)."""
+    lib = tcs.lib()
+    assert lib.tcs_letters_run(None, None, None, None, None, None, None, None, None, 0) == tcs.TCS_EINVAL
+    t = tcs.trie_build(*labels_to_csr([[3], [4, 5]]), 0, 16)
+    fake = 256
+    dev = tcs.tcs_trie_dev(n_nodes=t.n_nodes, n_int=t.n_int, n_labels=t.n_labels,
+                           max_depth=t.max_depth,
+                           **{n: fake for n in tcs.TRIE_DEV_ARRAYS})
+    model = tcs.tcs_model(dtype=tcs.TCS_BF16, head_dtype=tcs.TCS_BF16, d=128, Hq=2, Hkv=1, hd=128,
+                          V=16, eps=1e-6, E=fake, Wq=fake, Wk=fake, Wv=fake, Wo=fake, W=fake)
+    docs = tcs.tcs_docs(B=1, total_tokens=4, doc_offsets=fake, Kd=fake, Vd=fake)
+    rc = lib.tcs_letters_run(None, C.byref(model), C.byref(dev), C.byref(docs), None, None, None,
+                             None, None, 0)
+    assert rc == tcs.TCS_EINVAL and b"one-token" in lib.tcs_last_error()

@@ -109,6 +109,7 @@ def lib():
                                                        C.POINTER(tcs_docs)]
         L.tcs_classify_run.argtypes = [vp, C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
                                        C.POINTER(tcs_docs), C.POINTER(tcs_prepared), vp, vp, vp, vp, sz]
+        L.tcs_letters_run.argtypes = list(L.tcs_classify_run.argtypes)
         L.tcs_timing_enable.argtypes = [C.c_int]
         L.tcs_timing_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i32)]
         _lib_handle = L
@@ -475,4 +476,33 @@ def classify(model: Model, trie_dev: TrieDevice, docs: Docs, label=None, prob=No
                                       C.byref(trie_dev.struct), C.byref(docs.struct),
                                       C.byref(prepared.struct), _ptr(label), _ptr(prob), _ptr(ll),
                                       _ptr(ws), ws.numel()))
+    return label, prob, ll
+
+
+def letters(model: Model, trie_dev: TrieDevice, docs: Docs, prepared: Prepared, label=None,
+            prob=None, ll=None, with_prob=True, ws=None, stream=None):
+    """letters (tcs_letters_run): one answer position per document, the M letter rows
+    of the head only, probabilities rescaled over the letters.  `trie_dev` holds the
+    letter tokens as one-token labels; `prepared` is its tcs_classify_prepare state.
+    Returns (label [B], prob [B, M], ll [B, M] letter logits)."""
+    torch = _torch()
+    B, M = docs.B, trie_dev.trie.n_labels
+    dev = docs.offsets.device
+    if label is None:
+        label = torch.empty(B, dtype=torch.int32, device=dev)
+    if prob is None and with_prob:
+        prob = torch.empty((B, M), dtype=torch.float32, device=dev)
+    if ll is None:
+        ll = torch.empty((B, M), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(classify_run_workspace_bytes(model, trie_dev, docs), dtype=torch.uint8,
+                         device=dev)
+    _need_cuda(label, prob, ll, ws)
+    if stream is not None:
+        for x in (label, prob, ll, ws):
+            if x is not None:
+                x.record_stream(stream)
+    _check(lib().tcs_letters_run(_stream(stream), C.byref(model.struct), C.byref(trie_dev.struct),
+                                 C.byref(docs.struct), C.byref(prepared.struct), _ptr(label),
+                                 _ptr(prob), _ptr(ll), _ptr(ws), ws.numel()))
     return label, prob, ll

@@ -250,9 +250,11 @@ static int prepare_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t,
                             t->e_child, t->n_nodes - 1, P.head);
 }
 
-// One batch on prepared state.
+// One batch on prepared state.  letters: the trie is the letters' one-level trie and
+// the head computes only the letter rows, with no log-sum-exp.
 static int run_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
-                    const void* prep_buf, int32_t* label, float* prob, float* ll, void* ws) {
+                    const void* prep_buf, int32_t* label, float* prob, float* ll, void* ws,
+                    bool letters = false) {
   const PrepLayout P = prep_layout(m, t, d->B, const_cast<void*>(prep_buf));
   const RunLayout L = run_layout(m, t, d, ws);
   const tcs_dtype dt = m->dtype;
@@ -290,6 +292,11 @@ static int run_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, con
   if (rc) return rc;
   if ((rc = launch_rownorm(stream, dt, L.y, R, m->d, gemm_resid_splits(dt, R, m->d, qd), m->eps,
                            L.h))) return rc;
+  if (letters) {
+    if ((rc = launch_letter_logits(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, L.h, m->W,
+                                   m->W_scale, t->token, L.lp))) return rc;
+    return launch_path_sum(stream, B, t, L.lp, ll ? ll : static_cast<float*>(L.ll), prob, label);
+  }
   // the head leaves raw child logits in lp; the path sum subtracts lse itself
   if ((rc = launch_lmhead_run(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,
                               m->W_scale, t->e_tok, t->e_qrow, t->e_child, L.lse, L.lp, P.head,
@@ -337,6 +344,26 @@ int tcs_classify_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* 
   const size_t need = run_layout(m, t, d, nullptr).total;
   if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "classify_run: workspace %zu < %zu bytes", ws_bytes, need);
   return run_impl(stream, m, t, d, prep->buf, label, prob, ll, ws);
+}
+
+int tcs_letters_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
+                    const tcs_prepared* prep, int32_t* label, float* prob, float* ll, void* ws,
+                    size_t ws_bytes) {
+  clear_error();
+  if (int rc = check_classify(m, t, d)) return rc;
+  if (t->max_depth != 1 || t->n_int != 1)
+    return fail(TCS_EINVAL, "letters: the trie must hold one-token labels only (depth %d, %d rows)",
+                t->max_depth, t->n_int);
+  if (d->B == 0) return TCS_OK;
+  if (!label) return fail(TCS_EINVAL, "letters: null label output");
+  if (!prep || !prep->buf) return fail(TCS_EINVAL, "letters: null prepared state");
+  if (prep->B != d->B)
+    return fail(TCS_EINVAL, "letters: state prepared for B=%d, batch has B=%d", prep->B, d->B);
+  if (prep->bytes < prep_layout(m, t, d->B, nullptr).total)
+    return fail(TCS_ECAPACITY, "letters: prepared buffer too small");
+  const size_t need = run_layout(m, t, d, nullptr).total;
+  if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "letters: workspace %zu < %zu bytes", ws_bytes, need);
+  return run_impl(stream, m, t, d, prep->buf, label, prob, ll, ws, true);
 }
 
 size_t tcs_classify_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,

@@ -99,6 +99,12 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
                   const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
                   const int32_t* e_child, int32_t n_edges, float* lse, float* lp, void* ws);
 
+// letters: lp[b][c] = h[b n_int] . W[token[c]] (x row scale for fp8 W) for the
+// root's children c = 1 .. n_nodes-1, lp[b][0] = 0.
+int launch_letter_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
+                         int32_t n_int, int32_t n_nodes, int32_t d, const void* h, const void* W,
+                         const float* w_scale, const int32_t* token, float* lp);
+
 // Tree attention pieces.
 int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32_t Hkv,
                     int32_t hd, const void* Qn, const void* Kn, const void* Vn,
