@@ -14,7 +14,11 @@ Sources (cited by page title and section):
        refund 0.8 x 0.6 = 0.48 against praise 0.3).
   [QI] "Building an Ultra-High Throughput AI-SQL Engine", section 3.2.4 (partial
        attention results merged by their log-sum-exp / online softmax).
-  [CT] also section 3.3 (letters: one letter token per label, read at the ANSWER:
+  [CT] also section 3.1 (trie_decode: greedy generation inside the trie, the model
+       only where labels branch, stopping once one label remains; note 2: a label
+       that is the start of another is never returned), section 4.3 (requests per
+       document, b = mean over labels of the branching nodes on their paths),
+       section 3.3 (letters: one letter token per label, read at the ANSWER:
        position and rescaled over the letters) and section 4.1 (when every label is
        one token only the label tokens' head rows are computed).
   [TA] "Trie Automata for Constrained Decoding over Large Finite Sets",
@@ -45,7 +49,9 @@ reason in the design notes):
   R10 letters ([CT] 3.3): the letter tokens are M distinct vocabulary ids (an
       input); the one answer position is the root, attending to the document and
       itself as in R4; the returned scores are the letter logits (log scores up to a
-      per-document constant, as the vocabulary log-sum-exp is never formed).
+      per-document constant, as the vocabulary log-sum-exp is never formed);
+  R11 trie_decode ties go to the lowest token id; a decode run at a node is the
+      model over [root, path tokens] attending to the document (as in R4/R5).
 
 Parity status: every function below is pinned by the non-GPU oracle tests
 (library routines, closed forms, the worked example, brute-force scoring).
@@ -62,7 +68,7 @@ __all__ = [
     "node_layer", "doc_kv_from_tokens", "tree_attention", "hidden_states",
     "lm_head_lse", "head_logits_at", "edge_logprobs", "log1mexp", "path_log_likelihoods",
     "label_softmax", "classify", "bruteforce_ll", "label_ll_on_paths",
-    "decision_depths", "truncate_labels", "letters_classify",
+    "decision_depths", "truncate_labels", "letters_classify", "greedy_walk", "trie_decode",
 ]
 
 TCS_OK = 0
@@ -624,3 +630,84 @@ def letters_classify(inp: dict, letters, docs=None, model: OracleModel | None = 
         z[i] = head_logits_at(model, hid[None], cols=letters)[0]
     prob, label = label_softmax(z)
     return dict(z=z, prob=prob, label=label, docs=docs)
+
+
+# =========================================================================== trie_decode ([CT] 3.1)
+
+def greedy_walk(labels, choose):
+    """Walk the label set the way trie_decode generates ([CT] 3.1).
+
+    The state is the token prefix generated so far (empty = the ANSWER: root).
+    While more than one label starts with the prefix: if those labels agree on the
+    next token, take it with no model run; else ask `choose(prefix, tokens)` for
+    one of the distinct next tokens (a model run).  A label equal to the prefix
+    while longer ones remain is never the answer (no stop token, [CT] note 2).
+    Returns (label id, number of `choose` calls).
+    """
+    labels = [tuple(map(int, l)) for l in labels]
+    prefix, runs = (), 0
+    while True:
+        remaining = [m for m, l in enumerate(labels) if l[:len(prefix)] == prefix]
+        if len(remaining) == 1:
+            return remaining[0], runs
+        nxt = sorted({labels[m][len(prefix)] for m in remaining if len(labels[m]) > len(prefix)})
+        if len(nxt) == 1:
+            prefix += (nxt[0],)
+            continue
+        runs += 1
+        prefix += (int(choose(prefix, nxt)),)
+
+
+def _sequence_last_hidden(model: OracleModel, Kb, Vb, seq):
+    """Hidden state at the last position of the token sequence `seq` placed after
+    the document: every position attends to the document and causally to the
+    sequence (R4, R5)."""
+    n = len(seq)
+    x, q, k, v = node_layer(model, seq)
+    keys = np.concatenate([Kb, k], axis=0)
+    vals = np.concatenate([Vb, v], axis=0)
+    L = Kb.shape[0]
+    group = model.Hq // model.Hkv
+    O = np.zeros((model.Hq, model.hd))
+    for h in range(model.Hq):
+        s = keys[:L + n, h // group, :] @ q[n - 1, h, :] * model.scale
+        p = np.exp(s - s.max())
+        O[h] = (p / p.sum()) @ vals[:L + n, h // group, :]
+    return hidden_states(model, x[n - 1][None], model.rnd(O)[None])[0]
+
+
+def trie_decode(inp: dict, docs=None, model: OracleModel | None = None):
+    """trie_decode for the listed documents ([CT] 3.1): at each branching point the
+    model runs on [root, prefix] and the next token is the candidate with the
+    highest logit (lowest token id on ties, R11); the vocabulary normaliser is the
+    same for all candidates, so logits decide.
+
+    Returns dict(label [B], runs [B] model runs per document, gap [B]: the smallest
+    difference between the two best candidate logits over the document's runs).
+    """
+    model = model or OracleModel(inp)
+    root = int(inp["root_token"])
+    offs = inp["doc_offsets"]
+    docs = list(range(len(offs) - 1)) if docs is None else list(docs)
+    labels, runs, gaps = [], [], []
+    for b in docs:
+        if inp["cfg"].doc_mode == "tokens":
+            Kb, Vb = doc_kv_from_tokens(model, inp["doc_tokens"][offs[b]:offs[b + 1]])
+        else:
+            dec = decode_bf16 if model.bf16 else (lambda a: np.asarray(a, dtype=np.float64))
+            Kb, Vb = dec(inp["Kd"][offs[b]:offs[b + 1]]), dec(inp["Vd"][offs[b]:offs[b + 1]])
+        gap = [np.inf]
+
+        def choose(prefix, cands):
+            hid = _sequence_last_hidden(model, Kb, Vb, [root] + list(prefix))
+            z = head_logits_at(model, hid[None], cols=cands)[0]
+            srt = np.sort(z)
+            gap[0] = min(gap[0], srt[-1] - srt[-2])
+            return cands[int(np.argmax(z))]
+
+        m, r = greedy_walk(inp["labels"], choose)
+        labels.append(m)
+        runs.append(r)
+        gaps.append(gap[0])
+    return dict(label=np.array(labels, dtype=np.int32), runs=np.array(runs, dtype=np.int32),
+                gap=np.array(gaps), docs=docs)
