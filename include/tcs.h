@@ -103,6 +103,12 @@ typedef struct {
   int32_t* row_level_offsets; /* [cap_levels] first query row of each depth, then n_int */
   int32_t* label_row;    /* [M] row whose prefix sum a label's score starts from: its
                             node's row if the node is internal, else its parent's */
+  /* optional (may be NULL): tables of greedy decoding (tcs_decode_run) */
+  int32_t* sub_label;    /* [cap_nodes] the label if the node's subtree holds exactly one
+                            label, else -1 */
+  int32_t* dec_node;     /* [cap_nodes] where decoding goes on from the node: follow single
+                            children while the subtree holds more than one label */
+  int32_t max_decode_steps; /* set with the tables: the most model runs any label needs */
 } tcs_trie;
 
 /*
@@ -159,6 +165,10 @@ typedef struct {
   const int32_t* qrow;               /* [n_nodes] */
   const int32_t* row_level_offsets;  /* [max_depth + 2] */
   const int32_t* label_row;          /* [n_labels] */
+  /* optional (NULL unless tcs_decode_run is used) */
+  const int32_t* sub_label;          /* [n_nodes] */
+  const int32_t* dec_node;           /* [n_nodes] */
+  int32_t max_decode_steps;
 } tcs_trie_dev;
 
 /* --------------------------------------------------------- tree attention ---- */
@@ -343,6 +353,35 @@ int tcs_classify_run(tcs_stream stream, const tcs_model* model, const tcs_trie_d
 int tcs_letters_run(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* trie,
                     const tcs_docs* docs, const tcs_prepared* prep, int32_t* label, float* prob,
                     float* ll, void* ws, size_t ws_bytes);
+
+/*
+ * trie_decode ("To Classify, Try a Trie Tree", section 3.1): the label is
+ * generated greedily inside the trie.  Each document starts at the root (the
+ * ANSWER: token).  Where labels branch (a node with several children and more
+ * than one label below it) the model runs at that node -- its query attends to
+ * the document and to the node's own path, as in tree attention -- and the child
+ * whose token has the highest logit is taken (the lowest token id on ties; the
+ * vocabulary normaliser is shared by the candidates, so logits decide and no
+ * log-sum-exp is formed).  A node with one child is passed without a run; a
+ * document stops once one label remains below its node.  All undecided documents
+ * take one step together; a label that is the start of another is never returned
+ * (there is no stop token: section 3.1, note 2).  No probabilities are produced.
+ *
+ * `trie` needs the optional qrow, sub_label and dec_node arrays and
+ * max_decode_steps (tcs_trie_build fills them when given the arrays); `prep` comes
+ * from tcs_classify_prepare for that trie and B; `ws` holds
+ * tcs_decode_workspace_bytes(model, trie, docs) bytes (0: invalid arguments).
+ * Runs max_decode_steps steps on `stream` with no host synchronisation; documents
+ * that are decided early skip the later steps' work.
+ * Outputs (device): label [B]; runs [B] (may be NULL): model runs per document.
+ * Errors as tcs_classify_run; TCS_EINVAL without the decoding arrays;
+ * TCS_EUNSUPPORTED for bf16 models with head_dim other than 128.
+ */
+size_t tcs_decode_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
+                                  const tcs_docs* docs);
+int tcs_decode_run(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* trie,
+                   const tcs_docs* docs, const tcs_prepared* prep, int32_t* label, int32_t* runs,
+                   void* ws, size_t ws_bytes);
 
 /* ----------------------------------------------------------- measurement ---- */
 /*

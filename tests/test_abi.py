@@ -209,3 +209,68 @@ def test_letters_rejects_deeper_tries_without_gpu():
     rc = lib.tcs_letters_run(None, C.byref(model), C.byref(dev), C.byref(docs), None, None, None,
                              None, None, 0)
     assert rc == tcs.TCS_EINVAL and b"one-token" in lib.tcs_last_error()
+
+
+# ------------------------------------------------------------ greedy-decoding tables
+
+def assert_decode_tables(labels, t):
+    """sub_label, dec_node and max_decode_steps against their definitions, with each
+    node named by its token path."""
+    labels = [tuple(l) for l in labels]
+    below = {}
+    for m, l in enumerate(labels):
+        for k in range(len(l) + 1):
+            below.setdefault(l[:k], []).append(m)
+    path = [()] * t.n_nodes
+    for u in range(1, t.n_nodes):
+        path[u] = path[t.parent[u]] + (int(t.token[u]),)
+    for u in range(t.n_nodes):
+        ms = below[path[u]]
+        assert t.sub_label[u] == (ms[0] if len(ms) == 1 else -1), u
+        w = u
+        while t.child_count[w] == 1 and len(below[path[w]]) > 1:
+            w = t.child_begin[w]
+        assert t.dec_node[u] == w, u
+    most = 0
+    for m, l in enumerate(labels):
+        if any(l2[:len(l)] == l and len(l2) > len(l) for l2 in labels):
+            continue  # never returned by greedy decoding
+        most = max(most, O.greedy_walk(labels, lambda p, c, l=l: l[len(p)])[1])
+    assert t.max_decode_steps == most
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_decode_tables_on_configs(cid):
+    inp = make_inputs(config(cid), weights=False)
+    t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], config(cid).V)
+    assert_decode_tables(inp["labels"], t)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.lists(st.integers(0, 5), min_size=1, max_size=6), min_size=1, max_size=25,
+                unique_by=tuple))
+def test_decode_tables_random(raw):
+    offs, toks = labels_to_csr(raw)
+    assert_decode_tables(raw, tcs.trie_build(offs, toks, 0, 8))
+
+
+def test_decode_run_errors_without_gpu():
+    lib = tcs.lib()
+    assert lib.tcs_decode_run(None, None, None, None, None, None, None, None, 0) == tcs.TCS_EINVAL
+    t = tcs.trie_build(*labels_to_csr([[3], [4, 5]]), 0, 16)
+    fake = 256
+    arrays = {n: fake for n in tcs.TRIE_DEV_ARRAYS}
+    arrays["dec_node"] = None
+    dev = tcs.tcs_trie_dev(n_nodes=t.n_nodes, n_int=t.n_int, n_labels=t.n_labels,
+                           max_depth=t.max_depth, max_decode_steps=t.max_decode_steps, **arrays)
+    model = tcs.tcs_model(dtype=tcs.TCS_BF16, head_dtype=tcs.TCS_BF16, d=128, Hq=2, Hkv=1, hd=128,
+                          V=16, eps=1e-6, E=fake, Wq=fake, Wk=fake, Wv=fake, Wo=fake, W=fake)
+    docs = tcs.tcs_docs(B=1, total_tokens=4, doc_offsets=fake, Kd=fake, Vd=fake)
+    assert lib.tcs_decode_workspace_bytes(C.byref(model), C.byref(dev), C.byref(docs)) == 0
+    rc = lib.tcs_decode_run(None, C.byref(model), C.byref(dev), C.byref(docs), None, None, None,
+                            None, 0)
+    assert rc == tcs.TCS_EINVAL and b"dec_node" in lib.tcs_last_error()
+    dev.dec_node = fake
+    model.hd, model.Hq = 64, 4
+    assert lib.tcs_decode_run(None, C.byref(model), C.byref(dev), C.byref(docs), None, None, None,
+                              None, 0) == tcs.TCS_EUNSUPPORTED

@@ -41,16 +41,19 @@ class tcs_trie(C.Structure):
                 ("max_depth", C.c_int32)] + [(n, P32) for n in (
                     "parent", "token", "depth", "child_begin", "child_count", "node_label", "qrow",
                     "qnode", "qparent", "label_node", "level_offsets", "e_tok", "e_qrow", "e_child",
-                    "row_level_offsets", "label_row")]
+                    "row_level_offsets", "label_row", "sub_label", "dec_node")] + [
+                ("max_decode_steps", C.c_int32)]
 
 
 TRIE_DEV_ARRAYS = ("parent", "token", "child_begin", "child_count", "qnode", "qparent", "label_node",
-                   "e_tok", "e_qrow", "e_child", "qrow", "row_level_offsets", "label_row")
+                   "e_tok", "e_qrow", "e_child", "qrow", "row_level_offsets", "label_row", "sub_label",
+                   "dec_node")
 
 
 class tcs_trie_dev(C.Structure):
     _fields_ = [("n_nodes", C.c_int32), ("n_int", C.c_int32), ("n_labels", C.c_int32),
-                ("max_depth", C.c_int32)] + [(n, C.c_void_p) for n in TRIE_DEV_ARRAYS]
+                ("max_depth", C.c_int32)] + [(n, C.c_void_p) for n in TRIE_DEV_ARRAYS] + [
+                ("max_decode_steps", C.c_int32)]
 
 
 class tcs_model(C.Structure):
@@ -110,6 +113,11 @@ def lib():
         L.tcs_classify_run.argtypes = [vp, C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
                                        C.POINTER(tcs_docs), C.POINTER(tcs_prepared), vp, vp, vp, vp, sz]
         L.tcs_letters_run.argtypes = list(L.tcs_classify_run.argtypes)
+        L.tcs_decode_workspace_bytes.restype = sz
+        L.tcs_decode_workspace_bytes.argtypes = [C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
+                                                 C.POINTER(tcs_docs)]
+        L.tcs_decode_run.argtypes = [vp, C.POINTER(tcs_model), C.POINTER(tcs_trie_dev),
+                                     C.POINTER(tcs_docs), C.POINTER(tcs_prepared), vp, vp, vp, sz]
         L.tcs_timing_enable.argtypes = [C.c_int]
         L.tcs_timing_read.argtypes = [C.c_int, C.POINTER(C.c_double), C.POINTER(i32)]
         _lib_handle = L
@@ -203,6 +211,7 @@ class Trie:
     n_labels: int
     max_depth: int
     arrays: dict
+    max_decode_steps: int = 0
 
     def __getattr__(self, k):
         a = self.__dict__.get("arrays")
@@ -221,7 +230,7 @@ def trie_build(label_offsets, label_tokens, root_token: int, V: int) -> Trie:
     for _ in range(2):
         arrays = {n: np.zeros(cap, dtype=np.int32) for n in (
             "parent", "token", "depth", "child_begin", "child_count", "node_label", "qrow", "qnode",
-            "qparent", "e_tok", "e_qrow", "e_child")}
+            "qparent", "e_tok", "e_qrow", "e_child", "sub_label", "dec_node")}
         arrays["label_node"] = np.zeros(max(M, 1), dtype=np.int32)
         arrays["label_row"] = np.zeros(max(M, 1), dtype=np.int32)
         arrays["level_offsets"] = np.zeros(cap + 1, dtype=np.int32)
@@ -239,7 +248,7 @@ def trie_build(label_offsets, label_tokens, root_token: int, V: int) -> Trie:
         cut = {"qnode": n_int, "qparent": n_int, "e_tok": N - 1, "e_qrow": N - 1, "e_child": N - 1,
                "label_node": M, "label_row": M, "level_offsets": D + 2, "row_level_offsets": D + 2}
         out = {n: a[:cut.get(n, N)].copy() for n, a in arrays.items()}
-        return Trie(N, n_int, M, D, out)
+        return Trie(N, n_int, M, D, out, int(t.max_decode_steps))
     raise TcsError(TCS_ECAPACITY, "trie capacity")
 
 
@@ -275,7 +284,7 @@ class TrieDevice:
         self.tensors = {n: torch.from_numpy(np.ascontiguousarray(trie.arrays[n])).to(device)
                         for n in TRIE_DEV_ARRAYS}
         self.struct = tcs_trie_dev(n_nodes=trie.n_nodes, n_int=trie.n_int, n_labels=trie.n_labels,
-                                   max_depth=trie.max_depth,
+                                   max_depth=trie.max_depth, max_decode_steps=trie.max_decode_steps,
                                    **{n: self.tensors[n].data_ptr() for n in TRIE_DEV_ARRAYS})
 
     def __getitem__(self, k):
@@ -506,3 +515,34 @@ def letters(model: Model, trie_dev: TrieDevice, docs: Docs, prepared: Prepared, 
                                  C.byref(docs.struct), C.byref(prepared.struct), _ptr(label),
                                  _ptr(prob), _ptr(ll), _ptr(ws), ws.numel()))
     return label, prob, ll
+
+
+def decode_workspace_bytes(model: Model, trie_dev: TrieDevice, docs: Docs) -> int:
+    n = int(lib().tcs_decode_workspace_bytes(C.byref(model.struct), C.byref(trie_dev.struct),
+                                             C.byref(docs.struct)))
+    if n == 0:
+        _check(TCS_EINVAL)
+    return n
+
+
+def trie_decode(model: Model, trie_dev: TrieDevice, docs: Docs, prepared: Prepared, label=None,
+                runs=None, ws=None, stream=None):
+    """trie_decode (tcs_decode_run): greedy generation inside the label trie, the
+    model run only where labels branch.  Returns (label [B], runs [B])."""
+    torch = _torch()
+    B = docs.B
+    dev = docs.offsets.device
+    if label is None:
+        label = torch.empty(B, dtype=torch.int32, device=dev)
+    if runs is None:
+        runs = torch.empty(B, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(decode_workspace_bytes(model, trie_dev, docs), dtype=torch.uint8, device=dev)
+    _need_cuda(label, runs, ws)
+    if stream is not None:
+        for x in (label, runs, ws):
+            x.record_stream(stream)
+    _check(lib().tcs_decode_run(_stream(stream), C.byref(model.struct), C.byref(trie_dev.struct),
+                                C.byref(docs.struct), C.byref(prepared.struct), _ptr(label),
+                                _ptr(runs), _ptr(ws), ws.numel()))
+    return label, runs

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libtcs.so")
 ARCH = "gfx950"
 
 SOURCES = ["trie_build.cpp", "tcs_api.hip", "k_gemm.hip", "k_lmhead.hip", "k_attn.hip", "k_path.hip",
-           "k_letters.hip", "timing.hip"]
+           "k_letters.hip", "k_decode.hip", "timing.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(
     int B, int n_int, int Hq, int Hkv, const T* __restrict__ Qn, const T* __restrict__ Kn,
     const T* __restrict__ Vn, const T* __restrict__ Kd, const T* __restrict__ Vd,
     const int32_t* __restrict__ doc_offsets, const int32_t* __restrict__ qparent, float scale,
-    T* __restrict__ O) {
+    T* __restrict__ O, const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel) {
   constexpr int E = HD / 64;
   const int lane = threadIdx.x & 63;
   const long gw = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -42,10 +42,17 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(
   const int r = int((gw / Hq) % n_int);
   const int b = int(gw / (long(Hq) * n_int));
   const int g = h / (Hq / Hkv);
+  // with sel: slot b scores document sel[2b] at query row sel[2b+1] (n_int is 1)
+  int doc = b, rr = r;
+  if (sel) {
+    if (b >= *n_sel) return;
+    doc = sel[2 * b];
+    rr = sel[2 * b + 1];
+  }
   float q[E], o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    q[e] = to_f32(Qn[((size_t)r * Hq + h) * HD + lane * E + e]);
+    q[e] = to_f32(Qn[((size_t)rr * Hq + h) * HD + lane * E + e]);
     o[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -61,9 +68,9 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(
     for (int e = 0; e < E; ++e) o[e] = o[e] * c + p * to_f32(v[lane * E + e]);
     m = mn;
   };
-  for (int j = doc_offsets[b]; j < doc_offsets[b + 1]; ++j)
+  for (int j = doc_offsets[doc]; j < doc_offsets[doc + 1]; ++j)
     visit(Kd + ((size_t)j * Hkv + g) * HD, Vd + ((size_t)j * Hkv + g) * HD);
-  for (int w = r, steps = 0; w >= 0 && steps <= r; w = qparent[w], ++steps)
+  for (int w = rr, steps = 0; w >= 0 && steps <= rr; w = qparent[w], ++steps)
     visit(Kn + ((size_t)w * Hkv + g) * HD, Vn + ((size_t)w * Hkv + g) * HD);
   const float inv = 1.0f / l;
 #pragma unroll
@@ -444,7 +451,7 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn, const uint16_t* __restrict__ Kd,
     const uint16_t* __restrict__ Vd, const int32_t* __restrict__ doc_offsets,
     const float2* __restrict__ anc_ml, const float* __restrict__ anc_o, float scale,
-    uint16_t* __restrict__ O) {
+    uint16_t* __restrict__ O, const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel) {
   static_assert(HD == 128, "256-byte key rows: 16 chunks, one per swizzle position");
   constexpr int KB = 32;                 // keys per stage
   constexpr int ROW = HD * 2;            // bytes per key row
@@ -465,11 +472,19 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   const int Bn = int(gridDim.x) / (n_rb * Hkv);
   const int b = blockIdx.x % Bn, rest = blockIdx.x / Bn;
   const int rb = rest % n_rb, g = rest / n_rb;
+  // with sel: slot b scores document sel[2b] with the queries and path partials of
+  // row sel[2b+1] (n_int is 1); slots from *n_sel on have nothing to do
+  int doc = b, rq = 0;
+  if (sel) {
+    if (b >= *n_sel) return;
+    doc = sel[2 * b];
+    rq = sel[2 * b + 1];
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = rb * 32;
-  const int doc0 = doc_offsets[b];
-  const int L = doc_offsets[b + 1] - doc0;
+  const int doc0 = doc_offsets[doc];
+  const int L = doc_offsets[doc + 1] - doc0;
   const int RS = Hkv * HD * 2;           // bytes between consecutive keys of one head
   uint8_t* const ring = lds + wave * WAVE_BYTES;
 
@@ -485,7 +500,7 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     const int j = j0 + (lane & 31);
     const bool ok = j < rows_total;
     const int r = ok ? j / G : 0, h = g * G + (ok ? j % G : 0);
-    const uint16_t* qp = Qn + ((size_t)r * Hq + h) * HD + 8 * (lane >> 5);
+    const uint16_t* qp = Qn + ((size_t)(rq + r) * Hq + h) * HD + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : uint4{0, 0, 0, 0};
@@ -656,11 +671,11 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     const int j = j0 + row;
     if (j < rows_total) {
       const int r = j / G, h = g * G + j % G;
-      const float4* ao = reinterpret_cast<const float4*>(anc_o + ((size_t)r * Hq + h) * HD + h0);
+      const float4* ao = reinterpret_cast<const float4*>(anc_o + ((size_t)(rq + r) * Hq + h) * HD + h0);
       float4 av[SEG / 4];
 #pragma unroll
       for (int i = 0; i < SEG / 4; ++i) av[i] = ao[i];
-      const float2 a = anc_ml[(size_t)r * Hq + h];
+      const float2 a = anc_ml[(size_t)(rq + r) * Hq + h];
       float M = -INFINITY;
 #pragma unroll
       for (int k = 0; k < 4; ++k) M = fmaxf(M, sml[(k * 32 + row) * 2]);
@@ -1207,10 +1222,12 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
 int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
                     int32_t hd, const void* Qn, const void* Kd, const void* Vd,
                     const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
-                    float scale, void* O) {
+                    float scale, void* O, const int32_t* sel, const int32_t* n_sel) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || n_int == 0) return TCS_OK;
   if (dt != TCS_BF16) return fail(TCS_EUNSUPPORTED, "doc_attn: MFMA path is bf16 only");
+  if (sel && (n_int != 1 || hd != 128 || Hq / Hkv > 64))
+    return fail(TCS_EUNSUPPORTED, "doc_attn: row selection needs one row, head_dim 128, <= 64 rows");
   const int G = Hq / Hkv;
   const long rows = long(n_int) * G;
   const float2* ml = reinterpret_cast<const float2*>(anc_ml);
@@ -1222,7 +1239,7 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
   if (rows <= 64) {
     const long grid = long(B) * Hkv * ((rows + 31) / 32);
     if (hd == 128)
-      doc_attn_stream_kernel<128, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
+      doc_attn_stream_kernel<128, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o, sel, n_sel);
     else
       doc_attn_mfma_kernel<64, 1, 4><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   } else {
@@ -1247,8 +1264,9 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
 int launch_attn_simt(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
                      int32_t hd, const void* Qn, const void* Kn, const void* Vn, const void* Kd,
                      const void* Vd, const int32_t* doc_offsets, const int32_t* qparent, float scale,
-                     void* O) {
+                     void* O, const int32_t* sel, const int32_t* n_sel) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sel && n_int != 1) return fail(TCS_EUNSUPPORTED, "attn_simt: row selection needs n_int = 1");
   const long waves = long(B) * n_int * Hq;
   if (waves == 0) return TCS_OK;
   const int grid = int((waves + 3) / 4);
@@ -1256,7 +1274,7 @@ int launch_attn_simt(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32
   attn_simt_kernel<T, HDV><<<grid, 256, 0, s>>>(                                                   \
       B, n_int, Hq, Hkv, static_cast<const T*>(Qn), static_cast<const T*>(Kn),                     \
       static_cast<const T*>(Vn), static_cast<const T*>(Kd), static_cast<const T*>(Vd), doc_offsets, \
-      qparent, scale, static_cast<T*>(O))
+      qparent, scale, static_cast<T*>(O), sel, n_sel)
   if (dt == TCS_BF16) {
     if (hd == 128) TCS_SIMT(bf16_t, 128); else TCS_SIMT(bf16_t, 64);
   } else {

@@ -17,9 +17,7 @@ namespace {
 // One wave per letter: child c = 1 + 4 blockIdx.x + wave of the root.  The wave
 // walks documents b = blockIdx.y, blockIdx.y + gridDim.y, ... and writes
 // lp[b][c] = h[b's root row] . W[token[c]] (times the row scale for fp8 W), the
-// fp32 partial products summed over the wave.  bf16 hidden states: each lane takes
-// 4 consecutive elements per step (d % 4 == 0, so every row is 8-byte aligned).
-// WK: 0 = fp32 h and W, 1 = bf16 h and W, 2 = bf16 h and E4M3 W.
+// fp32 partial products summed over the wave.
 template <int WK>
 __global__ __launch_bounds__(256) void letter_logits_kernel(
     int B, int n_int, int n_nodes, int d, const void* __restrict__ h, const void* __restrict__ W,
@@ -29,43 +27,11 @@ __global__ __launch_bounds__(256) void letter_logits_kernel(
   if (c >= n_nodes) return;  // whole wave
   const int tok = token[c];
   const float sc = WK == 2 ? w_scale[tok] : 1.0f;
+  const size_t es = WK == 0 ? 4 : 2;
   for (int b = blockIdx.y; b < B; b += gridDim.y) {
-    const size_t hrow = size_t(b) * n_int * d;  // row 0 of document b is the root's
-    float acc = 0.f;
-    if constexpr (WK == 0) {
-      const float* hr = static_cast<const float*>(h) + hrow;
-      const float* wr = static_cast<const float*>(W) + size_t(tok) * d;
-      for (int k = lane; k < d; k += 64) acc = fmaf(hr[k], wr[k], acc);
-    } else {
-      const uint2* hr = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(h) + hrow);
-      for (int k4 = lane; k4 < d / 4; k4 += 64) {
-        const uint2 hv = hr[k4];
-        float w[4];
-        if constexpr (WK == 1) {
-          const uint2 wv = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(W) +
-                                                          size_t(tok) * d)[k4];
-          w[0] = bf16_to_f32(uint16_t(wv.x));
-          w[1] = bf16_to_f32(uint16_t(wv.x >> 16));
-          w[2] = bf16_to_f32(uint16_t(wv.y));
-          w[3] = bf16_to_f32(uint16_t(wv.y >> 16));
-        } else {
-          // four E4M3 codes -> bf16 (hardware conversion at scale 1, exact)
-          const uint32_t wv = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(W) +
-                                                                size_t(tok) * d)[k4];
-          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv, 1.0f, false);
-          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv, 1.0f, true);
-          w[0] = float(lo[0]);
-          w[1] = float(lo[1]);
-          w[2] = float(hi[0]);
-          w[3] = float(hi[1]);
-        }
-        acc = fmaf(bf16_to_f32(uint16_t(hv.x)), w[0], acc);
-        acc = fmaf(bf16_to_f32(uint16_t(hv.x >> 16)), w[1], acc);
-        acc = fmaf(bf16_to_f32(uint16_t(hv.y)), w[2], acc);
-        acc = fmaf(bf16_to_f32(uint16_t(hv.y >> 16)), w[3], acc);
-      }
-    }
-    acc = wave_sum(acc);
+    // row 0 of document b is the root's
+    const void* hr = static_cast<const char*>(h) + size_t(b) * n_int * d * es;
+    const float acc = wave_sum(head_row_dot_lane<WK>(hr, W, tok, d, lane));
     if (lane == 0) {
       lp[size_t(b) * n_nodes + c] = acc * sc;
       if (c == 1) lp[size_t(b) * n_nodes] = 0.f;  // the root has no edge

@@ -25,7 +25,7 @@ void clear_error() { g_err[0] = 0; }
 int launch_attn_simt(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
                      int32_t hd, const void* Qn, const void* Kn, const void* Vn, const void* Kd,
                      const void* Vd, const int32_t* doc_offsets, const int32_t* qparent, float scale,
-                     void* O);
+                     void* O, const int32_t* sel = nullptr, const int32_t* n_sel = nullptr);
 
 static int check_attn_dims(tcs_dtype dt, int32_t Hq, int32_t Hkv, int32_t hd) {
   if (dt != TCS_F32 && dt != TCS_BF16) return fail(TCS_EUNSUPPORTED, "dtype %d not supported", int(dt));
@@ -364,6 +364,122 @@ int tcs_letters_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t
   const size_t need = run_layout(m, t, d, nullptr).total;
   if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "letters: workspace %zu < %zu bytes", ws_bytes, need);
   return run_impl(stream, m, t, d, prep->buf, label, prob, ll, ws, true);
+}
+
+// ---------------------------------------------------------------- trie_decode
+
+// Per-batch workspace of tcs_decode_run: document K/V (token documents), then per
+// slot the attention output, projection partials and hidden state, and the
+// per-document decoding state.
+struct DecodeLayout {
+  size_t total;
+  void *a_doc, *Kd, *Vd, *O, *h;
+  float* y;
+  int32_t *cur, *sel, *row_node, *n_sel, *runs;
+};
+
+static DecodeLayout decode_layout(const tcs_model* m, const tcs_docs* d, void* ws) {
+  const size_t es = dtype_bytes(m->dtype);
+  const size_t B = d->B > 0 ? d->B : 1;
+  const size_t qd = size_t(m->Hq) * m->hd, kd = size_t(m->Hkv) * m->hd;
+  Carve c(ws);
+  DecodeLayout L{};
+  if (!d->Kd) {
+    const size_t T = d->total_tokens;
+    L.a_doc = c.take<char>(T * m->d * es);
+    L.Kd = c.take<char>(T * kd * es);
+    L.Vd = c.take<char>(T * kd * es);
+  }
+  L.O = c.take<char>(B * qd * es);
+  L.y = c.take<float>(B * m->d * gemm_resid_splits(m->dtype, int32_t(B), m->d, int32_t(qd)));
+  L.h = c.take<char>(B * m->d * es);
+  L.cur = c.take<int32_t>(B);
+  L.sel = c.take<int32_t>(2 * B);
+  L.row_node = c.take<int32_t>(B);
+  L.n_sel = c.take<int32_t>(1);
+  L.runs = c.take<int32_t>(B);
+  L.total = c.used;
+  return L;
+}
+
+static int check_decode(const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d) {
+  if (int rc = check_classify(m, t, d)) return rc;
+  if (!t->sub_label || !t->dec_node || !t->qrow)
+    return fail(TCS_EINVAL, "decode: the trie needs its qrow, sub_label and dec_node arrays");
+  if (t->max_decode_steps < 0 || t->max_decode_steps > t->max_depth)
+    return fail(TCS_EINVAL, "decode: max_decode_steps %d outside [0, %d]", t->max_decode_steps,
+                t->max_depth);
+  if (m->dtype == TCS_BF16 && (m->hd != 128 || m->Hq / m->Hkv > 64))
+    return fail(TCS_EUNSUPPORTED, "decode: bf16 models need head_dim 128 (hd=%d)", m->hd);
+  return TCS_OK;
+}
+
+size_t tcs_decode_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,
+                                  const tcs_docs* docs) {
+  if (check_decode(model, trie, docs)) return 0;
+  return decode_layout(model, docs, nullptr).total;
+}
+
+int tcs_decode_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d,
+                   const tcs_prepared* prep, int32_t* label, int32_t* runs, void* ws,
+                   size_t ws_bytes) {
+  clear_error();
+  if (int rc = check_decode(m, t, d)) return rc;
+  if (d->B == 0) return TCS_OK;
+  if (!label) return fail(TCS_EINVAL, "decode: null label output");
+  if (!prep || !prep->buf) return fail(TCS_EINVAL, "decode: null prepared state");
+  if (prep->B != d->B)
+    return fail(TCS_EINVAL, "decode: state prepared for B=%d, batch has B=%d", prep->B, d->B);
+  if (prep->bytes < prep_layout(m, t, d->B, nullptr).total)
+    return fail(TCS_ECAPACITY, "decode: prepared buffer too small");
+  const size_t need = decode_layout(m, d, nullptr).total;
+  if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "decode: workspace %zu < %zu bytes", ws_bytes, need);
+
+  const PrepLayout P = prep_layout(m, t, d->B, const_cast<void*>(prep->buf));
+  const DecodeLayout L = decode_layout(m, d, ws);
+  const tcs_dtype dt = m->dtype;
+  const int B = d->B, qd = m->Hq * m->hd, kd = m->Hkv * m->hd;
+  const float scale = 1.0f / std::sqrt(float(m->hd));
+  int32_t* const nruns = runs ? runs : L.runs;
+  int rc;
+  const void* Kd = d->Kd;
+  const void* Vd = d->Vd;
+  if (!Kd) {  // documents given as tokens: their k and v through the same input block
+    const int T = d->total_tokens;
+    if ((rc = launch_embed_rmsnorm(stream, dt, m->E, d->doc_tokens, nullptr, T, m->d, m->V, m->eps, L.a_doc))) return rc;
+    if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, T, kd, m->d, L.a_doc, m->d, m->Wk, m->d, L.Kd, kd, nullptr))) return rc;
+    if ((rc = launch_gemm_nt(stream, dt, GEMM_STORE, T, kd, m->d, L.a_doc, m->d, m->Wv, m->d, L.Vd, kd, nullptr))) return rc;
+    Kd = L.Kd;
+    Vd = L.Vd;
+  }
+  if ((rc = launch_decode_init(stream, B, t->dec_node, t->sub_label, t->qrow, L.cur, label, nruns,
+                               L.sel, L.row_node, L.n_sel))) return rc;
+  const GemmResid res{m->E, t->token, L.row_node, B};
+  const int splits = gemm_resid_splits(dt, B, m->d, qd);
+  for (int step = 0; step < t->max_decode_steps; ++step) {
+    // one answer position per undecided document: its node's queries over the
+    // document, merged with the node's own path
+    if (dt == TCS_F32) {
+      rc = launch_attn_simt(stream, dt, B, 1, m->Hq, m->Hkv, m->hd, P.Qn, P.Kn, P.Vn, Kd, Vd,
+                            d->doc_offsets, t->qparent, scale, L.O, L.sel, L.n_sel);
+    } else {
+      Carve c(P.anc);
+      const float* ml = c.take<float>(size_t(t->n_int) * m->Hq * 2);
+      const float* ao = c.take<float>(size_t(t->n_int) * m->Hq * m->hd);
+      rc = launch_doc_attn(stream, dt, B, 1, m->Hq, m->Hkv, m->hd, P.Qn, Kd, Vd, d->doc_offsets,
+                           ml, ao, scale, L.O, L.sel, L.n_sel);
+    }
+    if (rc) return rc;
+    if ((rc = launch_gemm_nt(stream, dt, GEMM_RESID, B, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d,
+                             &res))) return rc;
+    if ((rc = launch_rownorm(stream, dt, L.y, B, m->d, splits, m->eps, L.h))) return rc;
+    if ((rc = launch_decode_step(stream, dt, m->head_dtype, B, m->d, L.h, m->W, m->W_scale,
+                                 t->token, t->child_begin, t->child_count, t->dec_node,
+                                 t->sub_label, L.sel, L.row_node, L.n_sel, L.cur, label,
+                                 nruns))) return rc;
+    if ((rc = launch_decode_compact(stream, B, L.cur, t->qrow, L.sel, L.row_node, L.n_sel))) return rc;
+  }
+  return TCS_OK;
 }
 
 size_t tcs_classify_workspace_bytes(const tcs_model* model, const tcs_trie_dev* trie,

@@ -89,6 +89,52 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// One lane's share of the dot product of a hidden row with head row `tok` of W
+// (restricted heads: a few vocabulary rows, no log-sum-exp); summing over the 64
+// lanes of the wave gives the product, before an fp8 row scale.  WK: 0 = fp32 h
+// and W; 1 = bf16 h and W; 2 = bf16 h and E4M3 W.  bf16 rows: each lane takes 4
+// consecutive elements per step, so d % 4 == 0 keeps every row 8-byte aligned.
+template <int WK>
+__device__ __forceinline__ float head_row_dot_lane(const void* __restrict__ h_row,
+                                                   const void* __restrict__ W, int tok, int d,
+                                                   int lane) {
+  float acc = 0.f;
+  if constexpr (WK == 0) {
+    const float* hr = static_cast<const float*>(h_row);
+    const float* wr = static_cast<const float*>(W) + size_t(tok) * d;
+    for (int k = lane; k < d; k += 64) acc = fmaf(hr[k], wr[k], acc);
+  } else {
+    const uint2* hr = static_cast<const uint2*>(h_row);
+    for (int k4 = lane; k4 < d / 4; k4 += 64) {
+      const uint2 hv = hr[k4];
+      float w[4];
+      if constexpr (WK == 1) {
+        const uint2 wv =
+            reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(W) + size_t(tok) * d)[k4];
+        w[0] = bf16_to_f32(uint16_t(wv.x));
+        w[1] = bf16_to_f32(uint16_t(wv.x >> 16));
+        w[2] = bf16_to_f32(uint16_t(wv.y));
+        w[3] = bf16_to_f32(uint16_t(wv.y >> 16));
+      } else {
+        // four E4M3 codes -> bf16 (hardware conversion at scale 1, exact)
+        const uint32_t wv =
+            reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(W) + size_t(tok) * d)[k4];
+        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv, 1.0f, false);
+        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv, 1.0f, true);
+        w[0] = float(lo[0]);
+        w[1] = float(lo[1]);
+        w[2] = float(hi[0]);
+        w[3] = float(hi[1]);
+      }
+      acc = fmaf(bf16_to_f32(uint16_t(hv.x)), w[0], acc);
+      acc = fmaf(bf16_to_f32(uint16_t(hv.x >> 16)), w[1], acc);
+      acc = fmaf(bf16_to_f32(uint16_t(hv.y)), w[2], acc);
+      acc = fmaf(bf16_to_f32(uint16_t(hv.y >> 16)), w[3], acc);
+    }
+  }
+  return acc;
+}
+
 // (max, sum-of-exp) merge of two softmax partials.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);

@@ -105,6 +105,19 @@ int launch_letter_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int
                          int32_t n_int, int32_t n_nodes, int32_t d, const void* h, const void* W,
                          const float* w_scale, const int32_t* token, float* lp);
 
+// Greedy decoding in the trie (per-document state on the device).
+int launch_decode_init(void* stream, int32_t B, const int32_t* dec_node, const int32_t* sub_label,
+                       const int32_t* qrow, int32_t* cur, int32_t* label, int32_t* runs,
+                       int32_t* sel, int32_t* row_node, int32_t* n_sel);
+int launch_decode_step(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t d,
+                       const void* h, const void* W, const float* w_scale, const int32_t* token,
+                       const int32_t* child_begin, const int32_t* child_count,
+                       const int32_t* dec_node, const int32_t* sub_label, const int32_t* sel,
+                       const int32_t* row_node, const int32_t* n_sel, int32_t* cur, int32_t* label,
+                       int32_t* runs);
+int launch_decode_compact(void* stream, int32_t B, const int32_t* cur, const int32_t* qrow,
+                          int32_t* sel, int32_t* row_node, int32_t* n_sel);
+
 // Tree attention pieces.
 int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32_t Hkv,
                     int32_t hd, const void* Qn, const void* Kn, const void* Vn,
@@ -112,7 +125,8 @@ int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32
 int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq,
                     int32_t Hkv, int32_t hd, const void* Qn, const void* Kd, const void* Vd,
                     const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
-                    float scale, void* O);
+                    float scale, void* O, const int32_t* sel = nullptr,
+                    const int32_t* n_sel = nullptr);
 
 // Path sums, label softmax and argmax.  lp: edge log-probs [B, n_nodes]; or, with
 // lse and node_qrow set, the raw child logits, each edge's log-prob being

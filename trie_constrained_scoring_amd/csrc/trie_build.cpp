@@ -191,6 +191,43 @@ extern "C" int tcs_trie_build(const int32_t* label_offsets, const int32_t* label
       out->label_row[m] = out->child_count[u] > 0 ? out->qrow[u] : out->qrow[out->parent[u]];
     }
   }
+  // greedy-decoding tables: labels per subtree, bottom-up (children have larger ids)
+  if (out->sub_label && out->dec_node) {
+    std::vector<int32_t> count(N, 0);
+    for (int32_t c = N - 1; c >= 0; --c) {
+      count[c] += out->node_label[c] >= 0;
+      int32_t one = out->node_label[c];
+      for (int32_t k = 0; k < out->child_count[c]; ++k) {
+        const int32_t ch = out->child_begin[c] + k;
+        if (count[ch] > 0 && one < 0) one = out->sub_label[ch];
+        count[c] += count[ch];
+      }
+      out->sub_label[c] = count[c] == 1 ? one : -1;
+    }
+    for (int32_t c = 0; c < N; ++c) {
+      int32_t w = c;
+      while (out->child_count[w] == 1 && out->sub_label[w] < 0) w = out->child_begin[w];
+      out->dec_node[c] = w;
+    }
+    // model runs on the way to each label: the undecided nodes decoding stops at.  A
+    // label that ends above such a node (the start of another label) is never
+    // reached; its count stops there.
+    int32_t most = 0;
+    for (int32_t m = 0; m < M; ++m) {
+      const int32_t lab = out->label_node[m];
+      int32_t runs = 0;
+      for (int32_t w = out->dec_node[0]; out->sub_label[w] < 0;) {
+        if (out->depth[lab] <= out->depth[w]) break;
+        int32_t v = lab;  // the child of w on the label's path
+        while (out->depth[v] > out->depth[w] + 1) v = out->parent[v];
+        if (out->parent[v] != w) break;
+        ++runs;
+        w = out->dec_node[v];
+      }
+      most = std::max(most, runs);
+    }
+    out->max_decode_steps = most;
+  }
   return TCS_OK;
 }
 
