@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
                     [--no-cpu-baseline] [--no-path-stress] [--no-decision-word] [--no-letters]
+                    [--no-decode]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
     python bench.py --head-probe --config 3 [--power]  # head alone: workload-like vs constant
                                                        # operands (+ socket power and clocks)
@@ -26,7 +27,9 @@ it against HBM).  ``decision_word`` runs the same documents and weights with eve
 label cut to the end of the word where it leaves the others (the decision-word form
 of trie_tree: fewer query rows, same kernels); the headline scores every label over
 its full root-to-leaf path.  ``letters`` runs them under the letters method (one
-answer position per document, only the letter rows of the head).  ``roofline`` is for the
+answer position per document, only the letter rows of the head), ``trie_decode`` under
+greedy decoding in the trie (one answer position per undecided document per step).
+``roofline`` is for the
 dominant kernel (the output head): after the timed steps, the same steps run
 again with the head launches bracketed by HIP events on the stream they run on
 (the library's tcs_timing_enable hook), and achieved = algorithmic FLOP per
@@ -175,6 +178,9 @@ def run_steps(S, steps, warmup):
         if S.get("letters"):
             tcs.letters(S["model"], S["td"], S["docs"], S["prep"], ws=S["ws"][k], stream=streams[k],
                         **S["out"][k])
+        elif S.get("decode"):
+            tcs.trie_decode(S["model"], S["td"], S["docs"], S["prep"], ws=S["ws"][k],
+                            stream=streams[k], **S["out"][k])
         else:
             tcs.classify(S["model"], S["td"], S["docs"], ws=S["ws"][k], prepared=S["prep"],
                          stream=streams[k], **S["out"][k])
@@ -263,6 +269,39 @@ def letters_measure(S, steps, warmup, streams):
         e["doc_attn_roofline"] = doc_attn_roofline(C, kern["doc_attn"])
         e["doc_attn_share_of_step"] = round(kern["doc_attn"] / (sec * 1e3), 4)
     del C, prep, ws, out, td
+    torch.cuda.empty_cache()
+    return e
+
+
+def decode_measure(S, steps, warmup, streams):
+    """The same documents, weights and trie under trie_decode (tcs_decode_run): greedy
+    generation, one answer position per undecided document per step.  The document
+    attention re-reads a document's K/V at every step it takes part in; its HBM
+    figure counts those bytes (sum over documents of runs x K/V bytes) against the
+    summed duration of the step launches."""
+    import torch
+    import trie_constrained_scoring_amd as tcs
+    cfg, inp, docs = S["cfg"], S["inp"], S["docs"]
+    B = docs.B
+    nbytes = tcs.decode_workspace_bytes(S["model"], S["td"], docs)
+    ws = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(max(1, streams))]
+    out = [dict(label=torch.empty(B, dtype=torch.int32, device="cuda"),
+                runs=torch.empty(B, dtype=torch.int32, device="cuda")) for _ in ws]
+    C = dict(S, ws=ws, out=out, decode=True)
+    sec, kern = run_steps(C, steps, warmup)
+    runs = out[0]["runs"].cpu().numpy().astype(np.int64)
+    n_steps = S["td"].trie.max_decode_steps
+    e = {"config": cfg.id, "docs_per_s": round(B / sec, 2), "ms_per_step": round(sec * 1e3, 4),
+         "mean_model_runs_per_doc": round(float(runs.mean()), 4), "decode_steps": n_steps}
+    if kern["doc_attn"] and n_steps:
+        lens = np.diff(np.asarray(inp["doc_offsets"], dtype=np.int64))
+        by = int((runs * lens).sum()) * 2 * cfg.Hkv * cfg.hd * 2
+        ms = kern["doc_attn"] * n_steps
+        gbs = by / (ms * 1e-3) / 1e9
+        e["doc_attn_roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                  "bytes_per_call": by, "ms_per_call": round(ms, 4)}
+    del C, ws, out
     torch.cuda.empty_cache()
     return e
 
@@ -423,6 +462,8 @@ def main():
                     help="leave the path-sum stress measurement (path_roofline) out")
     ap.add_argument("--no-decision-word", action="store_true",
                     help="leave the decision-word measurements (labels cut to their deciding word) out")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="leave the trie_decode measurements (greedy decoding in the trie) out")
     ap.add_argument("--no-letters", action="store_true",
                     help="leave the letters measurements (one answer position, letter rows only) out")
     ap.add_argument("--power", action="store_true",
@@ -486,11 +527,13 @@ def main():
     res["head_share_of_step"] = round(kern["head"] / (sec * 1e3), 4)
     if kern["doc_attn"]:
         res["doc_attn_roofline"] = doc_attn_roofline(S, kern["doc_attn"])
-    decision, letters = {}, {}
+    decision, letters, decode = {}, {}, {}
     if not args.no_decision_word:
         decision[cfg.name] = decision_word(S, args.steps, args.warmup, args.streams)
     if not args.no_letters:
         letters[cfg.name] = letters_measure(S, args.steps, args.warmup, args.streams)
+    if not args.no_decode:
+        decode[cfg.name] = decode_measure(S, args.steps, args.warmup, args.streams)
     extra = {}
     for c in [int(x) for x in args.extra.split(",") if x.strip()]:
         if c == args.config:
@@ -514,6 +557,8 @@ def main():
             decision[S2["cfg"].name] = decision_word(S2, max(3, args.steps // 2), 2, args.streams)
         if not args.no_letters:
             letters[S2["cfg"].name] = letters_measure(S2, max(3, args.steps // 2), 2, args.streams)
+        if not args.no_decode:
+            decode[S2["cfg"].name] = decode_measure(S2, max(3, args.steps // 2), 2, args.streams)
         S = S2
     if extra:
         res["at_labels"] = extra
@@ -521,6 +566,8 @@ def main():
         res["decision_word"] = decision
     if letters:
         res["letters"] = letters
+    if decode:
+        res["trie_decode"] = decode
     if not args.no_path_stress:
         del S
         torch.cuda.empty_cache()

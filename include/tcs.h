@@ -109,6 +109,7 @@ typedef struct {
   int32_t* dec_node;     /* [cap_nodes] where decoding goes on from the node: follow single
                             children while the subtree holds more than one label */
   int32_t max_decode_steps; /* set with the tables: the most model runs any label needs */
+  int32_t max_children;     /* set with the tables: the most children of any node */
 } tcs_trie;
 
 /*
@@ -169,6 +170,7 @@ typedef struct {
   const int32_t* sub_label;          /* [n_nodes] */
   const int32_t* dec_node;           /* [n_nodes] */
   int32_t max_decode_steps;
+  int32_t max_children;
 } tcs_trie_dev;
 
 /* --------------------------------------------------------- tree attention ---- */
@@ -367,8 +369,8 @@ int tcs_letters_run(tcs_stream stream, const tcs_model* model, const tcs_trie_de
  * take one step together; a label that is the start of another is never returned
  * (there is no stop token: section 3.1, note 2).  No probabilities are produced.
  *
- * `trie` needs the optional qrow, sub_label and dec_node arrays and
- * max_decode_steps (tcs_trie_build fills them when given the arrays); `prep` comes
+ * `trie` needs the optional qrow, sub_label and dec_node arrays, max_decode_steps
+ * and max_children (tcs_trie_build fills them when given the arrays); `prep` comes
  * from tcs_classify_prepare for that trie and B; `ws` holds
  * tcs_decode_workspace_bytes(model, trie, docs) bytes (0: invalid arguments).
  * Runs max_decode_steps steps on `stream` with no host synchronisation; documents

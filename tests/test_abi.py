@@ -237,6 +237,7 @@ def assert_decode_tables(labels, t):
             continue  # never returned by greedy decoding
         most = max(most, O.greedy_walk(labels, lambda p, c, l=l: l[len(p)])[1])
     assert t.max_decode_steps == most
+    assert t.max_children == max(int(c) for c in t.child_count)
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
@@ -262,7 +263,8 @@ def test_decode_run_errors_without_gpu():
     arrays = {n: fake for n in tcs.TRIE_DEV_ARRAYS}
     arrays["dec_node"] = None
     dev = tcs.tcs_trie_dev(n_nodes=t.n_nodes, n_int=t.n_int, n_labels=t.n_labels,
-                           max_depth=t.max_depth, max_decode_steps=t.max_decode_steps, **arrays)
+                           max_depth=t.max_depth, max_decode_steps=t.max_decode_steps,
+                           max_children=t.max_children, **arrays)
     model = tcs.tcs_model(dtype=tcs.TCS_BF16, head_dtype=tcs.TCS_BF16, d=128, Hq=2, Hkv=1, hd=128,
                           V=16, eps=1e-6, E=fake, Wq=fake, Wk=fake, Wv=fake, Wo=fake, W=fake)
     docs = tcs.tcs_docs(B=1, total_tokens=4, doc_offsets=fake, Kd=fake, Vd=fake)

@@ -42,7 +42,7 @@ class tcs_trie(C.Structure):
                     "parent", "token", "depth", "child_begin", "child_count", "node_label", "qrow",
                     "qnode", "qparent", "label_node", "level_offsets", "e_tok", "e_qrow", "e_child",
                     "row_level_offsets", "label_row", "sub_label", "dec_node")] + [
-                ("max_decode_steps", C.c_int32)]
+                ("max_decode_steps", C.c_int32), ("max_children", C.c_int32)]
 
 
 TRIE_DEV_ARRAYS = ("parent", "token", "child_begin", "child_count", "qnode", "qparent", "label_node",
@@ -53,7 +53,7 @@ TRIE_DEV_ARRAYS = ("parent", "token", "child_begin", "child_count", "qnode", "qp
 class tcs_trie_dev(C.Structure):
     _fields_ = [("n_nodes", C.c_int32), ("n_int", C.c_int32), ("n_labels", C.c_int32),
                 ("max_depth", C.c_int32)] + [(n, C.c_void_p) for n in TRIE_DEV_ARRAYS] + [
-                ("max_decode_steps", C.c_int32)]
+                ("max_decode_steps", C.c_int32), ("max_children", C.c_int32)]
 
 
 class tcs_model(C.Structure):
@@ -212,6 +212,7 @@ class Trie:
     max_depth: int
     arrays: dict
     max_decode_steps: int = 0
+    max_children: int = 0
 
     def __getattr__(self, k):
         a = self.__dict__.get("arrays")
@@ -248,7 +249,7 @@ def trie_build(label_offsets, label_tokens, root_token: int, V: int) -> Trie:
         cut = {"qnode": n_int, "qparent": n_int, "e_tok": N - 1, "e_qrow": N - 1, "e_child": N - 1,
                "label_node": M, "label_row": M, "level_offsets": D + 2, "row_level_offsets": D + 2}
         out = {n: a[:cut.get(n, N)].copy() for n, a in arrays.items()}
-        return Trie(N, n_int, M, D, out, int(t.max_decode_steps))
+        return Trie(N, n_int, M, D, out, int(t.max_decode_steps), int(t.max_children))
     raise TcsError(TCS_ECAPACITY, "trie capacity")
 
 
@@ -285,6 +286,7 @@ class TrieDevice:
                         for n in TRIE_DEV_ARRAYS}
         self.struct = tcs_trie_dev(n_nodes=trie.n_nodes, n_int=trie.n_int, n_labels=trie.n_labels,
                                    max_depth=trie.max_depth, max_decode_steps=trie.max_decode_steps,
+                                   max_children=trie.max_children,
                                    **{n: self.tensors[n].data_ptr() for n in TRIE_DEV_ARRAYS})
 
     def __getitem__(self, k):

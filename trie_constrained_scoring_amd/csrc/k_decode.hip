@@ -23,7 +23,8 @@ __global__ void decode_init_kernel(int B, const int32_t* __restrict__ dec_node,
                                    const int32_t* __restrict__ qrow, int32_t* __restrict__ cur,
                                    int32_t* __restrict__ label, int32_t* __restrict__ runs,
                                    int32_t* __restrict__ sel, int32_t* __restrict__ row_node,
-                                   int32_t* __restrict__ n_sel) {
+                                   int32_t* __restrict__ n_sel,
+                                   unsigned long long* __restrict__ best_key) {
   const int w0 = dec_node[0];
   const int lab = sub_label[w0];
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -35,75 +36,83 @@ __global__ void decode_init_kernel(int B, const int32_t* __restrict__ dec_node,
   sel[2 * b] = b;
   sel[2 * b + 1] = lab >= 0 ? 0 : qrow[w0];
   row_node[b] = w0;
+  best_key[b] = 0;
 }
 
-// One workgroup per slot a < *n_sel: the hidden state h[a] at node u = row_node[a]
-// against the head rows of u's children (one wave per child in turn), the
-// highest logit wins (lowest child index, i.e. lowest token id, on ties); then the
-// document moves to dec_node[child] and is decided if one label remains there.
+// Order-preserving key of (logit, child index): a larger logit wins, then the
+// lower index (lowest token id on ties).
+__device__ __forceinline__ unsigned long long pick_key(float z, int i) {
+  const uint32_t u = __float_as_uint(z);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(o) << 32) | (0xFFFFFFFFu - uint32_t(i));
+}
+
+// Workgroup (a, y) for slot a < *n_sel scores children y*CH .. y*CH+CH-1 of the
+// slot's node u = row_node[a] (one wave per child in turn): the hidden state h[a]
+// against the children's head rows.  Each workgroup folds its best (logit, child)
+// into the slot's key with a 64-bit atomic max; the next launch reads the keys.
+constexpr int STEP_CH = 32;  // children per workgroup: 8 per wave
 template <int WK>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(256) void decode_logits_kernel(
     int d, const void* __restrict__ h, const void* __restrict__ W,
     const float* __restrict__ w_scale, const int32_t* __restrict__ token,
     const int32_t* __restrict__ child_begin, const int32_t* __restrict__ child_count,
-    const int32_t* __restrict__ dec_node, const int32_t* __restrict__ sub_label,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ row_node,
-    const int32_t* __restrict__ n_sel, int32_t* __restrict__ cur, int32_t* __restrict__ label,
-    int32_t* __restrict__ runs) {
-  __shared__ float bz[4];
-  __shared__ int bi[4];
+    const int32_t* __restrict__ row_node, const int32_t* __restrict__ n_sel,
+    unsigned long long* __restrict__ best_key) {
+  __shared__ unsigned long long bk[4];
   const int a = blockIdx.x;
   if (a >= *n_sel) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int doc = sel[2 * a], u = row_node[a];
+  const int u = row_node[a];
   const int c0 = child_begin[u], nc = child_count[u];
   const void* hr = static_cast<const char*>(h) + size_t(a) * d * (WK == 0 ? 4 : 2);
-  float best = -INFINITY;
-  int bidx = 0x7fffffff;
-  for (int i = wave; i < nc; i += 4) {
+  unsigned long long key = 0;  // below every real key
+  const int i_end = min(nc, int(blockIdx.y + 1) * STEP_CH);
+  for (int i = int(blockIdx.y) * STEP_CH + wave; i < i_end; i += 4) {
     const int tok = token[c0 + i];
     float z = wave_sum(head_row_dot_lane<WK>(hr, W, tok, d, lane));
     if (WK == 2) z *= w_scale[tok];
-    if (z > best || bidx == 0x7fffffff) {  // i grows, so ties keep the first
-      best = z;
-      bidx = i;
-    }
+    key = max(key, pick_key(z, i));
   }
-  if (lane == 0) {
-    bz[wave] = best;
-    bi[wave] = bidx;
-  }
+  if (lane == 0) bk[wave] = key;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float z = bz[0];
-    int i = bi[0];
-    for (int w = 1; w < 4; ++w)
-      if (bi[w] != 0x7fffffff && (bz[w] > z || (bz[w] == z && bi[w] < i) || i == 0x7fffffff)) {
-        z = bz[w];
-        i = bi[w];
-      }
-    if (i == 0x7fffffff) {  // no child: cannot happen for a node the tables mark undecided
-      label[doc] = -1;
-      cur[doc] = -1;
-      return;
-    }
-    const int v = dec_node[c0 + i];
-    const int lab = sub_label[v];
-    if (runs) ++runs[doc];
-    label[doc] = lab;
-    cur[doc] = lab >= 0 ? -1 : v;
+    key = max(max(bk[0], bk[1]), max(bk[2], bk[3]));
+    if (key) atomicMax(best_key + a, key);
   }
 }
 
-// The next step's slots: the undecided documents in document order (one
-// workgroup, blocks of 1024 documents, a ballot prefix count per wave).
-__global__ __launch_bounds__(1024) void decode_compact_kernel(int B, const int32_t* __restrict__ cur,
-                                                             const int32_t* __restrict__ qrow,
-                                                             int32_t* __restrict__ sel,
-                                                             int32_t* __restrict__ row_node,
-                                                             int32_t* __restrict__ n_sel) {
+// One workgroup.  First every slot a < *n_sel takes its best child (and clears
+// its key): the document moves to dec_node[child] and is decided if one label
+// remains there.  Then the next step's slots are the undecided documents in
+// document order (blocks of 1024 documents, a ballot prefix count per wave).
+__global__ __launch_bounds__(1024) void decode_advance_kernel(
+    int B, const int32_t* __restrict__ child_begin, const int32_t* __restrict__ dec_node,
+    const int32_t* __restrict__ sub_label, const int32_t* __restrict__ qrow,
+    unsigned long long* __restrict__ best_key, int32_t* __restrict__ cur,
+    int32_t* __restrict__ label, int32_t* __restrict__ runs, int32_t* __restrict__ sel,
+    int32_t* __restrict__ row_node, int32_t* __restrict__ n_sel) {
   __shared__ int wsum[16];
+  const int n_old = *n_sel;
+  if (n_old == 0) return;  // every document decided: nothing changes
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int a = tid; a < n_old; a += 1024) {
+    const unsigned long long key = best_key[a];
+    best_key[a] = 0;
+    const int doc = sel[2 * a];
+    if (runs) ++runs[doc];
+    if (key == 0) {  // no child: cannot happen for a node the tables mark undecided
+      label[doc] = -1;
+      cur[doc] = -1;
+      continue;
+    }
+    const int i = int(0xFFFFFFFFu - uint32_t(key));
+    const int v = dec_node[child_begin[row_node[a]] + i];
+    const int lab = sub_label[v];
+    label[doc] = lab;
+    cur[doc] = lab >= 0 ? -1 : v;
+  }
+  __syncthreads();  // the documents' new states are in before they are gathered
   int base = 0;
   for (int b0 = 0; b0 < B; b0 += 1024) {
     const int b = b0 + tid;
@@ -133,30 +142,32 @@ __global__ __launch_bounds__(1024) void decode_compact_kernel(int B, const int32
 
 int launch_decode_init(void* stream, int32_t B, const int32_t* dec_node, const int32_t* sub_label,
                        const int32_t* qrow, int32_t* cur, int32_t* label, int32_t* runs,
-                       int32_t* sel, int32_t* row_node, int32_t* n_sel) {
+                       int32_t* sel, int32_t* row_node, int32_t* n_sel,
+                       unsigned long long* best_key) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B < 1) return TCS_OK;
   decode_init_kernel<<<(B + 255) / 256, 256, 0, s>>>(B, dec_node, sub_label, qrow, cur, label, runs,
-                                                      sel, row_node, n_sel);
+                                                      sel, row_node, n_sel, best_key);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "decode_init: %s", hipGetErrorString(e));
   return TCS_OK;
 }
 
-int launch_decode_step(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t d,
-                       const void* h, const void* W, const float* w_scale, const int32_t* token,
-                       const int32_t* child_begin, const int32_t* child_count,
-                       const int32_t* dec_node, const int32_t* sub_label, const int32_t* sel,
-                       const int32_t* row_node, const int32_t* n_sel, int32_t* cur, int32_t* label,
-                       int32_t* runs) {
+int launch_decode_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
+                         int32_t d, const void* h, const void* W, const float* w_scale,
+                         const int32_t* token, const int32_t* child_begin,
+                         const int32_t* child_count, const int32_t* row_node, const int32_t* n_sel,
+                         int32_t max_children, unsigned long long* best_key) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B < 1) return TCS_OK;
   if (h_dtype != TCS_F32 && d % 4 != 0)
     return fail(TCS_EUNSUPPORTED, "decode: d=%d is not a multiple of 4", d);
-#define TCS_STEP(WK)                                                                             \
-  decode_step_kernel<WK><<<B, 256, 0, s>>>(d, h, W, w_scale, token, child_begin, child_count,   \
-                                           dec_node, sub_label, sel, row_node, n_sel, cur, label, \
-                                           runs)
+  if (max_children < 1) return fail(TCS_EINVAL, "decode: max_children %d", max_children);
+  const dim3 grid(B, (max_children + STEP_CH - 1) / STEP_CH);
+  if (grid.y > 65535) return fail(TCS_EUNSUPPORTED, "decode: %d children", max_children);
+#define TCS_STEP(WK)                                                                       \
+  decode_logits_kernel<WK><<<grid, 256, 0, s>>>(d, h, W, w_scale, token, child_begin,      \
+                                                child_count, row_node, n_sel, best_key)
   if (h_dtype == TCS_F32 && w_dtype == TCS_F32)
     TCS_STEP(0);
   else if (h_dtype == TCS_BF16 && w_dtype == TCS_BF16)
@@ -168,17 +179,20 @@ int launch_decode_step(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32
                 int(w_dtype));
 #undef TCS_STEP
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TCS_EHIP, "decode_step: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(TCS_EHIP, "decode_logits: %s", hipGetErrorString(e));
   return TCS_OK;
 }
 
-int launch_decode_compact(void* stream, int32_t B, const int32_t* cur, const int32_t* qrow,
-                          int32_t* sel, int32_t* row_node, int32_t* n_sel) {
+int launch_decode_advance(void* stream, int32_t B, const int32_t* child_begin,
+                          const int32_t* dec_node, const int32_t* sub_label, const int32_t* qrow,
+                          unsigned long long* best_key, int32_t* cur, int32_t* label,
+                          int32_t* runs, int32_t* sel, int32_t* row_node, int32_t* n_sel) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B < 1) return TCS_OK;
-  decode_compact_kernel<<<1, 1024, 0, s>>>(B, cur, qrow, sel, row_node, n_sel);
+  decode_advance_kernel<<<1, 1024, 0, s>>>(B, child_begin, dec_node, sub_label, qrow, best_key, cur,
+                                           label, runs, sel, row_node, n_sel);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TCS_EHIP, "decode_compact: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(TCS_EHIP, "decode_advance: %s", hipGetErrorString(e));
   return TCS_OK;
 }
 

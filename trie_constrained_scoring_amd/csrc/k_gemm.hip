@@ -15,6 +15,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
     int M, int N, int K, const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B,
     int ldb, void* __restrict__ C, int ldc, int epi, GemmResid resid) {
   using S = GemmShape<BM, BN, WM, WN>;
+  if (resid.live && *resid.live == 0) return;  // no live rows this call
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   int mt, nt;
@@ -66,6 +67,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(
     int M, int N, int K, const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B,
     int ldb, void* __restrict__ C, int ldc, int epi, GemmResid resid) {
   constexpr uint32_t RSRC_W3 = 0x00020000u, OOB = 0x80000000u;
+  if (resid.live && *resid.live == 0) return;  // no live rows this call
   constexpr int U = 4;
   __shared__ float red[4][RB][256];
   const int lane = threadIdx.x & 63;
@@ -171,6 +173,7 @@ __global__ __launch_bounds__(512, 1) void gemm_split_kernel(
     int M, int N, int K, int s, const uint16_t* __restrict__ A, int lda,
     const uint16_t* __restrict__ B, int ldb, float* __restrict__ C, int ldc, GemmResid resid) {
   using S = SplitShape<BM>;
+  if (resid.live && *resid.live == 0) return;  // no live rows this call
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::NST * S::STAGE];
   const int nbm = (M + BM - 1) / BM, nbn = (N + S::BN - 1) / S::BN;
   // items in order (split, column tile, row tile); XCD x (block i runs on XCD
@@ -298,6 +301,7 @@ __global__ __launch_bounds__(256) void gemm_nt_f32_kernel(int M, int N, int K,
                                                           float* __restrict__ C, int ldc, int epi,
                                                           GemmResid resid) {
   __shared__ float sA[16][68];
+  if (resid.live && *resid.live == 0) return;  // no live rows this call
   __shared__ float sB[16][68];
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -384,7 +388,9 @@ __global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const T* __restrict_
 // Any d: one workgroup per row, two passes over y.
 template <typename T>
 __global__ __launch_bounds__(256) void rownorm_any_kernel(const float* __restrict__ y, int n, int d,
-                                                          int n_part, float eps, T* __restrict__ out) {
+                                                          int n_part, float eps, T* __restrict__ out,
+    const int32_t* __restrict__ live) {
+  if (live && *live == 0) return;  // no live rows this call
   __shared__ float red[4];
   const int r = blockIdx.x;
   auto val = [&](int i) {
@@ -406,7 +412,9 @@ __global__ __launch_bounds__(256) void rownorm_any_kernel(const float* __restric
 // it (the n_part partials' loads all issued before the sums), one block reduction.
 template <typename T, int RB4>
 __global__ __launch_bounds__(256) void rownorm_block_kernel(const float* __restrict__ y, int n, int d,
-                                                            int n_part, float eps, T* __restrict__ out) {
+                                                            int n_part, float eps, T* __restrict__ out,
+    const int32_t* __restrict__ live) {
+  if (live && *live == 0) return;  // no live rows this call
   __shared__ float red[4];
   const int r = blockIdx.x, t = threadIdx.x;
   const int d4 = d / 4;
@@ -456,7 +464,9 @@ __global__ __launch_bounds__(256) void rownorm_block_kernel(const float* __restr
 // partials in a fixed order; one read of y, one write of h.
 template <typename T, int RN4>
 __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ y, int n, int d,
-                                                      int n_part, float eps, T* __restrict__ out) {
+                                                      int n_part, float eps, T* __restrict__ out,
+    const int32_t* __restrict__ live) {
+  if (live && *live == 0) return;  // no live rows this call
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n) return;
@@ -520,30 +530,30 @@ int launch_embed_rmsnorm(void* stream, tcs_dtype dt, const void* E, const int32_
 }
 
 int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, int32_t n_part,
-                   float eps, void* out) {
+                   float eps, void* out, const int32_t* live) {
   if (n <= 0) return TCS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int grid = (n + 3) / 4;
   if (d % 4 != 0 || d > 256 * 16) {
     if (dt == TCS_BF16)
-      rownorm_any_kernel<bf16_t><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+      rownorm_any_kernel<bf16_t><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out), live);
     else
-      rownorm_any_kernel<float><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+      rownorm_any_kernel<float><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out), live);
   } else if (n <= 2048 && n_part > 1) {  // few rows, split-K partials: a workgroup per row
     if (dt == TCS_BF16)
-      rownorm_block_kernel<bf16_t, 4><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+      rownorm_block_kernel<bf16_t, 4><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out), live);
     else
-      rownorm_block_kernel<float, 4><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+      rownorm_block_kernel<float, 4><<<n, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out), live);
   } else if (dt == TCS_BF16) {
     if (d <= 256 * 10)
-      rownorm_kernel<bf16_t, 10><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+      rownorm_kernel<bf16_t, 10><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out), live);
     else
-      rownorm_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out));
+      rownorm_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<bf16_t*>(out), live);
   } else {
     if (d <= 256 * 10)
-      rownorm_kernel<float, 10><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+      rownorm_kernel<float, 10><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out), live);
     else
-      rownorm_kernel<float, 16><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out));
+      rownorm_kernel<float, 16><<<grid, 256, 0, s>>>(y, n, d, n_part, eps, static_cast<float*>(out), live);
   }
   return check_launch("rownorm");
 }
@@ -567,10 +577,11 @@ static void split_plan(int M, int N, int K, int& bm, int& s) {
   s = std::min(s, std::min(8, K / GEMM_BK));
 }
 
-// Few-row bf16 products with a residual go to gemm_split_kernel (K-split partials);
+// Few-row bf16 products with a residual go to gemm_split_kernel (K-split partials),
+// down to a single row: the K split spreads even one row tile over the CUs;
 // larger ones to the generic tiles, one partial.
 static bool use_split(tcs_dtype dt, int M, int N) {
-  if (dt != TCS_BF16 || M <= 64) return false;
+  if (dt != TCS_BF16 || M < 1) return false;
   const long t256 = long((M + 255) / 256) * ((N + 255) / 256);
   const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
   return t256 < 512 && t128 < 512;

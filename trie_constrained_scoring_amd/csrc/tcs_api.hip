@@ -376,6 +376,7 @@ struct DecodeLayout {
   void *a_doc, *Kd, *Vd, *O, *h;
   float* y;
   int32_t *cur, *sel, *row_node, *n_sel, *runs;
+  unsigned long long* best_key;
 };
 
 static DecodeLayout decode_layout(const tcs_model* m, const tcs_docs* d, void* ws) {
@@ -398,6 +399,7 @@ static DecodeLayout decode_layout(const tcs_model* m, const tcs_docs* d, void* w
   L.row_node = c.take<int32_t>(B);
   L.n_sel = c.take<int32_t>(1);
   L.runs = c.take<int32_t>(B);
+  L.best_key = c.take<unsigned long long>(B);
   L.total = c.used;
   return L;
 }
@@ -409,6 +411,8 @@ static int check_decode(const tcs_model* m, const tcs_trie_dev* t, const tcs_doc
   if (t->max_decode_steps < 0 || t->max_decode_steps > t->max_depth)
     return fail(TCS_EINVAL, "decode: max_decode_steps %d outside [0, %d]", t->max_decode_steps,
                 t->max_depth);
+  if (t->max_children < 1 || t->max_children >= t->n_nodes)
+    return fail(TCS_EINVAL, "decode: max_children %d outside [1, %d)", t->max_children, t->n_nodes);
   if (m->dtype == TCS_BF16 && (m->hd != 128 || m->Hq / m->Hkv > 64))
     return fail(TCS_EUNSUPPORTED, "decode: bf16 models need head_dim 128 (hd=%d)", m->hd);
   return TCS_OK;
@@ -453,8 +457,9 @@ int tcs_decode_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t,
     Vd = L.Vd;
   }
   if ((rc = launch_decode_init(stream, B, t->dec_node, t->sub_label, t->qrow, L.cur, label, nruns,
-                               L.sel, L.row_node, L.n_sel))) return rc;
-  const GemmResid res{m->E, t->token, L.row_node, B};
+                               L.sel, L.row_node, L.n_sel, L.best_key))) return rc;
+  // every launch of a step returns at once when no document is left undecided
+  const GemmResid res{m->E, t->token, L.row_node, B, L.n_sel};
   const int splits = gemm_resid_splits(dt, B, m->d, qd);
   for (int step = 0; step < t->max_decode_steps; ++step) {
     // one answer position per undecided document: its node's queries over the
@@ -472,12 +477,13 @@ int tcs_decode_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t,
     if (rc) return rc;
     if ((rc = launch_gemm_nt(stream, dt, GEMM_RESID, B, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d,
                              &res))) return rc;
-    if ((rc = launch_rownorm(stream, dt, L.y, B, m->d, splits, m->eps, L.h))) return rc;
-    if ((rc = launch_decode_step(stream, dt, m->head_dtype, B, m->d, L.h, m->W, m->W_scale,
-                                 t->token, t->child_begin, t->child_count, t->dec_node,
-                                 t->sub_label, L.sel, L.row_node, L.n_sel, L.cur, label,
-                                 nruns))) return rc;
-    if ((rc = launch_decode_compact(stream, B, L.cur, t->qrow, L.sel, L.row_node, L.n_sel))) return rc;
+    if ((rc = launch_rownorm(stream, dt, L.y, B, m->d, splits, m->eps, L.h, L.n_sel))) return rc;
+    if ((rc = launch_decode_logits(stream, dt, m->head_dtype, B, m->d, L.h, m->W, m->W_scale,
+                                   t->token, t->child_begin, t->child_count, L.row_node, L.n_sel,
+                                   t->max_children, L.best_key))) return rc;
+    if ((rc = launch_decode_advance(stream, B, t->child_begin, t->dec_node, t->sub_label, t->qrow,
+                                    L.best_key, L.cur, label, nruns, L.sel, L.row_node,
+                                    L.n_sel))) return rc;
   }
   return TCS_OK;
 }

@@ -42,8 +42,9 @@ int launch_embed_rmsnorm(void* stream, tcs_dtype dt, const void* E, const int32_
 
 // h[r] = RMSNorm(y[r]) for fp32 y = sum of n_part partials [n_part][n][d], written in
 // dtype dt.
+// live (optional, device): when it holds 0 the launch does nothing.
 int launch_rownorm(void* stream, tcs_dtype dt, const float* y, int32_t n, int32_t d, int32_t n_part,
-                   float eps, void* out);
+                   float eps, void* out, const int32_t* live = nullptr);
 
 // C[m, n] = sum_k A[m, k] * B[n, k].  Epilogues:
 //   STORE: C stored in dtype dt (rounded) with leading dimension ldc.
@@ -58,6 +59,7 @@ struct GemmResid {
   const int32_t* token;
   const int32_t* qnode;
   int32_t n_int;
+  const int32_t* live;  // optional (device): when it holds 0 the launch does nothing
 };
 int launch_gemm_nt(void* stream, tcs_dtype dt, GemmEpi epi, int32_t M, int32_t N, int32_t K,
                    const void* A, int32_t lda, const void* B, int32_t ldb, void* C, int32_t ldc,
@@ -108,15 +110,17 @@ int launch_letter_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int
 // Greedy decoding in the trie (per-document state on the device).
 int launch_decode_init(void* stream, int32_t B, const int32_t* dec_node, const int32_t* sub_label,
                        const int32_t* qrow, int32_t* cur, int32_t* label, int32_t* runs,
-                       int32_t* sel, int32_t* row_node, int32_t* n_sel);
-int launch_decode_step(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t d,
-                       const void* h, const void* W, const float* w_scale, const int32_t* token,
-                       const int32_t* child_begin, const int32_t* child_count,
-                       const int32_t* dec_node, const int32_t* sub_label, const int32_t* sel,
-                       const int32_t* row_node, const int32_t* n_sel, int32_t* cur, int32_t* label,
-                       int32_t* runs);
-int launch_decode_compact(void* stream, int32_t B, const int32_t* cur, const int32_t* qrow,
-                          int32_t* sel, int32_t* row_node, int32_t* n_sel);
+                       int32_t* sel, int32_t* row_node, int32_t* n_sel,
+                       unsigned long long* best_key);
+int launch_decode_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
+                         int32_t d, const void* h, const void* W, const float* w_scale,
+                         const int32_t* token, const int32_t* child_begin,
+                         const int32_t* child_count, const int32_t* row_node, const int32_t* n_sel,
+                         int32_t max_children, unsigned long long* best_key);
+int launch_decode_advance(void* stream, int32_t B, const int32_t* child_begin,
+                          const int32_t* dec_node, const int32_t* sub_label, const int32_t* qrow,
+                          unsigned long long* best_key, int32_t* cur, int32_t* label,
+                          int32_t* runs, int32_t* sel, int32_t* row_node, int32_t* n_sel);
 
 // Tree attention pieces.
 int launch_anc_attn(void* stream, tcs_dtype dt, int32_t n_int, int32_t Hq, int32_t Hkv,

@@ -227,6 +227,9 @@ extern "C" int tcs_trie_build(const int32_t* label_offsets, const int32_t* label
       most = std::max(most, runs);
     }
     out->max_decode_steps = most;
+    int32_t widest = 0;
+    for (int32_t c = 0; c < N; ++c) widest = std::max(widest, out->child_count[c]);
+    out->max_children = widest;
   }
   return TCS_OK;
 }
