@@ -358,7 +358,7 @@ def path_stress(cid: int = 4, B: int = 4096, reps: int = 10):
     nbytes = B * (N * 4 + 2 * M * 4 + 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "path_sum_kernel",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "path_levels_kernel",
             "workload": f"{B} documents on the {M}-label trie of config {cid} ({N} nodes)",
             "bytes_per_launch": nbytes, "ms_per_launch": round(ms, 4),
             "timing": "torch.cuda.Event around 10 launches on the current stream"}
