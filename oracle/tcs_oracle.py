@@ -51,7 +51,13 @@ reason in the design notes):
       itself as in R4; the returned scores are the letter logits (log scores up to a
       per-document constant, as the vocabulary log-sum-exp is never formed);
   R11 trie_decode ties go to the lowest token id; a decode run at a node is the
-      model over [root, path tokens] attending to the document (as in R4/R5).
+      model over [root, path tokens] attending to the document (as in R4/R5);
+  R12 W8A8 head ("Building an Ultra-High Throughput AI-SQL Engine", fp8 weights and
+      activations): each stored hidden row h (bf16 values) is quantized before the
+      head with s = fl32(max|h| / 448) and codes = E4M3(fl32(h / s)), nearest value,
+      ties to the even code, saturating at 448 (an all-zero row keeps s = 0); the
+      logit is s * s_w * sum(codes_h * codes_w).  The scale and the quotients are
+      fp32, as the kernel computes them, because they decide integer codes.
 
 Parity status: every function below is pinned by the non-GPU oracle tests
 (library routines, closed forms, the worked example, brute-force scoring).
@@ -69,6 +75,7 @@ __all__ = [
     "lm_head_lse", "head_logits_at", "edge_logprobs", "log1mexp", "path_log_likelihoods",
     "label_softmax", "classify", "bruteforce_ll", "label_ll_on_paths",
     "decision_depths", "truncate_labels", "letters_classify", "greedy_walk", "trie_decode",
+    "e4m3_encode", "quantize_rows_e4m3",
 ]
 
 TCS_OK = 0
@@ -225,6 +232,41 @@ def decode_e4m3(codes):
     return s * mag
 
 
+def e4m3_encode(x):
+    """Values -> OCP E4M3FN codes (R12): the nearest finite E4M3 value, ties to the
+    even code, magnitudes from 448 up saturating to 448; the sign is kept.
+
+    The candidates are the 127 non-negative finite values decode_e4m3 gives for
+    codes 0..126, in increasing order: the two neighbours of |x| are compared.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    vals = decode_e4m3(np.arange(127))
+    a = np.abs(x)
+    up = np.clip(np.searchsorted(vals, a, side="left"), 1, 126)   # vals[up-1] < a <= vals[up]
+    below, above = up - 1, up
+    d_below = a - vals[below]
+    d_above = vals[above] - a
+    code = np.where(d_above < d_below, above, below)
+    tie = d_above == d_below
+    code = np.where(tie, np.where(above % 2 == 0, above, below), code)
+    code = np.where(a >= 448.0, 126, code)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_rows_e4m3(h):
+    """Per-row E4M3 quantization of hidden states (R12): s = fl32(max|h| / 448),
+    codes = e4m3_encode(fl32(h / s)); rows of zeros get s = 0 and zero codes.
+    h: [R, d] (values representable in fp32).  Returns (codes uint8 [R, d], s [R])."""
+    h32 = np.asarray(h, dtype=np.float32)
+    amax = np.abs(h32).max(axis=1)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = (h32 / safe[:, None]).astype(np.float32)
+    codes = e4m3_encode(q.astype(np.float64))
+    codes[s == 0] = 0
+    return codes, s.astype(np.float64)
+
+
 def rmsnorm(x, eps: float = 1e-6):
     """x / sqrt(mean(x^2) + eps) over the last axis, gain 1 (reading R5)."""
     x = np.asarray(x, dtype=np.float64)
@@ -246,7 +288,8 @@ class OracleModel:
         self.Wk = dec(inp["Wk"])
         self.Wv = dec(inp["Wv"])
         self.Wo = dec(inp["Wo"])
-        if cfg.head == "fp8":
+        self.act8 = cfg.head == "fp8a8"
+        if cfg.head in ("fp8", "fp8a8"):
             self.W = decode_e4m3(inp["W"])
             self.W_scale = np.asarray(inp["W_scale"], dtype=np.float64)
         else:
@@ -322,9 +365,14 @@ def hidden_states(model: OracleModel, x_nodes, O):
 
 def head_logits_at(model: OracleModel, h, cols=None):
     """Logits h W^T for all vocabulary rows (or the listed ones); fp8 heads scale
-    each dot product by the row's scale (R7)."""
+    each dot product by the row's scale (R7); a W8A8 head first quantizes each
+    hidden row to E4M3 with its own scale (R12)."""
     W = model.W if cols is None else model.W[cols]
-    z = h @ W.T
+    if getattr(model, "act8", False):
+        codes, sh = quantize_rows_e4m3(h)
+        z = (decode_e4m3(codes) @ W.T) * sh[:, None]
+    else:
+        z = h @ W.T
     if model.W_scale is not None:
         z = z * (model.W_scale if cols is None else model.W_scale[cols])
     return z

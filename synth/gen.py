@@ -42,7 +42,8 @@ class Config:
     Hkv: int
     hd: int
     dtype: str                   # "f32" or "bf16": storage of weights and activations
-    head: str                    # "same" (LM head in `dtype`) or "fp8" (E4M3FN + fp32 row scale)
+    head: str                    # "same" (LM head in `dtype`), "fp8" (E4M3FN + fp32 row scale) or
+                                 # "fp8a8" (the same weights; activations quantized to E4M3 too)
     trie: tuple                  # ("running",) or ("zipf", M, lo, hi, s)
     doc_mode: str                # "kv": doc K/V given; "tokens": doc token ids given
     doc_lens: tuple | None = None  # ragged lengths (overrides B and L)
@@ -282,7 +283,7 @@ def make_inputs(cfg: Config, seed: int | None = None, *, weights: bool = True):
         out["Wk"] = _weight(rngs["Wk"], (Hkv * hd, d), cfg.std, cfg.dtype)
         out["Wv"] = _weight(rngs["Wv"], (Hkv * hd, d), cfg.std, cfg.dtype)
         out["Wo"] = _weight(rngs["Wo"], (d, Hq * hd), cfg.std, cfg.dtype)
-        if cfg.head == "fp8":
+        if cfg.head in ("fp8", "fp8a8"):
             out["W"], out["W_scale"] = _fp8_head(rngs["W"], V, d, cfg.std)
         else:
             out["W"] = _weight(rngs["W"], (V, d), cfg.std, cfg.dtype)
