@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
                     [--no-cpu-baseline] [--no-path-stress] [--no-decision-word] [--no-letters]
-                    [--no-decode]
+                    [--no-decode] [--no-shard]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
     python bench.py --head-probe --config 3 [--power]  # head alone: workload-like vs constant
                                                        # operands (+ socket power and clocks)
@@ -29,6 +29,8 @@ of trie_tree: fewer query rows, same kernels); the headline scores every label o
 its full root-to-leaf path.  ``letters`` runs them under the letters method (one
 answer position per document, only the letter rows of the head), ``trie_decode`` under
 greedy decoding in the trie (one answer position per undecided document per step).
+``shard_of_8`` runs the long-document workload at one GPU's share of an 8-GPU run
+(16 of its 128 documents; documents shard over GPUs with no collective).
 ``roofline`` is for the
 dominant kernel (the output head): after the timed steps, the same steps run
 again with the head launches bracketed by HIP events on the stream they run on
@@ -90,11 +92,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup(cid: int, streams: int = 1):
+def setup(cid: int, streams: int = 1, **overrides):
     import torch
     import trie_constrained_scoring_amd as tcs
     from synth import config, make_inputs
-    cfg = config(cid)
+    cfg = config(cid, **overrides)
     t0 = time.time()
     inp = make_inputs(cfg)
     log(f"[bench] config {cid} inputs generated in {time.time() - t0:.1f}s")
@@ -462,6 +464,8 @@ def main():
                     help="leave the path-sum stress measurement (path_roofline) out")
     ap.add_argument("--no-decision-word", action="store_true",
                     help="leave the decision-word measurements (labels cut to their deciding word) out")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="leave out the long-document workload at one GPU's share of 8 (B = 16)")
     ap.add_argument("--no-decode", action="store_true",
                     help="leave the trie_decode measurements (greedy decoding in the trie) out")
     ap.add_argument("--no-letters", action="store_true",
@@ -562,6 +566,21 @@ def main():
         S = S2
     if extra:
         res["at_labels"] = extra
+    if not args.no_shard:
+        # documents shard over GPUs with no collective: one GPU's share of the
+        # 128-document long-document batch over 8 GPUs is 16 documents
+        del S
+        torch.cuda.empty_cache()
+        S = setup(5, args.streams, B=16)
+        s5, k5 = run_steps(S, max(3, args.steps // 2), 2)
+        f5, _ = head_flops(S)
+        tf = f5 / (k5["head"] * 1e-3) / 1e12
+        res["shard_of_8"] = {"config": 5, "global_batch": 128, "per_gpu_batch": 16,
+                             "docs_per_s": round(16 / s5, 2), "ms_per_step": round(s5 * 1e3, 4),
+                             "head_ms": round(k5["head"], 4), "head_tflops": round(tf, 2),
+                             "head_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if k5["doc_attn"]:
+            res["shard_of_8"]["doc_attn_roofline"] = doc_attn_roofline(S, k5["doc_attn"])
     if decision:
         res["decision_word"] = decision
     if letters:
