@@ -237,10 +237,11 @@ int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtyp
  * Per-label log score, label softmax and argmax (section 3.2).
  *   ll[b, m]  = sum of lp[b, .] over the path root -> label_node[m], plus
  *               log(1 - sum_{children c} exp(lp[b, c])) when label_node[m] has
- *               children (-inf if the children take all mass).  Path sums are
- *               carried in fp64, or as a pair of fp32 values (about 2^-33 relative
- *               error per step) when the trie arrays for level-by-level sums are
- *               given; the prefix term in fp64.
+ *               children (-inf if the children take all mass).  Up to 512 labels,
+ *               or without the trie arrays for level-by-level sums, each label's
+ *               path is walked with fp64 sums; past 512 labels with the arrays the
+ *               sums run level by level as a pair of fp32 values (about 2^-33
+ *               relative error per step).  The prefix term is fp64.
  *   prob[b,.] = softmax over m of ll[b, .]            (optional: prob may be NULL)
  *   label[b]  = argmax_m ll[b, m] of the returned (fp32) ll, lowest label id among
  *               equal maxima

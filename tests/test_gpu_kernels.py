@@ -86,9 +86,10 @@ def test_path_sum_vs_oracle(dev, case, with_prob):
 
 @pytest.mark.parametrize("cid,B", [(4, 300), (3, 600)])
 def test_path_sum_many_docs_per_workgroup(dev, cid, B):
-    """More documents than workgroups (the 5000-label trie takes one 1024-thread
-    workgroup per CU, the 255-label trie two), so workgroups score several
-    documents in turn, each loaded while the previous one is scored."""
+    """Many documents: on the 5000-label trie the level-by-level kernel has more
+    documents than workgroups, so workgroups score several in turn, each loaded
+    while the previous one is scored; the 255-label trie takes the per-label walk,
+    one workgroup per document."""
     inp = make_inputs(config(cid), weights=False)
     labels, root, V = inp["labels"], inp["root_token"], config(cid).V
     trie = O.build_trie(labels, root, V)
