@@ -82,3 +82,29 @@ def test_decode_full_size(dev, cid):
     docs = list(range(cfg.B)) if cid != 5 else [0, 1, cfg.B // 2, cfg.B - 1]
     o = O.trie_decode(inp, docs=docs)
     check_decode(label, runs, o, inp["labels"], f"decode[config {cid} full]")
+
+
+def test_decode_runs_on_two_streams(dev):
+    """Two batches in flight, as bench.py runs them: tcs_decode_run on two HIP streams
+    at once, each with its own workspace (the per-document decoding state lives
+    there), gives the single-stream labels and run counts."""
+    import torch
+    cfg = config(3, V=4096, d=128, Hq=8, Hkv=2, B=40, L=50, trie=("zipf", 60, 2, 9, 1.2))
+    inp = make_inputs(cfg, seed=117)
+    t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(t)
+    model = tcs.Model(cfg, inp)
+    docs = tcs.Docs(cfg, inp)
+    prep = tcs.Prepared(model, td, docs.B)
+    ref = [x.cpu().numpy() for x in tcs.trie_decode(model, td, docs, prep)]
+    nbytes = tcs.decode_workspace_bytes(model, td, docs)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    ws = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    outs = [tcs.trie_decode(model, td, docs, prep, ws=ws[i % 2], stream=streams[i % 2])
+            for i in range(6)]
+    torch.cuda.synchronize()
+    for o in outs:
+        for a, b in zip(o, ref):
+            np.testing.assert_array_equal(a.cpu().numpy(), b)
+    say(f"decode on two streams: 6 batches == single-stream run (max steps {t.max_decode_steps})")

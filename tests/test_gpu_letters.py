@@ -69,3 +69,27 @@ def test_letters_full_size(dev, cid):
                  f"letters[config {cid} full, {len(docs)} docs]")
     np.testing.assert_allclose(prob.sum(axis=1), 1.0, atol=1e-4)
     say(f"letters[config {cid}]: M={len(inp['letters'])}")
+
+
+def test_letters_runs_on_two_streams(dev):
+    """tcs_letters_run on two HIP streams at once, each with its own workspace, gives
+    the single-stream results bit for bit."""
+    import torch
+    cfg = SMALL["running-bf16-small"]
+    inp = make_inputs(cfg, seed=119)
+    letters = np.asarray(inp["letters"], dtype=np.int32)
+    t = tcs.trie_build(np.arange(len(letters) + 1, dtype=np.int32), letters, inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(t)
+    model = tcs.Model(cfg, inp)
+    docs = tcs.Docs(cfg, inp)
+    prep = tcs.Prepared(model, td, docs.B)
+    ref = [x.cpu().numpy() for x in tcs.letters(model, td, docs, prep)]
+    nbytes = tcs.classify_run_workspace_bytes(model, td, docs)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    ws = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    outs = [tcs.letters(model, td, docs, prep, ws=ws[i % 2], stream=streams[i % 2]) for i in range(6)]
+    torch.cuda.synchronize()
+    for o in outs:
+        for a, b in zip(o, ref):
+            np.testing.assert_array_equal(a.cpu().numpy(), b)
