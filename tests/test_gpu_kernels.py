@@ -30,10 +30,15 @@ def _proper_lp(trie, B, rng):
     return lp.astype(np.float32)
 
 
-def _run_path_sum(labels, root, V, lp, with_prob=True):
+def _run_path_sum(labels, root, V, lp, with_prob=True, walk=False):
+    """tcs_path_sum_softmax; walk=True leaves out the level-by-level arrays, so every
+    label's path is walked whatever the trie's size."""
     torch = _torch()
     t = tcs.trie_build(*labels_to_csr(labels), root, V)
     td = tcs.TrieDevice(t)
+    if walk:
+        td.struct.row_level_offsets = None
+        td.struct.label_row = None
     ll, prob, label = tcs.path_sum_softmax(torch.from_numpy(lp).cuda(), td, with_prob=with_prob)
     torch.cuda.synchronize()
     return ll.cpu().numpy(), (prob.cpu().numpy() if prob is not None else None), label.cpu().numpy()
@@ -277,3 +282,21 @@ def test_tree_attn_many_rows_many_docs(dev):
     exact = float((got == ref).mean())
     say(f"tree_attn[many rows, B={B}] n_int={n}: exact bf16 match {exact:.4f}, max off {off.max():.2f} ulp")
     assert off.max() <= 1.0 and exact >= 0.99
+
+
+def test_path_sum_walk_and_levels_agree_on_large_trie(dev):
+    """The 5000-label trie through both path kernels: the level-by-level one (its
+    arrays given) and the per-label walk (arrays left out), each against the oracle."""
+    inp = make_inputs(config(4), weights=False)
+    labels, root, V = inp["labels"], inp["root_token"], config(4).V
+    trie = O.build_trie(labels, root, V)
+    lp = _proper_lp(trie, 9, np.random.default_rng(44))
+    o_ll = O.path_log_likelihoods(trie, lp.astype(np.float64))
+    o_p, o_lab = O.label_softmax(o_ll)
+    got = {}
+    for walk in (False, True):
+        ll, prob, label = _run_path_sum(labels, root, V, lp, walk=walk)
+        assert np.abs(ll - o_ll).max() < 1e-4
+        assert np.abs(prob - o_p).max() < 1e-5
+        got[walk] = ll
+    assert np.abs(got[True] - got[False]).max() < 1e-4
