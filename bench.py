@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
                     [--no-cpu-baseline] [--no-path-stress] [--no-decision-word] [--no-letters]
-                    [--no-decode] [--no-shard]
+                    [--no-decode] [--no-shard] [--no-w8a8]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
     python bench.py --head-probe --config 3 [--power]  # head alone: workload-like vs constant
                                                        # operands (+ socket power and clocks)
@@ -29,6 +29,8 @@ of trie_tree: fewer query rows, same kernels); the headline scores every label o
 its full root-to-leaf path.  ``letters`` runs them under the letters method (one
 answer position per document, only the letter rows of the head), ``trie_decode`` under
 greedy decoding in the trie (one answer position per undecided document per step).
+``w8a8`` runs the long-document workload with the hidden rows quantized to E4M3 before
+the head (fp8 x fp8 matrix cores; roofline against the 5.0 PFLOP/s fp8 peak).
 ``shard_of_8`` runs the long-document workload at one GPU's share of an 8-GPU run
 (16 of its 128 documents; documents shard over GPUs with no collective).
 ``roofline`` is for the
@@ -59,6 +61,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "documents classified/sec at 10/255/5000 labels; % of HBM/MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix cores
 PEAK_HBM_GBS = 8000.0
 HEAD_SOURCES = ["gemm_core.h", "k_lmhead.hip", "tcs_device.h"]
 HEAD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lmhead_ring_bf16_running_example_B64_traffic.md")
@@ -464,6 +467,10 @@ def main():
                     help="leave the path-sum stress measurement (path_roofline) out")
     ap.add_argument("--no-decision-word", action="store_true",
                     help="leave the decision-word measurements (labels cut to their deciding word) out")
+    ap.add_argument("--head", default=None, choices=["same", "fp8", "fp8a8"],
+                    help="output-head kind for the primary workload (default: the workload's own)")
+    ap.add_argument("--no-w8a8", action="store_true",
+                    help="leave out the long-document workload with the W8A8 head (fp8 activations)")
     ap.add_argument("--no-shard", action="store_true",
                     help="leave out the long-document workload at one GPU's share of 8 (B = 16)")
     ap.add_argument("--no-decode", action="store_true",
@@ -497,7 +504,7 @@ def main():
         print(json.dumps({"path_roofline": path_stress()}), flush=True)
         return
 
-    S = setup(args.config, args.streams)
+    S = setup(args.config, args.streams, **({"head": args.head} if args.head else {}))
     cfg, trie = S["cfg"], S["trie"]
     sec, kern = run_steps(S, args.steps, args.warmup)
     B = S["docs"].B
@@ -506,7 +513,8 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "docs/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.dtype if cfg.head == "same" else f"{cfg.dtype} (head weights fp8 e4m3)",
+        "dtype": {"same": cfg.dtype, "fp8": f"{cfg.dtype} (head weights fp8 e4m3)",
+                  "fp8a8": f"{cfg.dtype} (head fp8 e4m3 weights and activations)"}[cfg.head],
         "data": "synthetic (seeded; random weights N(0,0.02), random doc KV N(0,1))",
         "config": {"workload": f"{cfg.name} (config {cfg.id}): B={B} docs x {cfg.L} tokens, "
                                f"{trie.n_labels} labels, {trie.n_nodes} trie nodes "
@@ -521,10 +529,13 @@ def main():
     }
     flops, R = head_flops(S)
     ach = flops / (kern["head"] * 1e-3) / 1e12
-    kname = "lmhead_ring_kernel<true> (fp8 W)" if cfg.head == "fp8" else "lmhead_ring_kernel<false> (bf16 W)"
+    kname = {"fp8": "lmhead_ring_kernel<true> (fp8 W)",
+             "fp8a8": "quant_rows_e4m3_kernel + lmhead_ring_kernel<fp8 W, fp8 h>"}.get(
+                 cfg.head, "lmhead_ring_kernel<false> (bf16 W)")
+    peak = PEAK_FP8_TFLOPS if cfg.head == "fp8a8" else PEAK_BF16_TFLOPS
     traffic = recorded_traffic() if cfg.id == 2 and cfg.head == "same" else None
-    res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+    res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                       "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                        "traffic": traffic, "kernel": kname, "rows": R,
                        "flops_per_launch": flops, "ms_per_launch": round(kern["head"], 4),
                        "timing": "HIP events around each head launch of a second pass of the same steps"}
@@ -566,6 +577,21 @@ def main():
         S = S2
     if extra:
         res["at_labels"] = extra
+    if not args.no_w8a8 and cfg.head != "fp8a8":
+        # the long-document workload with its hidden rows quantized to E4M3 before
+        # the head (fp8 x fp8 matrix cores); a precision change, so reported apart
+        del S
+        torch.cuda.empty_cache()
+        S = setup(5, args.streams, head="fp8a8")
+        s8, k8 = run_steps(S, max(3, args.steps // 2), 2)
+        f8, R8 = head_flops(S)
+        tf = f8 / (k8["head"] * 1e-3) / 1e12
+        res["w8a8"] = {"config": 5, "docs_per_s": round(S["docs"].B / s8, 2),
+                       "ms_per_step": round(s8 * 1e3, 4), "dtype": "fp8 e4m3 x fp8 e4m3 (head only)",
+                       "head_ms": round(k8["head"], 4), "rows": R8,
+                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                                    "kernel": "quant_rows_e4m3_kernel + lmhead_ring_kernel<fp8 W, fp8 h>"}}
     if not args.no_shard:
         # documents shard over GPUs with no collective: one GPU's share of the
         # 128-document long-document batch over 8 GPUs is 16 documents

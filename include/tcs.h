@@ -51,7 +51,10 @@ extern "C" {
 typedef enum {
   TCS_F32 = 0,       /* IEEE fp32 */
   TCS_BF16 = 1,      /* bfloat16 bit patterns */
-  TCS_FP8_E4M3 = 2   /* OCP E4M3FN bytes, with one fp32 scale per row */
+  TCS_FP8_E4M3 = 2,  /* OCP E4M3FN bytes, with one fp32 scale per row */
+  TCS_FP8_E4M3_A8 = 3 /* output head only: E4M3 weights with row scales as TCS_FP8_E4M3, and
+                         each hidden row quantized to E4M3 before the head with its own
+                         scale max|h|/448 (fp8 x fp8 matrix cores, "W8A8") */
 } tcs_dtype;
 
 /* hipStream_t without including HIP headers; NULL is the default stream. */

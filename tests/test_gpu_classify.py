@@ -43,6 +43,10 @@ SMALL = {
     "prefix-bf16-small": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=64, B=5, L=40,
                                 trie=("explicit", [[3], [3, 4], [3, 4, 5], [3, 6], [9, 9, 9], [9, 9], [1]])),
     "fp8-small": config(5, V=2500, d=192, Hq=4, Hkv=1, B=4, L=300),
+    # W8A8 head: hidden rows quantized to E4M3 per row; the second case has 320
+    # rows, a full and a ragged row tile
+    "fp8a8-small": config(5, V=2500, d=192, Hq=4, Hkv=1, B=4, L=300, head="fp8a8"),
+    "fp8a8-rows": config(5, V=3000, d=256, Hq=4, Hkv=1, B=40, L=50, head="fp8a8"),
     # one label (probability 1, always chosen); a 40-token chain beside short labels
     "single-label-bf16": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=64, B=3, L=20,
                                 trie=("explicit", [[4, 2, 7]])),
@@ -140,7 +144,13 @@ def cfg5():
     return cfg, make_inputs(cfg)
 
 
-@pytest.mark.parametrize("which", ["cfg2", "cfg5"])
+@pytest.fixture(scope="module")
+def cfg5a8():
+    cfg = config(5, head="fp8a8")
+    return cfg, make_inputs(cfg)
+
+
+@pytest.mark.parametrize("which", ["cfg2", "cfg5", "cfg5a8"])
 def test_classify_full_size_sampled_docs(dev, which, request):
     """Running-example trie at full size: every label of sampled documents."""
     cfg, inp = request.getfixturevalue(which)

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libtcs.so")
 
 TCS_OK, TCS_EINVAL, TCS_EDUPLICATE, TCS_ECAPACITY, TCS_EUNSUPPORTED, TCS_EHIP, TCS_ENOTIMPL = \
     0, -1, -2, -3, -4, -5, -6
-TCS_F32, TCS_BF16, TCS_FP8_E4M3 = 0, 1, 2
+TCS_F32, TCS_BF16, TCS_FP8_E4M3, TCS_FP8_E4M3_A8 = 0, 1, 2, 3
 DTYPES = {"f32": TCS_F32, "bf16": TCS_BF16, "fp8": TCS_FP8_E4M3}
 
 P32 = C.POINTER(C.c_int32)
@@ -383,14 +383,15 @@ class Model:
         kind = cfg.dtype
         self.cfg = cfg
         self.t = {k: to_device(inp[k], kind, device) for k in ("E", "Wq", "Wk", "Wv", "Wo")}
-        if cfg.head == "fp8":
+        if cfg.head in ("fp8", "fp8a8"):
             self.t["W"] = to_device(inp["W"], "fp8", device)
             self.t["W_scale"] = to_device(inp["W_scale"], "f32", device)
         else:
             self.t["W"] = to_device(inp["W"], kind, device)
             self.t["W_scale"] = None
+        head = {"fp8": TCS_FP8_E4M3, "fp8a8": TCS_FP8_E4M3_A8}.get(cfg.head, DTYPES[kind])
         self.struct = tcs_model(
-            dtype=DTYPES[kind], head_dtype=TCS_FP8_E4M3 if cfg.head == "fp8" else DTYPES[kind],
+            dtype=DTYPES[kind], head_dtype=head,
             d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, hd=cfg.hd, V=cfg.V, eps=eps,
             E=self.t["E"].data_ptr(), Wq=self.t["Wq"].data_ptr(), Wk=self.t["Wk"].data_ptr(),
             Wv=self.t["Wv"].data_ptr(), Wo=self.t["Wo"].data_ptr(), W=self.t["W"].data_ptr(),

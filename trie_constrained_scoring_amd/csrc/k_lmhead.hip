@@ -109,6 +109,11 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
 constexpr int RING_WAVES = 8;
 constexpr int RING_LOADS = 4;   // bf16 operand: 1 KB loads per wave per k-tile
 constexpr int RING_LOADS8 = 2;  // fp8 W: 1 KB loads per wave per k-tile
+// Rows per tile of the W8A8 head (fp8 hidden states): 256 as the other heads, or
+// 128 (one 32-row block per wave), which needs fewer registers but re-reads the
+// weights twice as often (measured on MI355X at 1,024 rows: 0.74 ms with 256, 0.83
+// ms with 128).
+constexpr int A8_TILE_ROWS = 256;
 
 // One bf16 operand k-tile of this wave into an LDS slot: load j (0..3) fills slot
 // rows wave*32 + 8j .. +7 (1 KB), lane i writing 16 bytes at row i/8, position i%8;
@@ -153,9 +158,10 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // v[jn] = acc[t / 16][jn][t % 16] for a wave-uniform t in [0, 64): a binary
 // select tree on the six bits of t (63 selects per jn, six lane masks), so the
 // accumulators are only read in place.
+template <int JN = 2>
 __device__ __forceinline__ void head_pick(int t, const f32x16 (&acc)[4][2], float (&v)[2]) {
 #pragma unroll
-  for (int jn = 0; jn < 2; ++jn) {
+  for (int jn = 0; jn < JN; ++jn) {
     float x[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -175,12 +181,12 @@ __device__ __forceinline__ void head_pick(int t, const f32x16 (&acc)[4][2], floa
 // MASK.  One row at a time, so only that row's 64 values are live.
 // exp2 is the hardware instruction: arguments are <= 0, and terms below 2^-126
 // of the row maximum, which it flushes, are far below fp32 resolution of the sum.
-template <bool MASK>
+template <bool MASK, int JN = 2>
 __device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][2], int vlim,
                                               float2 (&out)[2]) {
   constexpr float LOG2E = 1.4426950408889634f;
 #pragma unroll
-  for (int jn = 0; jn < 2; ++jn) {
+  for (int jn = 0; jn < JN; ++jn) {
     float m = -INFINITY;
 #pragma unroll
     for (int im = 0; im < 4; ++im)
@@ -206,6 +212,7 @@ __device__ __forceinline__ void head_rows_lse(const f32x16 (&acc)[4][2], int vli
 
 // acc[im][jn][e] *= scale of vocabulary entry vb + 32 im + 8 (e>>2) + (e&3) (fp8
 // head); entries at or past V are left alone (the row sums exclude them).
+template <int JN = 2>
 __device__ __forceinline__ void head_scale_rows(f32x16 (&acc)[4][2], const float* __restrict__ w_scale,
                                                 int vb, int V) {
 #pragma unroll
@@ -223,7 +230,7 @@ __device__ __forceinline__ void head_scale_rows(f32x16 (&acc)[4][2], const float
         sc.w = 1.f;
       }
 #pragma unroll
-      for (int jn = 0; jn < 2; ++jn) {
+      for (int jn = 0; jn < JN; ++jn) {
         acc[im][jn][4 * g + 0] *= sc.x;
         acc[im][jn][4 * g + 1] *= sc.y;
         acc[im][jn][4 * g + 2] *= sc.z;
@@ -254,17 +261,23 @@ __device__ __forceinline__ bool gemm_tile_coords(int bid, int n_rt, int n_vt, in
   return t < n_rt * n_vt;
 }
 
-template <bool W8, bool GEMM>
+template <bool W8, bool GEMM, bool A8 = false>
 __device__ __forceinline__ void ring_body(
     int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
-    const float* __restrict__ w_scale, const int32_t* __restrict__ list_head,
+    const float* __restrict__ w_scale, const float* __restrict__ h_scale,
+    const int32_t* __restrict__ list_head,
     const int4* __restrict__ rec, float* __restrict__ raw, float2* __restrict__ part,
     const uint16_t* __restrict__ zero, int rounds_per_wg, const RingGemmOut& go) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[DMA_SLOT_BYTES], st1[DMA_SLOT_BYTES],
       st2[DMA_SLOT_BYTES], st3[DMA_SLOT_BYTES], st4[DMA_SLOT_BYTES];
   uint8_t* const slot[DMA_SLOTS] = {st0, st1, st2, st3, st4};
+  static_assert(!A8 || (W8 && !GEMM), "fp8 activations go with fp8 weights in the head");
   constexpr int WRB = W8 ? 1 : 2;  // bytes per weight element
-  const int n_rt = (R + 255) / 256, n_vt = (V + HEAD_BN - 1) / HEAD_BN;
+  constexpr int HRB = A8 ? 1 : 2;  // bytes per hidden-state element
+  constexpr int TR = A8 ? A8_TILE_ROWS : 256;  // rows per tile
+  constexpr int JN = TR / 128;                 // 32-row blocks per wave
+  const int n_rt = (R + TR - 1) / TR, n_vt = (V + HEAD_BN - 1) / HEAD_BN;
+  const int n_rt256 = (R + 255) / 256;  // row tiles of the gather lists
   // workgroup g takes rounds [w_lo, rounds) of slot g % 256: a bounded run of
   // consecutive rounds, so the workgroups that share operand tiles in an XCD's L2
   // stay within a few rounds of each other
@@ -294,15 +307,16 @@ __device__ __forceinline__ void ring_body(
   // keeps them in scalar registers.)
   struct Span {
     const uint8_t* wb;
-    const uint16_t* hb;
+    const uint8_t* hb;
     int wn, hn;
   };
+  const uint8_t* const hbytes = reinterpret_cast<const uint8_t*>(h);
   auto span = [&](int w) __attribute__((always_inline)) {
     int rt, vt;
     if (w < rounds && coords(w, rt, vt))
-      return Span{W + (size_t)vt * 256 * d * WRB, h + (size_t)rt * 256 * d,
-                  min(256, V - vt * 256) * d * WRB, min(256, R - rt * 256) * d * 2};
-    return Span{W, h, 0, 0};
+      return Span{W + (size_t)vt * 256 * d * WRB, hbytes + (size_t)rt * TR * d * HRB,
+                  min(256, V - vt * 256) * d * WRB, min(TR, R - rt * TR) * d * HRB};
+    return Span{W, hbytes, 0, 0};
   };
 
   // Load j (0..3) of this wave fills slot rows wave*32 + 8j .. +7 (1 KB): lane i
@@ -322,6 +336,15 @@ __device__ __forceinline__ void ring_body(
     vo8[j] = row * d + (((lane & 3) ^ dma8_swz(row & 15)) << 4);
   }
   constexpr int W_LOADS = W8 ? RING_LOADS8 : RING_LOADS;
+  constexpr int H_LOADS = A8 ? TR / 128 : RING_LOADS;
+  // A8 h k-tile (TR rows x 64 bytes): load j of a wave fills rows wave*TR/8 + 16j ..
+  // +15, lane i writing 16 bytes at row i/4, position i%4 (chunk (i%4) ^ dma8_swz(row % 16))
+  int vo8h[TR / 128];
+#pragma unroll
+  for (int j = 0; j < TR / 128; ++j) {
+    const int row = wave * (TR / 8) + 16 * j + (lane >> 2);
+    vo8h[j] = row * d + (((lane & 3) ^ dma8_swz(row & 15)) << 4);
+  }
   int w = next_valid(w_lo);
   if (w >= rounds) return;
   // A tile runs nk5 = nk rounded up to a multiple of 5 steps, so every tile starts
@@ -353,9 +376,19 @@ __device__ __forceinline__ void ring_body(
     const bool nxt = q >= nk5;
     const int k = nxt ? q - nk5 : q;
     const bool pad = k >= nk;
-    const uint16_t* b = s0.hb + (nxt ? dhb : 0);
+    const uint8_t* b = s0.hb + (nxt ? dhb : 0);
     const int n = s0.hn + (nxt ? dhn : 0);
-    head_issue(pad ? zero : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
+    if constexpr (A8) {
+      const void* base = pad ? static_cast<const void*>(zero) : static_cast<const void*>(b);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, pad ? zbytes : n, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < TR / 128; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * (TR / 8) + 16 * j) * 64), 16,
+                                                 vo8h[j], (pad ? 0 : k) * DMA_BK, 0, 0);
+    }
+    else
+      head_issue(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
   };
 
   // h fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32 (bf16 W) or
@@ -438,7 +471,7 @@ __device__ __forceinline__ void ring_body(
       mfma_step(fa[0], fb[0]);
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
-        if (g < RING_LOADS + W_LOADS)
+        if (g < H_LOADS + W_LOADS)
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
         if (W8) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
         else if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
@@ -461,16 +494,75 @@ __device__ __forceinline__ void ring_body(
     if constexpr (!LAST) interleave_ds();
   };
 
+  // fp8 x fp8 (A8): one v_mfma_scale_f32_32x32x64_f8f6f4 per 32x32 block and k-step.
+  // Lane l supplies k 32 (l/32) .. +31 of its row on both operands (16-byte chunks
+  // 2 (l/32) and 2 (l/32) + 1 of the 64-byte slot row); any k order shared by the
+  // two operands gives the same dot products.
+  int fq[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) fq[t] = (lane & 31) * 64 + (((2 * (lane >> 5) + t) ^ dma8_swz(lane & 15)) << 4);
+  v8i_t wf[4], hf[JN];  // W fragments (vocabulary blocks) and the h fragments of this step
+  auto frag8 = [&](const uint8_t* base) __attribute__((always_inline)) {
+    const uint4 x = *reinterpret_cast<const uint4*>(base + fq[0]);
+    const uint4 y = *reinterpret_cast<const uint4*>(base + fq[1]);
+    return v8i_t{int(x.x), int(x.y), int(x.z), int(x.w), int(y.x), int(y.y), int(y.z), int(y.w)};
+  };
+  auto mfma8 = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < JN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], hf[j], acc[i][j], 0, 0, 0, 127,
+                                                                 0, 127);
+  };
+  // one k-step g: W(g) blocks 2-3 are read while blocks 0-1 are multiplied (their
+  // fragments and h(g)'s were read in the previous step); after the barrier the
+  // next step's W blocks 0-1 are read while blocks 2-3 are multiplied, then h(g+1).
+  auto step8 = [&](auto Uc, int kt, auto Lc) __attribute__((always_inline)) {
+    constexpr int U = decltype(Uc)::value;
+    constexpr bool LAST = decltype(Lc)::value;
+    constexpr int sA = (2 * U) % 5;
+    constexpr int sB1 = (2 * U + 3) % 5, sA1 = (2 * U + 2) % 5, sA2 = (2 * U + 4) % 5;
+    issue_h(kt + 1, slot[sB1]);  // h(g+1)
+    issue_w(kt + 2, slot[sA2]);  // W(g+2)
+    wf[2] = frag8(slot[sA] + (wm * 128 + 64) * 64);
+    wf[3] = frag8(slot[sA] + (wm * 128 + 96) * 64);
+    mfma8(0);
+    mfma8(1);
+    wait_vmcnt<W_LOADS>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) {
+      wf[0] = frag8(slot[sA1] + (wm * 128 + 0) * 64);
+      wf[1] = frag8(slot[sA1] + (wm * 128 + 32) * 64);
+    }
+    mfma8(2);
+    mfma8(3);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) {  // after blocks 2-3 issued
+#pragma unroll
+      for (int j = 0; j < JN; ++j) hf[j] = frag8(slot[sB1] + (wr * 32 * JN + 32 * j) * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // fragments of a tile's first step: W(0) blocks 0-1 in slot 0, h(0) in slot 1
+  auto first_frags8 = [&]() __attribute__((always_inline)) {
+    wf[0] = frag8(slot[0] + (wm * 128) * 64);
+    wf[1] = frag8(slot[0] + (wm * 128 + 32) * 64);
+#pragma unroll
+    for (int j = 0; j < JN; ++j) hf[j] = frag8(slot[1] + (wr * 32 * JN + 32 * j) * 64);
+  };
+
   // prologue: W(0), h(0), W(1)
   issue_w(0, slot[0]);
   issue_h(0, slot[1]);
   issue_w(1, slot[2]);
   wait_vmcnt<W_LOADS>();
   __builtin_amdgcn_s_barrier();
-  read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
+  if constexpr (A8) first_frags8();
+  else read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
 
   const int vhalf = wm * 128 + 4 * (lane >> 5);  // + 32 im + 8 (e>>2) + (e&3)
-  const int rloc = wr * 64 + (lane & 31);        // + 32 jn
+  const int rloc = wr * 32 * JN + (lane & 31);   // + 32 jn
   for (; w < rounds;) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -480,23 +572,39 @@ __device__ __forceinline__ void ring_body(
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     using F = std::false_type;
     int kt = 0;
-    for (; kt + 5 < nk5; kt += 5) {
+    if constexpr (A8) {
+#pragma unroll 1
+      for (; kt + 5 < nk5; kt += 5) {
+        step8(std::integral_constant<int, 0>{}, kt, F{});
+        step8(std::integral_constant<int, 1>{}, kt + 1, F{});
+        step8(std::integral_constant<int, 2>{}, kt + 2, F{});
+        step8(std::integral_constant<int, 3>{}, kt + 3, F{});
+        step8(std::integral_constant<int, 4>{}, kt + 4, F{});
+      }
+      step8(std::integral_constant<int, 0>{}, kt, F{});
+      step8(std::integral_constant<int, 1>{}, kt + 1, F{});
+      step8(std::integral_constant<int, 2>{}, kt + 2, F{});
+      step8(std::integral_constant<int, 3>{}, kt + 3, F{});
+      step8(std::integral_constant<int, 4>{}, kt + 4, std::true_type{});
+    } else {
+      for (; kt + 5 < nk5; kt += 5) {
+        step(std::integral_constant<int, 0>{}, kt, F{});
+        step(std::integral_constant<int, 1>{}, kt + 1, F{});
+        step(std::integral_constant<int, 2>{}, kt + 2, F{});
+        step(std::integral_constant<int, 3>{}, kt + 3, F{});
+        step(std::integral_constant<int, 4>{}, kt + 4, F{});
+      }
       step(std::integral_constant<int, 0>{}, kt, F{});
       step(std::integral_constant<int, 1>{}, kt + 1, F{});
       step(std::integral_constant<int, 2>{}, kt + 2, F{});
       step(std::integral_constant<int, 3>{}, kt + 3, F{});
-      step(std::integral_constant<int, 4>{}, kt + 4, F{});
+      step(std::integral_constant<int, 4>{}, kt + 4, std::true_type{});
     }
-    step(std::integral_constant<int, 0>{}, kt, F{});
-    step(std::integral_constant<int, 1>{}, kt + 1, F{});
-    step(std::integral_constant<int, 2>{}, kt + 2, F{});
-    step(std::integral_constant<int, 3>{}, kt + 3, F{});
-    step(std::integral_constant<int, 4>{}, kt + 4, std::true_type{});
 
     // ---- epilogue of tile w (no LDS: the ring keeps loading the next tile) ----
     int rt, vt;
     coords(w, rt, vt);
-    const int r0 = rt * 256, v0 = vt * HEAD_BN;
+    const int r0 = rt * TR, v0 = vt * HEAD_BN;
     // acc[im][jn][e]: vocabulary v0 + vhalf + 32 im + 8 (e>>2) + (e&3); hidden row
     // r0 + rloc + 32 jn
     if constexpr (GEMM) {
@@ -526,18 +634,32 @@ __device__ __forceinline__ void ring_body(
           }
       }
     } else {
-    if constexpr (W8) head_scale_rows(acc, w_scale, v0 + vhalf, V);
+    if constexpr (W8) head_scale_rows<JN>(acc, w_scale, v0 + vhalf, V);
+    if constexpr (A8) {  // each hidden row's own activation scale
+#pragma unroll
+      for (int jn = 0; jn < JN; ++jn) {
+        const int r = r0 + rloc + 32 * jn;
+        const float hs = r < R ? h_scale[r] : 0.f;
+#pragma unroll
+        for (int im = 0; im < 4; ++im)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[im][jn][e] *= hs;
+      }
+    }
     // entries at or past V (last vocabulary tile) drop out of the row sums; the
     // accumulators are only read from here on
     const int vlim = V - v0 - vhalf;  // entry (im, e) is valid iff 32 im + 8 (e>>2) + (e&3) < vlim
     // child-token gather: walk this half-tile's list for this row tile (scalar)
-    for (int k = list_head[(2 * vt + wm) * n_rt + rt]; k >= 0;) {
+    // (the lists are per 256-row tile: rit is the row within it)
+    for (int k = list_head[(2 * vt + wm) * n_rt256 + (TR == 128 ? rt >> 1 : rt)]; k >= 0;) {
       const int4 q = rec[k];
       const int t = q.z & 63, hh = (q.z >> 6) & 1, rit = q.z >> 7;
-      if ((rit >> 6) == wr) {  // row r0 + rit is in this wave's quarter of the rows
+      // row r0 + (rit mod TR) is in this wave's share of the tile's rows
+      const bool mine = TR == 128 ? ((rit >> 7) == (rt & 1) && ((rit >> 5) & 3) == wr) : (rit >> 6) == wr;
+      if (mine) {
         float v[2];
-        head_pick(t, acc, v);
-        const float x = ((rit >> 5) & 1) ? v[1] : v[0];
+        head_pick<JN>(t, acc, v);
+        const float x = (JN == 2 && ((rit >> 5) & 1)) ? v[1] : v[0];
         if (lane == (rit & 31) + 32 * hh) raw[q.y] = x;
       }
       k = q.x;
@@ -545,10 +667,10 @@ __device__ __forceinline__ void ring_body(
     // per hidden row: max and sum of exp over this wave's 128 vocabulary entries
     // (only the last vocabulary tile has entries at or past V)
     float2 ms[2];
-    if (v0 + HEAD_BN <= V) head_rows_lse<false>(acc, vlim, ms);
-    else head_rows_lse<true>(acc, vlim, ms);
+    if (v0 + HEAD_BN <= V) head_rows_lse<false, JN>(acc, vlim, ms);
+    else head_rows_lse<true, JN>(acc, vlim, ms);
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
+    for (int jn = 0; jn < JN; ++jn) {
       const int r = r0 + rloc + 32 * jn;
       // few rows: partials [row][half-tile], so each row's are contiguous for the
       // finalisation; else [half-tile][row]
@@ -558,7 +680,11 @@ __device__ __forceinline__ void ring_body(
     }
     }
     // the next tile's W(0) and h(0) are in slots 0 and 1 (landed at the last barrier)
-    read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
+    if constexpr (A8) {
+      __builtin_amdgcn_sched_barrier(0);  // the epilogue's registers are free first
+      first_frags8();
+    }
+    else read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
     w = w1;
     w1 = next_valid(w1 + 1);
     s0 = s1;
@@ -571,15 +697,15 @@ __device__ __forceinline__ void ring_body(
   wait_vmcnt<0>();  // loads past the last tile: nothing may still target LDS at exit
 }
 
-// The output head (bf16 or fp8 weights).
-template <bool W8>
+// The output head (bf16 or fp8 weights; A8: fp8 hidden states with row scales).
+template <bool W8, bool A8 = false>
 __global__ __launch_bounds__(64 * RING_WAVES, 1) void lmhead_ring_kernel(
     int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
-    const float* __restrict__ w_scale, const int32_t* __restrict__ list_head,
-    const int4* __restrict__ rec, float* __restrict__ raw, float2* __restrict__ part,
-    const uint16_t* __restrict__ zero, int rounds_per_wg) {
-  ring_body<W8, false>(R, V, d, h, W, w_scale, list_head, rec, raw, part, zero, rounds_per_wg,
-                       RingGemmOut{});
+    const float* __restrict__ w_scale, const float* __restrict__ h_scale,
+    const int32_t* __restrict__ list_head, const int4* __restrict__ rec, float* __restrict__ raw,
+    float2* __restrict__ part, const uint16_t* __restrict__ zero, int rounds_per_wg) {
+  ring_body<W8, false, A8>(R, V, d, h, W, w_scale, h_scale, list_head, rec, raw, part, zero,
+                           rounds_per_wg, RingGemmOut{});
 }
 
 // The output projection of many rows (plain products plus the embedding residual).
@@ -588,7 +714,7 @@ __global__ __launch_bounds__(64 * RING_WAVES, 1) void proj_ring_kernel(int M, in
                                                            const uint8_t* __restrict__ B,
                                                            const uint16_t* __restrict__ zero,
                                                            int rounds_per_wg, RingGemmOut go) {
-  ring_body<false, true>(M, N, K, A, B, nullptr, nullptr, nullptr, nullptr, nullptr, zero,
+  ring_body<false, true>(M, N, K, A, B, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, zero,
                          rounds_per_wg, go);
 }
 
@@ -821,11 +947,64 @@ int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int
   return TCS_OK;
 }
 
+// E4M3FN code of a finite fp32 value: the nearest E4M3 value, ties to the even
+// code (rintf rounds half to even), magnitudes from 448 up saturating to 448.
+__device__ __forceinline__ uint32_t e4m3_rne(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 31) << 7;
+  const float a = fabsf(q);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7E;
+  } else if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (8 steps is the smallest normal)
+    code = uint32_t(rintf(a * 512.0f));
+  } else {  // a in [2^E, 2^(E+1)), E in [-6, 8]: mantissa steps of 2^(E-3)
+    const int E = int((__float_as_uint(a) >> 23) & 0xFF) - 127;
+    const float m = rintf(a * __uint_as_float(uint32_t(127 - E) << 23) * 8.0f) - 8.0f;  // 0..8
+    code = uint32_t((E + 7) * 8 + int(m));  // m = 8 carries into the exponent
+  }
+  return code | sign;
+}
+
+// One wave per hidden row: s = max|h| / 448 and codes E4M3(h / s), both divisions
+// correctly rounded; an all-zero row gets s = 0 and zero codes.  d % 4 == 0.
+__global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(int R, int d, const uint16_t* __restrict__ h,
+                                                              uint32_t* __restrict__ q,
+                                                              float* __restrict__ scale) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= R) return;
+  const uint2* hr = reinterpret_cast<const uint2*>(h + (size_t)row * d);
+  float amax = 0.f;
+  for (int k4 = lane; k4 < d / 4; k4 += 64) {
+    const uint2 v = hr[k4];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_to_f32(uint16_t(v.x))), fabsf(bf16_to_f32(uint16_t(v.x >> 16)))),
+                             fmaxf(fabsf(bf16_to_f32(uint16_t(v.y))), fabsf(bf16_to_f32(uint16_t(v.y >> 16))))));
+  }
+  amax = wave_max(amax);
+  const float s = __fdiv_rn(amax, 448.0f);
+  if (lane == 0) scale[row] = s;
+  uint32_t* qr = q + (size_t)row * (d / 4);
+  for (int k4 = lane; k4 < d / 4; k4 += 64) {
+    const uint2 v = hr[k4];
+    const float x[4] = {bf16_to_f32(uint16_t(v.x)), bf16_to_f32(uint16_t(v.x >> 16)),
+                        bf16_to_f32(uint16_t(v.y)), bf16_to_f32(uint16_t(v.y >> 16))};
+    uint32_t packed = 0;
+    if (s > 0.f) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) packed |= e4m3_rne(__fdiv_rn(x[t], s)) << (8 * t);
+    }
+    qr[k4] = packed;
+  }
+}
+
+size_t lmhead_act8_bytes(tcs_dtype w_dtype, int32_t R, int32_t d) {
+  return w_dtype == TCS_FP8_E4M3_A8 ? align_up(size_t(R) * d) + align_up(size_t(R) * 4) : 0;
+}
+
 int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
                       int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                       const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
                       const int32_t* e_child, float* lse, float* lp, const void* prep, void* part,
-                      bool finalize_lp) {
+                      bool finalize_lp, void* act8) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = B * n_int;
   if (R <= 0) return TCS_OK;
@@ -838,16 +1017,27 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
   timer_begin(TCS_TIMER_HEAD, stream);
   if (h_dtype == TCS_BF16) {
     if (d % 64 != 0) return fail(TCS_EUNSUPPORTED, "lmhead: d=%d is not a multiple of 64", d);
-    const int rounds = head_grid(n_rt, n_tiles) / HEAD_WGS;
+    // the W8A8 head's tiles have A8_TILE_ROWS rows (see ring_body)
+    const int n_rt_k = w_dtype == TCS_FP8_E4M3_A8 ? (R + A8_TILE_ROWS - 1) / A8_TILE_ROWS : n_rt;
+    const int rounds = head_grid(n_rt_k, n_tiles) / HEAD_WGS;
     const int per = head_rounds_per_wg(rounds);
     const int grid = (rounds + per - 1) / per * HEAD_WGS;
     auto hp = static_cast<const uint16_t*>(h);
     auto wp = static_cast<const uint8_t*>(W);
     auto zp = reinterpret_cast<const uint16_t*>(P.zero);
-    if (w_dtype == TCS_FP8_E4M3)
-      lmhead_ring_kernel<true><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, w_scale, P.list_head, P.rec, lp, p, zp, per);
-    else
-      lmhead_ring_kernel<false><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, nullptr, P.list_head, P.rec, lp, p, zp, per);
+    if (w_dtype == TCS_FP8_E4M3_A8) {
+      if (!act8) return fail(TCS_EINVAL, "lmhead: W8A8 head without its activation buffer");
+      auto codes = static_cast<uint32_t*>(act8);
+      auto hs = reinterpret_cast<float*>(static_cast<char*>(act8) + align_up(size_t(R) * d));
+      quant_rows_e4m3_kernel<<<(R + 3) / 4, 256, 0, s>>>(R, d, hp, codes, hs);
+      lmhead_ring_kernel<true, true><<<grid, 64 * RING_WAVES, 0, s>>>(
+          R, V, d, reinterpret_cast<const uint16_t*>(codes), wp, w_scale, hs, P.list_head, P.rec, lp,
+          p, zp, per);
+    } else if (w_dtype == TCS_FP8_E4M3) {
+      lmhead_ring_kernel<true><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, w_scale, nullptr, P.list_head, P.rec, lp, p, zp, per);
+    } else {
+      lmhead_ring_kernel<false><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, nullptr, nullptr, P.list_head, P.rec, lp, p, zp, per);
+    }
     n_parts = 2 * n_tiles;
   } else {
     dim3 grid(n_tiles, (R + 7) / 8);

@@ -165,7 +165,7 @@ static PrepLayout prep_layout(const tcs_model* m, const tcs_trie_dev* t, int32_t
 // Per-batch workspace (tcs_classify_run).
 struct RunLayout {
   size_t total;
-  void *a_doc, *Kd, *Vd, *O, *h, *part, *ll;
+  void *a_doc, *Kd, *Vd, *O, *h, *part, *ll, *act8;
   float *y, *lse, *lp;
 };
 
@@ -188,6 +188,7 @@ static RunLayout run_layout(const tcs_model* m, const tcs_trie_dev* t, const tcs
   L.lse = c.take<float>(R);
   L.lp = c.take<float>(size_t(d->B) * t->n_nodes);
   L.ll = c.take<float>(size_t(d->B) * t->n_labels);
+  L.act8 = c.take<char>(lmhead_act8_bytes(m->head_dtype, int32_t(R), m->d));
   L.total = c.used;
   return L;
 }
@@ -195,14 +196,15 @@ static RunLayout run_layout(const tcs_model* m, const tcs_trie_dev* t, const tcs
 static int check_classify(const tcs_model* m, const tcs_trie_dev* t, const tcs_docs* d) {
   if (!m || !t || !d) return fail(TCS_EINVAL, "classify: null model/trie/docs");
   if (int rc = check_attn_dims(m->dtype, m->Hq, m->Hkv, m->hd)) return rc;
-  if (!(m->head_dtype == m->dtype || (m->dtype == TCS_BF16 && m->head_dtype == TCS_FP8_E4M3)))
+  if (!(m->head_dtype == m->dtype ||
+        (m->dtype == TCS_BF16 && (m->head_dtype == TCS_FP8_E4M3 || m->head_dtype == TCS_FP8_E4M3_A8))))
     return fail(TCS_EUNSUPPORTED, "classify: head dtype %d with model dtype %d", int(m->head_dtype),
                 int(m->dtype));
   if (m->d < 1 || m->V < 1) return fail(TCS_EINVAL, "classify: d=%d V=%d", m->d, m->V);
   if (m->dtype == TCS_BF16 && m->d % 64 != 0)
     return fail(TCS_EUNSUPPORTED, "classify: bf16 model needs d %% 64 == 0 (d=%d)", m->d);
   if (!m->E || !m->Wq || !m->Wk || !m->Wv || !m->Wo || !m->W ||
-      (m->head_dtype == TCS_FP8_E4M3 && !m->W_scale))
+      ((m->head_dtype == TCS_FP8_E4M3 || m->head_dtype == TCS_FP8_E4M3_A8) && !m->W_scale))
     return fail(TCS_EINVAL, "classify: null weight pointer");
   if (t->n_nodes < 2 || t->n_int < 1 || t->n_labels < 1)
     return fail(TCS_EINVAL, "classify: trie with %d nodes, %d rows, %d labels", t->n_nodes, t->n_int,
@@ -300,7 +302,7 @@ static int run_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, con
   // the head leaves raw child logits in lp; the path sum subtracts lse itself
   if ((rc = launch_lmhead_run(stream, dt, m->head_dtype, B, n_int, t->n_nodes, m->d, m->V, L.h, m->W,
                               m->W_scale, t->e_tok, t->e_qrow, t->e_child, L.lse, L.lp, P.head,
-                              L.part, false))) return rc;
+                              L.part, false, L.act8))) return rc;
   return launch_path_sum(stream, B, t, L.lp, ll ? ll : static_cast<float*>(L.ll), prob, label,
                          L.lse, P.node_qrow);
 }
@@ -354,6 +356,8 @@ int tcs_letters_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t
   if (t->max_depth != 1 || t->n_int != 1)
     return fail(TCS_EINVAL, "letters: the trie must hold one-token labels only (depth %d, %d rows)",
                 t->max_depth, t->n_int);
+  if (m->head_dtype == TCS_FP8_E4M3_A8)
+    return fail(TCS_EUNSUPPORTED, "letters: fp8 activations are for the full-vocabulary head only");
   if (d->B == 0) return TCS_OK;
   if (!label) return fail(TCS_EINVAL, "letters: null label output");
   if (!prep || !prep->buf) return fail(TCS_EINVAL, "letters: null prepared state");
@@ -415,6 +419,8 @@ static int check_decode(const tcs_model* m, const tcs_trie_dev* t, const tcs_doc
     return fail(TCS_EINVAL, "decode: max_children %d outside [1, %d)", t->max_children, t->n_nodes);
   if (m->dtype == TCS_BF16 && (m->hd != 128 || m->Hq / m->Hkv > 64))
     return fail(TCS_EUNSUPPORTED, "decode: bf16 models need head_dim 128 (hd=%d)", m->hd);
+  if (m->head_dtype == TCS_FP8_E4M3_A8)
+    return fail(TCS_EUNSUPPORTED, "decode: fp8 activations are for the full-vocabulary head only");
   return TCS_OK;
 }
 

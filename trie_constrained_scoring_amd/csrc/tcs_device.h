@@ -13,6 +13,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));  // 32 fp8 codes: one fp8 MFMA operand
 
 // Storage tags: the kernels move bf16 as raw 16-bit patterns.
 struct bf16_t {

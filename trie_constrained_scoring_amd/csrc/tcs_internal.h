@@ -95,7 +95,10 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
                       int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                       const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
                       const int32_t* e_child, float* lse, float* lp, const void* prep, void* part,
-                      bool finalize_lp = true);
+                      bool finalize_lp = true, void* act8 = nullptr);
+// Scratch of a W8A8 head (w_dtype TCS_FP8_E4M3_A8): the hidden rows' E4M3 codes and
+// scales; 0 for other heads.
+size_t lmhead_act8_bytes(tcs_dtype w_dtype, int32_t R, int32_t d);
 int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
                   int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                   const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
