@@ -264,7 +264,9 @@ int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie,
  */
 typedef struct {
   tcs_dtype dtype;       /* TCS_F32 or TCS_BF16: E, Wq, Wk, Wv, Wo and activations */
-  tcs_dtype head_dtype;  /* dtype, or TCS_FP8_E4M3 (bf16 models) */
+  tcs_dtype head_dtype;  /* dtype, or for bf16 models TCS_FP8_E4M3 (W8A16) or TCS_FP8_E4M3_A8
+                            (W8A8: tcs_classify / tcs_classify_run only; tcs_letters_run and
+                            tcs_decode_run answer TCS_EUNSUPPORTED) */
   int32_t d, Hq, Hkv, hd, V;
   float eps;
   const void* E;         /* [V, d] token embeddings */
