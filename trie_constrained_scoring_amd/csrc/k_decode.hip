@@ -48,24 +48,45 @@ __device__ __forceinline__ unsigned long long pick_key(float z, int i) {
 }
 
 // Workgroup (a, y) for slot a < *n_sel scores children y*CH .. y*CH+CH-1 of the
-// slot's node u = row_node[a] (one wave per child in turn): the hidden state h[a]
-// against the children's head rows.  Each workgroup folds its best (logit, child)
-// into the slot's key with a 64-bit atomic max; the next launch reads the keys.
+// slot's node u = row_node[a] (one wave per child in turn).  It first forms the
+// slot's hidden state in LDS from the projection's fp32 partials: y = their sum
+// (in partial order), h = y / sqrt(mean(y^2) + eps), stored as the model dtype
+// (bf16: nearest-even), as the RMSNorm of the classify pass does.  Then h against
+// the children's head rows; each workgroup folds its best (logit, child) into the
+// slot's key with a 64-bit atomic max, and the next launch reads the keys.
 constexpr int STEP_CH = 32;  // children per workgroup: 8 per wave
 template <int WK>
 __global__ __launch_bounds__(256) void decode_logits_kernel(
-    int d, const void* __restrict__ h, const void* __restrict__ W,
+    int B, int d, int n_part, float eps, const float* __restrict__ y, const void* __restrict__ W,
     const float* __restrict__ w_scale, const int32_t* __restrict__ token,
     const int32_t* __restrict__ child_begin, const int32_t* __restrict__ child_count,
     const int32_t* __restrict__ row_node, const int32_t* __restrict__ n_sel,
     unsigned long long* __restrict__ best_key) {
+  extern __shared__ __attribute__((aligned(16))) float ys[];  // [d] fp32, then h [d]
   __shared__ unsigned long long bk[4];
+  __shared__ float red[4];
   const int a = blockIdx.x;
   if (a >= *n_sel) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float ss = 0.f;
+  for (int k = tid; k < d; k += 256) {
+    float v = y[size_t(a) * d + k];
+    for (int p = 1; p < n_part; ++p) v += y[(size_t(p) * B + a) * d + k];
+    ys[k] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float rs = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / float(d) + eps);
+  void* hr = ys + d;
+  for (int k = tid; k < d; k += 256) {
+    if constexpr (WK == 0) static_cast<float*>(hr)[k] = ys[k] * rs;
+    else static_cast<uint16_t*>(hr)[k] = f32_to_bf16(ys[k] * rs);
+  }
+  __syncthreads();
   const int u = row_node[a];
   const int c0 = child_begin[u], nc = child_count[u];
-  const void* hr = static_cast<const char*>(h) + size_t(a) * d * (WK == 0 ? 4 : 2);
   unsigned long long key = 0;  // below every real key
   const int i_end = min(nc, int(blockIdx.y + 1) * STEP_CH);
   for (int i = int(blockIdx.y) * STEP_CH + wave; i < i_end; i += 4) {
@@ -154,7 +175,8 @@ int launch_decode_init(void* stream, int32_t B, const int32_t* dec_node, const i
 }
 
 int launch_decode_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
-                         int32_t d, const void* h, const void* W, const float* w_scale,
+                         int32_t d, int32_t n_part, float eps, const float* y, const void* W,
+                         const float* w_scale,
                          const int32_t* token, const int32_t* child_begin,
                          const int32_t* child_count, const int32_t* row_node, const int32_t* n_sel,
                          int32_t max_children, unsigned long long* best_key) {
@@ -165,9 +187,12 @@ int launch_decode_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int
   if (max_children < 1) return fail(TCS_EINVAL, "decode: max_children %d", max_children);
   const dim3 grid(B, (max_children + STEP_CH - 1) / STEP_CH);
   if (grid.y > 65535) return fail(TCS_EUNSUPPORTED, "decode: %d children", max_children);
-#define TCS_STEP(WK)                                                                       \
-  decode_logits_kernel<WK><<<grid, 256, 0, s>>>(d, h, W, w_scale, token, child_begin,      \
-                                                child_count, row_node, n_sel, best_key)
+  const size_t lds = size_t(d) * (4 + (h_dtype == TCS_F32 ? 4 : 2));
+  if (lds > 64 * 1024) return fail(TCS_EUNSUPPORTED, "decode: d=%d too wide", d);
+#define TCS_STEP(WK)                                                                           \
+  decode_logits_kernel<WK><<<grid, 256, lds, s>>>(B, d, n_part, eps, y, W, w_scale, token,     \
+                                                  child_begin, child_count, row_node, n_sel,   \
+                                                  best_key)
   if (h_dtype == TCS_F32 && w_dtype == TCS_F32)
     TCS_STEP(0);
   else if (h_dtype == TCS_BF16 && w_dtype == TCS_BF16)

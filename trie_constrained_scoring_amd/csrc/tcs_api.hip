@@ -373,11 +373,11 @@ int tcs_letters_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t
 // ---------------------------------------------------------------- trie_decode
 
 // Per-batch workspace of tcs_decode_run: document K/V (token documents), then per
-// slot the attention output, projection partials and hidden state, and the
-// per-document decoding state.
+// slot the attention output and the projection partials, and the per-document
+// decoding state.
 struct DecodeLayout {
   size_t total;
-  void *a_doc, *Kd, *Vd, *O, *h;
+  void *a_doc, *Kd, *Vd, *O;
   float* y;
   int32_t *cur, *sel, *row_node, *n_sel, *runs;
   unsigned long long* best_key;
@@ -397,7 +397,6 @@ static DecodeLayout decode_layout(const tcs_model* m, const tcs_docs* d, void* w
   }
   L.O = c.take<char>(B * qd * es);
   L.y = c.take<float>(B * m->d * gemm_resid_splits(m->dtype, int32_t(B), m->d, int32_t(qd)));
-  L.h = c.take<char>(B * m->d * es);
   L.cur = c.take<int32_t>(B);
   L.sel = c.take<int32_t>(2 * B);
   L.row_node = c.take<int32_t>(B);
@@ -483,8 +482,8 @@ int tcs_decode_run(tcs_stream stream, const tcs_model* m, const tcs_trie_dev* t,
     if (rc) return rc;
     if ((rc = launch_gemm_nt(stream, dt, GEMM_RESID, B, m->d, qd, L.O, qd, m->Wo, qd, L.y, m->d,
                              &res))) return rc;
-    if ((rc = launch_rownorm(stream, dt, L.y, B, m->d, splits, m->eps, L.h, L.n_sel))) return rc;
-    if ((rc = launch_decode_logits(stream, dt, m->head_dtype, B, m->d, L.h, m->W, m->W_scale,
+    if ((rc = launch_decode_logits(stream, dt, m->head_dtype, B, m->d, splits, m->eps, L.y, m->W,
+                                   m->W_scale,
                                    t->token, t->child_begin, t->child_count, L.row_node, L.n_sel,
                                    t->max_children, L.best_key))) return rc;
     if ((rc = launch_decode_advance(stream, B, t->child_begin, t->dec_node, t->sub_label, t->qrow,

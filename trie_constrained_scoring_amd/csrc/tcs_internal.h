@@ -115,8 +115,10 @@ int launch_decode_init(void* stream, int32_t B, const int32_t* dec_node, const i
                        const int32_t* qrow, int32_t* cur, int32_t* label, int32_t* runs,
                        int32_t* sel, int32_t* row_node, int32_t* n_sel,
                        unsigned long long* best_key);
+// y: the projection's fp32 partials [n_part][B][d] (RMSNorm applied in the kernel).
 int launch_decode_logits(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
-                         int32_t d, const void* h, const void* W, const float* w_scale,
+                         int32_t d, int32_t n_part, float eps, const float* y, const void* W,
+                         const float* w_scale,
                          const int32_t* token, const int32_t* child_begin,
                          const int32_t* child_count, const int32_t* row_node, const int32_t* n_sel,
                          int32_t max_children, unsigned long long* best_key);
