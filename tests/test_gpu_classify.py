@@ -150,7 +150,27 @@ def cfg5a8():
     return cfg, make_inputs(cfg)
 
 
-@pytest.mark.parametrize("which", ["cfg2", "cfg5", "cfg5a8"])
+@pytest.fixture(scope="module")
+def cfg2b32():
+    cfg = config(2, B=32)
+    return cfg, make_inputs(cfg)
+
+
+@pytest.fixture(scope="module")
+def cfg5b16():
+    cfg = config(5, B=16)
+    return cfg, make_inputs(cfg)
+
+
+@pytest.fixture(scope="module")
+def cfg5a8b16():
+    cfg = config(5, B=16, head="fp8a8")
+    return cfg, make_inputs(cfg)
+
+
+# cfg2b32 (256 head rows) and the B = 16 cases (128 rows) run the head on 128-row
+# tiles over the full vocabulary; the others on 256-row tiles
+@pytest.mark.parametrize("which", ["cfg2", "cfg5", "cfg5a8", "cfg2b32", "cfg5b16", "cfg5a8b16"])
 def test_classify_full_size_sampled_docs(dev, which, request):
     """Running-example trie at full size: every label of sampled documents."""
     cfg, inp = request.getfixturevalue(which)

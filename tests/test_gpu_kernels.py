@@ -126,12 +126,13 @@ HEAD_CASES = {
     "small-fp8": dict(V=777, d=192, labels=("zipf", 40, 2, 6, 1.2), B=9, head="fp8"),
     "small-f32": dict(V=1000, d=64, labels=("running",), B=4, head="f32"),
     "ragged-vocab": dict(V=257, d=64, labels=("zipf", 12, 1, 4, 1.0), B=3, head="bf16"),
-    # row-tile counts (72 rows per document) for the head's tile order: 16 tiles (two
-    # strips of 8), 39 (one group of 32 + a 7-row strip), 73 (two groups + strips of
-    # 5 and 4)
-    "rows-16-tiles": dict(V=1000, d=128, labels=("zipf", 40, 2, 6, 1.2), B=56, head="bf16"),
-    "rows-39-tiles": dict(V=1000, d=128, labels=("zipf", 40, 2, 6, 1.2), B=138, head="bf16"),
-    "rows-73-tiles-fp8": dict(V=777, d=192, labels=("zipf", 40, 2, 6, 1.2), B=259, head="fp8"),
+    # row-tile counts (72 rows per document) for the head's tile order, in the tile
+    # size the launcher picks for these vocabularies: 32 tiles of 128 rows (one group
+    # of 32), 39 of 256 (one group of 32 + a 7-row strip), 146 of 128 (four groups +
+    # strips of 6 and 6 and 6)
+    "rows-56-docs": dict(V=1000, d=128, labels=("zipf", 40, 2, 6, 1.2), B=56, head="bf16"),
+    "rows-138-docs": dict(V=1000, d=128, labels=("zipf", 40, 2, 6, 1.2), B=138, head="bf16"),
+    "rows-259-docs-fp8": dict(V=777, d=192, labels=("zipf", 40, 2, 6, 1.2), B=259, head="fp8"),
 }
 
 

@@ -109,24 +109,24 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
 constexpr int RING_WAVES = 8;
 constexpr int RING_LOADS = 4;   // bf16 operand: 1 KB loads per wave per k-tile
 constexpr int RING_LOADS8 = 2;  // fp8 W: 1 KB loads per wave per k-tile
-// Rows per tile of the W8A8 head (fp8 hidden states): 256 as the other heads, or
-// 128 (one 32-row block per wave), which needs fewer registers but re-reads the
-// weights twice as often (measured on MI355X at 1,024 rows: 0.74 ms with 256, 0.83
-// ms with 128).
-constexpr int A8_TILE_ROWS = 256;
+// Rows per tile of the head: 256, or 128 (one 32-row block per wave).  A 128-row
+// tile reads the weights once per 128 rows instead of per 256 and each wave's
+// fragment reads feed 4 matrix ops instead of 8, so it costs more per product,
+// but it pads fewer rows and gives the chip more tiles when the rows are few
+// (the launcher's choice is head_tile_rows).
 
-// One bf16 operand k-tile of this wave into an LDS slot: load j (0..3) fills slot
-// rows wave*32 + 8j .. +7 (1 KB), lane i writing 16 bytes at row i/8, position i%8;
+// NL bf16 loads (1 KB each) of an operand k-tile into an LDS slot: load j fills
+// slot rows row0 + 8j .. +7, lane i writing 16 bytes at row i/8, position i%8;
 // `vo` holds each load's lane byte offset, `k` the k-tile (scalar offset).
-__device__ __forceinline__ void head_issue(const void* base, int bytes, int k, uint8_t* sl,
-                                           int wave, const int (&vo)[RING_LOADS]) {
+template <int NL>
+__device__ __forceinline__ void head_issue(const void* base, int bytes, int k, uint8_t* sl, int row0,
+                                           const int* vo) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
   const int so = k * DMA_BK * 2;
 #pragma unroll
-  for (int j = 0; j < RING_LOADS; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * 32 + j * 8) * 128), 16, vo[j],
-                                             so, 0, 0);
+  for (int j = 0; j < NL; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (row0 + j * 8) * 128), 16, vo[j], so, 0, 0);
 }
 
 // fp8 W k-tile (256 rows x 64 bytes, 16 KB) of this wave: load j (0..1) fills slot
@@ -261,7 +261,7 @@ __device__ __forceinline__ bool gemm_tile_coords(int bid, int n_rt, int n_vt, in
   return t < n_rt * n_vt;
 }
 
-template <bool W8, bool GEMM, bool A8 = false>
+template <bool W8, bool GEMM, bool A8 = false, int TR = 256>
 __device__ __forceinline__ void ring_body(
     int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
     const float* __restrict__ w_scale, const float* __restrict__ h_scale,
@@ -272,10 +272,10 @@ __device__ __forceinline__ void ring_body(
       st2[DMA_SLOT_BYTES], st3[DMA_SLOT_BYTES], st4[DMA_SLOT_BYTES];
   uint8_t* const slot[DMA_SLOTS] = {st0, st1, st2, st3, st4};
   static_assert(!A8 || (W8 && !GEMM), "fp8 activations go with fp8 weights in the head");
+  static_assert(TR == 256 || (TR == 128 && !GEMM), "rows per tile: 256, or 128 in the head");
   constexpr int WRB = W8 ? 1 : 2;  // bytes per weight element
   constexpr int HRB = A8 ? 1 : 2;  // bytes per hidden-state element
-  constexpr int TR = A8 ? A8_TILE_ROWS : 256;  // rows per tile
-  constexpr int JN = TR / 128;                 // 32-row blocks per wave
+  constexpr int JN = TR / 128;  // 32-row blocks per wave
   const int n_rt = (R + TR - 1) / TR, n_vt = (V + HEAD_BN - 1) / HEAD_BN;
   const int n_rt256 = (R + 255) / 256;  // row tiles of the gather lists
   // workgroup g takes rounds [w_lo, rounds) of slot g % 256: a bounded run of
@@ -327,6 +327,11 @@ __device__ __forceinline__ void ring_body(
 #pragma unroll
   for (int j = 0; j < RING_LOADS; ++j)
     vo[j] = ((wave * 32 + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
+  // bf16 h k-tile (TR rows): the wave's TR/64 loads fill rows wave*TR/8 + 8j + i/8
+  int voh[TR / 64];
+#pragma unroll
+  for (int j = 0; j < TR / 64; ++j)
+    voh[j] = ((wave * (TR / 8) + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
   // fp8 W: load j (0..1) fills rows wave*32 + 16j + i/4, position i%4, which holds
   // chunk (i%4) ^ dma8_swz(row % 16)
   int vo8[RING_LOADS8];
@@ -336,7 +341,7 @@ __device__ __forceinline__ void ring_body(
     vo8[j] = row * d + (((lane & 3) ^ dma8_swz(row & 15)) << 4);
   }
   constexpr int W_LOADS = W8 ? RING_LOADS8 : RING_LOADS;
-  constexpr int H_LOADS = A8 ? TR / 128 : RING_LOADS;
+  constexpr int H_LOADS = A8 ? TR / 128 : TR / 64;
   // A8 h k-tile (TR rows x 64 bytes): load j of a wave fills rows wave*TR/8 + 16j ..
   // +15, lane i writing 16 bytes at row i/4, position i%4 (chunk (i%4) ^ dma8_swz(row % 16))
   int vo8h[TR / 128];
@@ -370,7 +375,8 @@ __device__ __forceinline__ void ring_body(
     if constexpr (W8)
       head_issue8(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo8);
     else
-      head_issue(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
+      head_issue<RING_LOADS>(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl,
+                             wave * 32, vo);
   };
   auto issue_h = [&](int q, uint8_t* sl) __attribute__((always_inline)) {
     const bool nxt = q >= nk5;
@@ -388,7 +394,8 @@ __device__ __forceinline__ void ring_body(
                                                  vo8h[j], (pad ? 0 : k) * DMA_BK, 0, 0);
     }
     else
-      head_issue(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo);
+      head_issue<TR / 64>(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl,
+                           wave * (TR / 8), voh);
   };
 
   // h fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32 (bf16 W) or
@@ -403,11 +410,11 @@ __device__ __forceinline__ void ring_body(
   int fo8[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) fo8[m] = (lane & 31) * 64 + (((2 * m + (lane >> 5)) ^ dma8_swz(lane & 15)) << 4);
-  bf16x8 fa[2][4], fb[2][2];
+  bf16x8 fa[2][4], fb[2][JN];
   uint4 wraw[4];  // fp8 W codes of the current pair of k-steps
   f32x16 acc[4][2];
   auto read_frags = [&](const uint8_t* sa, const uint8_t* sb, int ks, bf16x8 (&xa)[4],
-                        bf16x8 (&xb)[2]) {
+                        bf16x8 (&xb)[JN]) {
     if constexpr (W8) {
       if ((ks & 1) == 0) {
 #pragma unroll
@@ -415,8 +422,8 @@ __device__ __forceinline__ void ring_body(
           wraw[i] = *reinterpret_cast<const uint4*>(sa + (wm * 128 + i * 32) * 64 + fo8[ks >> 1]);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        xb[j] = *reinterpret_cast<const bf16x8*>(sb + (wr * 64 + j * 32) * 128 + fo[ks]);
+      for (int j = 0; j < JN; ++j)
+        xb[j] = *reinterpret_cast<const bf16x8*>(sb + (wr * 32 * JN + j * 32) * 128 + fo[ks]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         xa[i] = (ks & 1) ? e4m3x8_to_bf16(wraw[i].z, wraw[i].w) : e4m3x8_to_bf16(wraw[i].x, wraw[i].y);
@@ -425,32 +432,38 @@ __device__ __forceinline__ void ring_body(
       for (int i = 0; i < 4; ++i)
         xa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + fo[ks]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        xb[j] = *reinterpret_cast<const bf16x8*>(sb + (wr * 64 + j * 32) * 128 + fo[ks]);
+      for (int j = 0; j < JN; ++j)
+        xb[j] = *reinterpret_cast<const bf16x8*>(sb + (wr * 32 * JN + j * 32) * 128 + fo[ks]);
     }
   };
-  auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[2]) {
+  auto mfma_step = [&](const bf16x8 (&xa)[4], const bf16x8 (&xb)[JN]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < JN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
   };
+  // a k-step's 4 JN matrix ops, each paired with a fragment read or conversions
+  constexpr int NM = 4 * JN;
   auto interleave_ds = [&]() __attribute__((always_inline)) {
     if constexpr (W8) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1 + JN % 2 * 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 1; g < NM / 2; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU (code conversion)
+      for (int g = 0; g < NM / 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 8 / JN, 0);  // VALU (code conversion)
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
     } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 - JN, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
 #pragma unroll
-      for (int g = 0; g < 6; ++g) {
+      for (int g = 1; g < 4 + JN && g < NM; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
@@ -469,12 +482,14 @@ __device__ __forceinline__ void ring_body(
     {
       read_frags(slot[sA], slot[sB], 1, fa[1], fb[1]);
       mfma_step(fa[0], fb[0]);
+      constexpr int VM = (H_LOADS + W_LOADS + NM - 1) / NM;  // loads per matrix op
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        if (g < H_LOADS + W_LOADS)
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (buffer -> LDS)
-        if (W8) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-        else if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      for (int g = 0; g < NM; ++g) {
+        if (g * VM < H_LOADS + W_LOADS)
+          __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);  // VMEM (buffer -> LDS)
+        if (W8) __builtin_amdgcn_sched_group_barrier(0x002, 4 / JN, 0);  // VALU
+        else if (g == 0) __builtin_amdgcn_sched_group_barrier(0x100, 3 - JN, 0);  // DS read
+        else if (g < 4 + JN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
       read_frags(slot[sA], slot[sB], 2, fa[0], fb[0]);
@@ -698,13 +713,13 @@ __device__ __forceinline__ void ring_body(
 }
 
 // The output head (bf16 or fp8 weights; A8: fp8 hidden states with row scales).
-template <bool W8, bool A8 = false>
+template <bool W8, bool A8 = false, int TR = 256>
 __global__ __launch_bounds__(64 * RING_WAVES, 1) void lmhead_ring_kernel(
     int R, int V, int d, const uint16_t* __restrict__ h, const uint8_t* __restrict__ W,
     const float* __restrict__ w_scale, const float* __restrict__ h_scale,
     const int32_t* __restrict__ list_head, const int4* __restrict__ rec, float* __restrict__ raw,
     float2* __restrict__ part, const uint16_t* __restrict__ zero, int rounds_per_wg) {
-  ring_body<W8, false, A8>(R, V, d, h, W, w_scale, h_scale, list_head, rec, raw, part, zero,
+  ring_body<W8, false, A8, TR>(R, V, d, h, W, w_scale, h_scale, list_head, rec, raw, part, zero,
                            rounds_per_wg, RingGemmOut{});
 }
 
@@ -902,6 +917,32 @@ static HeadPrep head_prep_layout(Carve& cv, tcs_dtype h_dtype, int32_t B, int32_
   return P;
 }
 
+// Rows per tile of the matrix-core head: the size whose busiest workgroup (tiles
+// dealt over HEAD_WGS slots) finishes first, a 128-row tile taking 0.56 of a
+// 256-row tile's time.  Measured on MI355X, long-document head (V = 151,936, d =
+// 2,560, fp8 W), ms per launch with 256- / 128-row tiles: 256 rows 0.260 / 0.254,
+// 384 rows 0.367 / 0.345, 512 rows 0.395 / 0.447, 640 rows 0.514 / 0.517, 1,024
+// rows 0.704 / 0.785 (the ratio 0.56 is the last pair's per tile); 128 rows take
+// 0.145 with 128-row tiles.
+static int head_tile_rows(int R, int n_vt) {
+  const long busiest256 = ((R + 255) / 256 * long(n_vt) + HEAD_WGS - 1) / HEAD_WGS;
+  const long busiest128 = ((R + 127) / 128 * long(n_vt) + HEAD_WGS - 1) / HEAD_WGS;
+  return busiest128 * 56 < busiest256 * 100 ? 128 : 256;
+}
+
+template <bool W8, bool A8>
+static void launch_ring_head(int TR, int grid, hipStream_t s, int R, int V, int d, const uint16_t* h,
+                             const uint8_t* W, const float* w_scale, const float* h_scale,
+                             const HeadPrep& P, float* lp, float2* part, const uint16_t* zero,
+                             int per) {
+  if (TR == 128)
+    lmhead_ring_kernel<W8, A8, 128><<<grid, 64 * RING_WAVES, 0, s>>>(
+        R, V, d, h, W, w_scale, h_scale, P.list_head, P.rec, lp, part, zero, per);
+  else
+    lmhead_ring_kernel<W8, A8, 256><<<grid, 64 * RING_WAVES, 0, s>>>(
+        R, V, d, h, W, w_scale, h_scale, P.list_head, P.rec, lp, part, zero, per);
+}
+
 size_t lmhead_prep_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
                          int32_t V) {
   Carve cv(nullptr);
@@ -1017,8 +1058,8 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
   timer_begin(TCS_TIMER_HEAD, stream);
   if (h_dtype == TCS_BF16) {
     if (d % 64 != 0) return fail(TCS_EUNSUPPORTED, "lmhead: d=%d is not a multiple of 64", d);
-    // the W8A8 head's tiles have A8_TILE_ROWS rows (see ring_body)
-    const int n_rt_k = w_dtype == TCS_FP8_E4M3_A8 ? (R + A8_TILE_ROWS - 1) / A8_TILE_ROWS : n_rt;
+    const int TR = head_tile_rows(R, n_tiles);
+    const int n_rt_k = (R + TR - 1) / TR;
     const int rounds = head_grid(n_rt_k, n_tiles) / HEAD_WGS;
     const int per = head_rounds_per_wg(rounds);
     const int grid = (rounds + per - 1) / per * HEAD_WGS;
@@ -1030,13 +1071,12 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
       auto codes = static_cast<uint32_t*>(act8);
       auto hs = reinterpret_cast<float*>(static_cast<char*>(act8) + align_up(size_t(R) * d));
       quant_rows_e4m3_kernel<<<(R + 3) / 4, 256, 0, s>>>(R, d, hp, codes, hs);
-      lmhead_ring_kernel<true, true><<<grid, 64 * RING_WAVES, 0, s>>>(
-          R, V, d, reinterpret_cast<const uint16_t*>(codes), wp, w_scale, hs, P.list_head, P.rec, lp,
-          p, zp, per);
+      launch_ring_head<true, true>(TR, grid, s, R, V, d, reinterpret_cast<const uint16_t*>(codes), wp,
+                                   w_scale, hs, P, lp, p, zp, per);
     } else if (w_dtype == TCS_FP8_E4M3) {
-      lmhead_ring_kernel<true><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, w_scale, nullptr, P.list_head, P.rec, lp, p, zp, per);
+      launch_ring_head<true, false>(TR, grid, s, R, V, d, hp, wp, w_scale, nullptr, P, lp, p, zp, per);
     } else {
-      lmhead_ring_kernel<false><<<grid, 64 * RING_WAVES, 0, s>>>(R, V, d, hp, wp, nullptr, nullptr, P.list_head, P.rec, lp, p, zp, per);
+      launch_ring_head<false, false>(TR, grid, s, R, V, d, hp, wp, nullptr, nullptr, P, lp, p, zp, per);
     }
     n_parts = 2 * n_tiles;
   } else {
