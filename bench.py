@@ -8,7 +8,7 @@
                                                        # operands (+ socket power and clocks)
 
 One step is one ``tcs_classify_run`` call over one batch of synthetic documents
-(consecutive steps alternate over ``--streams`` HIP streams, default 2, each with its
+(consecutive steps alternate over ``--streams`` HIP streams, default 3, each with its
 own run workspace, so one batch's attention and projection can use the CUs the
 previous batch's output head leaves idle in its last partial round of tiles):
 ancestor-masked tree attention over the documents, output projection + RMSNorm,
@@ -483,7 +483,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--extra", default="3,4", help="other label-set sizes to report (config ids)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--streams", type=int, default=2,
+    ap.add_argument("--streams", type=int, default=3,
                     help="batches in flight: consecutive steps alternate over this many HIP streams, "
                          "each with its own run workspace")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -113,10 +113,10 @@ def cfg2():
     return cfg, make_inputs(cfg)
 
 
-def test_prepared_runs_on_two_streams(dev, cfg2):
-    """Two batches in flight, as bench.py runs them: tcs_classify_run on two HIP streams
-    at once, each with its own workspace, on one prepared state (running-example
-    shape, B = 64) gives the single-stream results bit for bit."""
+def test_prepared_runs_on_three_streams(dev, cfg2):
+    """Three batches in flight, as bench.py runs them: tcs_classify_run on three HIP
+    streams at once, each with its own workspace, on one prepared state
+    (running-example shape, B = 64) gives the single-stream results bit for bit."""
     torch = _torch()
     cfg, inp = cfg2
     t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
@@ -126,16 +126,16 @@ def test_prepared_runs_on_two_streams(dev, cfg2):
     prep = tcs.Prepared(model, td, docs.B)
     ref = [x.cpu().numpy() for x in tcs.classify(model, td, docs, prepared=prep)]
     nbytes = tcs.classify_run_workspace_bytes(model, td, docs)
-    streams = [torch.cuda.Stream() for _ in range(2)]
-    ws = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    ws = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
     torch.cuda.synchronize()
-    outs = [tcs.classify(model, td, docs, ws=ws[i % 2], prepared=prep, stream=streams[i % 2])
+    outs = [tcs.classify(model, td, docs, ws=ws[i % 3], prepared=prep, stream=streams[i % 3])
             for i in range(6)]
     torch.cuda.synchronize()
     for i, o in enumerate(outs):
         for a, b in zip(o, ref):
             np.testing.assert_array_equal(a.cpu().numpy(), b)
-    say("two streams: 6 batches == single-stream run")
+    say("three streams: 6 batches == single-stream run")
 
 
 @pytest.fixture(scope="module")
