@@ -481,6 +481,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--batch", type=int, default=None,
+                    help="documents per batch (default: the workload's own batch)")
     ap.add_argument("--extra", default="3,4", help="other label-set sizes to report (config ids)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streams", type=int, default=3,
@@ -533,7 +535,10 @@ def main():
         print(json.dumps({"path_roofline": path_stress()}), flush=True)
         return
 
-    S = setup(args.config, args.streams, **({"head": args.head} if args.head else {}))
+    over = {"head": args.head} if args.head else {}
+    if args.batch:
+        over["B"] = args.batch
+    S = setup(args.config, args.streams, **over)
     cfg, trie = S["cfg"], S["trie"]
     sec, kern = run_steps(S, args.steps, args.warmup)
     few = max(3, min(args.steps, 20) // 2)  # steps of the slow secondary passes

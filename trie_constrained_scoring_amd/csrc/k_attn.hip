@@ -451,7 +451,8 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn, const uint16_t* __restrict__ Kd,
     const uint16_t* __restrict__ Vd, const int32_t* __restrict__ doc_offsets,
     const float2* __restrict__ anc_ml, const float* __restrict__ anc_o, float scale,
-    uint16_t* __restrict__ O, const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel) {
+    uint16_t* __restrict__ O, const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+    int S, float2* __restrict__ pml, float* __restrict__ po) {
   static_assert(HD == 128, "256-byte key rows: 16 chunks, one per swizzle position");
   constexpr int KB = 32;                 // keys per stage
   constexpr int ROW = HD * 2;            // bytes per key row
@@ -469,9 +470,13 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   const int n_rb = (rows_total + 31) / 32;
   // block i -> document i mod B: block i runs on XCD i mod 8, so each XCD reads whole
   // key rows (all KV heads) of its documents
-  const int Bn = int(gridDim.x) / (n_rb * Hkv);
+  // S > 1: the S workgroups z of a (document, row block, KV head) take every S-th
+  // group of four key stages each and leave (max, sum, unnormalised output)
+  // partials for doc_attn_merge_kernel
+  const int Bn = int(gridDim.x) / (n_rb * Hkv * S);
   const int b = blockIdx.x % Bn, rest = blockIdx.x / Bn;
-  const int rb = rest % n_rb, g = rest / n_rb;
+  const int rb = rest % n_rb, g = (rest / n_rb) % Hkv, z = rest / (n_rb * Hkv);
+  const int vw = z * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6), NW = 4 * S;
   // with sel: slot b scores document sel[2b] with the queries and path partials of
   // row sel[2b+1] (n_int is 1); slots from *n_sel on have nothing to do
   int doc = b, rq = 0;
@@ -617,27 +622,28 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   };
 
   const int n_st = (L + KB - 1) / KB;
-  const int cnt = n_st > wave ? (n_st - wave + 3) / 4 : 0;
+  // stages vw, vw + NW, ...
+  const int cnt = n_st > vw ? (n_st - vw + NW - 1) / NW : 0;
   wait_lgkmcnt0();  // the zero fill is in LDS before any load can land on it
   if constexpr (NS == 2) {
-    if (cnt > 0) issue(wave, 0);
-    if (cnt > 1) issue(wave + 4, 1);
+    if (cnt > 0) issue(vw, 0);
+    if (cnt > 1) issue(vw + NW, 1);
     for (int i = 0; i < cnt; ++i) {
       if (i + 1 < cnt) wait_vmcnt<2 * NLD>(); else wait_vmcnt<0>();
       __builtin_amdgcn_sched_barrier(0);
-      compute(ring + (i & 1) * 2 * OPB, wave + 4 * i);
+      compute(ring + (i & 1) * 2 * OPB, vw + NW * i);
       if (i + 2 < cnt) {
         wait_lgkmcnt0();  // this slot's reads are done before it is refilled
         __builtin_amdgcn_sched_barrier(0);
-        issue(wave + 4 * (i + 2), i & 1);
+        issue(vw + NW * (i + 2), i & 1);
       }
     }
   } else {  // one slot: the other workgroup on the CU covers each wave's load wait
     for (int i = 0; i < cnt; ++i) {
-      issue(wave + 4 * i, 0);
+      issue(vw + NW * i, 0);
       wait_vmcnt<0>();
       __builtin_amdgcn_sched_barrier(0);
-      compute(ring, wave + 4 * i);
+      compute(ring, vw + NW * i);
       wait_lgkmcnt0();  // the slot's reads are done before it is refilled
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -671,6 +677,32 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     const int j = j0 + row;
     if (j < rows_total) {
       const int r = j / G, h = g * G + j % G;
+      if (S > 1) {  // this workgroup's share of the keys: (max, sum, unnormalised output)
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) M = fmaxf(M, sml[(k * 32 + row) * 2]);
+        float f[4], Ls = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[k] = M == -INFINITY ? 0.f : exp2f(sml[(k * 32 + row) * 2] - M);
+          Ls += f[k] * sml[(k * 32 + row) * 2 + 1];
+        }
+        const size_t pi = (size_t)z * Bn * n_int * Hq + ((size_t)b * n_int + r) * Hq + h;
+        if ((tid & 7) == 0) pml[pi] = float2{M, Ls};
+        float4* pp = reinterpret_cast<float4*>(po + pi * HD + h0);
+#pragma unroll
+        for (int i = 0; i < SEG / 4; ++i) {
+          float w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[e] += f[k] * so[((size_t)k * 32 + row) * OUT_LD + h0 + 4 * i + e];
+          }
+          pp[i] = float4{w[0], w[1], w[2], w[3]};
+        }
+        return;
+      }
       const float4* ao = reinterpret_cast<const float4*>(anc_o + ((size_t)(rq + r) * Hq + h) * HD + h0);
       float4 av[SEG / 4];
 #pragma unroll
@@ -706,6 +738,61 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
                       pack_bf16(v[8 * i + 4], v[8 * i + 5]), pack_bf16(v[8 * i + 6], v[8 * i + 7])};
     }
   }
+}
+
+// Output of a key-split document attention: per (document row, query head) x, the
+// S workgroup partials (base-2 max, sum, unnormalised output) of its document keys
+// and the path partial of its trie row merge into one softmax; 4 output values per
+// thread.  NRH = B n_int Hq, NH = n_int Hq (path partials are per trie row).
+__global__ __launch_bounds__(256) void doc_attn_merge_kernel(int NRH, int NH, int HD, int S,
+                                                             const float2* __restrict__ anc_ml,
+                                                             const float* __restrict__ anc_o,
+                                                             const float2* __restrict__ pml,
+                                                             const float* __restrict__ po,
+                                                             uint16_t* __restrict__ O) {
+  const long t = long(blockIdx.x) * 256 + threadIdx.x;
+  const int nq = HD / 4;
+  if (t >= long(NRH) * nq) return;
+  const int x = int(t / nq), q4 = int(t % nq) * 4;
+  const float2 a = anc_ml[x % NH];
+  const float ma = a.x * LOG2E;
+  float Mt = ma;
+  for (int z = 0; z < S; ++z) Mt = fmaxf(Mt, pml[(size_t)z * NRH + x].x);
+  const float fa = exp2f(ma - Mt);
+  float den = a.y * fa;
+  const float4 an = *reinterpret_cast<const float4*>(anc_o + (size_t)(x % NH) * HD + q4);
+  float4 num{an.x * fa, an.y * fa, an.z * fa, an.w * fa};
+  for (int z = 0; z < S; ++z) {
+    const float2 p = pml[(size_t)z * NRH + x];
+    const float fz = p.x == -INFINITY ? 0.f : exp2f(p.x - Mt);
+    den += fz * p.y;
+    const float4 o = *reinterpret_cast<const float4*>(po + ((size_t)z * NRH + x) * HD + q4);
+    num.x += fz * o.x;
+    num.y += fz * o.y;
+    num.z += fz * o.z;
+    num.w += fz * o.w;
+  }
+  const float inv = 1.0f / den;
+  *reinterpret_cast<uint2*>(O + (size_t)x * HD + q4) =
+      uint2{pack_bf16(num.x * inv, num.y * inv), pack_bf16(num.z * inv, num.w * inv)};
+}
+
+// Key split of the document attention with few rows per (document, KV head): the
+// (document, row block, KV head) workgroups alone would leave CUs idle (fewer
+// than 256), so each is split S ways over its keys (S <= 4, up to ~512
+// workgroups).  Not with a row selection.
+static int doc_attn_splits(int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv, int32_t hd) {
+  const long rows = long(n_int) * (Hq / Hkv);
+  if (hd != 128 || rows > 64 || B <= 0) return 1;
+  const long blocks = long(B) * Hkv * ((rows + 31) / 32);
+  return blocks >= 256 ? 1 : int(std::min(4L, std::max(1L, 512 / blocks)));
+}
+
+size_t doc_attn_split_bytes(int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv, int32_t hd) {
+  const int S = doc_attn_splits(B, n_int, Hq, Hkv, hd);
+  if (S == 1) return 0;
+  const size_t nrh = size_t(B) * n_int * Hq;
+  return align_up(S * nrh * 8) + S * nrh * hd * 4;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1222,7 +1309,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
 int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
                     int32_t hd, const void* Qn, const void* Kd, const void* Vd,
                     const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
-                    float scale, void* O, const int32_t* sel, const int32_t* n_sel) {
+                    float scale, void* O, const int32_t* sel, const int32_t* n_sel, void* split) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || n_int == 0) return TCS_OK;
   if (dt != TCS_BF16) return fail(TCS_EUNSUPPORTED, "doc_attn: MFMA path is bf16 only");
@@ -1238,8 +1325,18 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
   timer_begin(TCS_TIMER_DOC_ATTN, stream);
   if (rows <= 64) {
     const long grid = long(B) * Hkv * ((rows + 31) / 32);
-    if (hd == 128)
-      doc_attn_stream_kernel<128, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o, sel, n_sel);
+    const int S = split && !sel ? doc_attn_splits(B, n_int, Hq, Hkv, hd) : 1;
+    if (hd == 128 && S > 1) {
+      const size_t nrh = size_t(B) * n_int * Hq;
+      auto pml = static_cast<float2*>(split);
+      auto po = reinterpret_cast<float*>(static_cast<char*>(split) + align_up(S * nrh * 8));
+      doc_attn_stream_kernel<128, 1><<<grid * S, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o,
+                                                              nullptr, nullptr, S, pml, po);
+      const long threads = long(nrh) * (hd / 4);
+      doc_attn_merge_kernel<<<int((threads + 255) / 256), 256, 0, s>>>(int(nrh), n_int * Hq, hd, S, ml, anc_o, pml, po, o);
+    } else if (hd == 128)
+      doc_attn_stream_kernel<128, 1><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o, sel, n_sel,
+                                                          1, nullptr, nullptr);
     else
       doc_attn_mfma_kernel<64, 1, 4><<<grid, 256, 0, s>>>(n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
   } else {

@@ -165,7 +165,7 @@ static PrepLayout prep_layout(const tcs_model* m, const tcs_trie_dev* t, int32_t
 // Per-batch workspace (tcs_classify_run).
 struct RunLayout {
   size_t total;
-  void *a_doc, *Kd, *Vd, *O, *h, *part, *ll, *act8;
+  void *a_doc, *Kd, *Vd, *O, *h, *part, *ll, *act8, *asplit;
   float *y, *lse, *lp;
 };
 
@@ -189,6 +189,7 @@ static RunLayout run_layout(const tcs_model* m, const tcs_trie_dev* t, const tcs
   L.lp = c.take<float>(size_t(d->B) * t->n_nodes);
   L.ll = c.take<float>(size_t(d->B) * t->n_labels);
   L.act8 = c.take<char>(lmhead_act8_bytes(m->head_dtype, int32_t(R), m->d));
+  L.asplit = c.take<char>(m->dtype == TCS_BF16 ? doc_attn_split_bytes(d->B, t->n_int, m->Hq, m->Hkv, m->hd) : 0);
   L.total = c.used;
   return L;
 }
@@ -282,7 +283,7 @@ static int run_impl(void* stream, const tcs_model* m, const tcs_trie_dev* t, con
     const float* ml = c.take<float>(size_t(n_int) * m->Hq * 2);
     const float* ao = c.take<float>(size_t(n_int) * m->Hq * m->hd);
     rc = launch_doc_attn(stream, dt, B, n_int, m->Hq, m->Hkv, m->hd, P.Qn, Kd, Vd, d->doc_offsets,
-                         ml, ao, scale, L.O);
+                         ml, ao, scale, L.O, nullptr, nullptr, L.asplit);
   }
   if (rc) return rc;
   // y = x + O Wo^T ; h = RMSNorm(y)

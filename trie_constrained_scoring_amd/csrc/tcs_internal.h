@@ -135,7 +135,10 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
                     int32_t Hkv, int32_t hd, const void* Qn, const void* Kd, const void* Vd,
                     const int32_t* doc_offsets, const float* anc_ml, const float* anc_o,
                     float scale, void* O, const int32_t* sel = nullptr,
-                    const int32_t* n_sel = nullptr);
+                    const int32_t* n_sel = nullptr, void* split = nullptr);
+// Scratch of a key-split document attention (partials per row, head and split;
+// 0 when that shape runs unsplit); `split` of launch_doc_attn, or null (unsplit).
+size_t doc_attn_split_bytes(int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv, int32_t hd);
 
 // Path sums, label softmax and argmax.  lp: edge log-probs [B, n_nodes]; or, with
 // lse and node_qrow set, the raw child logits, each edge's log-prob being
