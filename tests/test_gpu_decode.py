@@ -85,7 +85,7 @@ def test_decode_full_size(dev, cid):
 
 
 def test_decode_runs_on_two_streams(dev):
-    """Two batches in flight, as bench.py runs them: tcs_decode_run on two HIP streams
+    """Batches in flight, as bench.py runs them (here two): tcs_decode_run on two HIP streams
     at once, each with its own workspace (the per-document decoding state lives
     there), gives the single-stream labels and run counts."""
     import torch
