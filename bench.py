@@ -24,7 +24,7 @@ primary workload (default: the running-example shape, 10 labels); the 255- and
 5000-label workloads are reported under ``at_labels``, and ``path_roofline`` times the
 path-sum kernel alone on 4096 documents of the 5000-label trie (enough bytes to hold
 it against HBM).  ``decision_word`` runs the same documents and weights with every
-label cut to the end of the word where it leaves the others (the decision-word form
+label cut after the word in which its prefix stops being shared (the decision-word form
 of trie_tree: fewer query rows, same kernels); the headline scores every label over
 its full root-to-leaf path.  ``letters`` runs them under the letters method (one
 answer position per document, only the letter rows of the head), ``trie_decode`` under
@@ -137,7 +137,7 @@ def run_buffers(model, td, docs, streams):
 
 def decision_word(S, steps, warmup, streams):
     """The same documents and weights scored in the decision-word form: every label
-    cut to the end of the word where it leaves the others (tcs_decision_truncate),
+    cut after the word in which its prefix stops being shared (tcs_decision_truncate),
     then the unchanged classify pass on the cut trie."""
     import torch
     import trie_constrained_scoring_amd as tcs

@@ -127,8 +127,8 @@ int tcs_trie_build(const int32_t* label_offsets, const int32_t* label_tokens, in
 
 /*
  * Decision-word cut of a label set ("To Classify, Try a Trie Tree", section 3.2):
- * trie_tree scores a label only up to the end of the word in which it leaves every
- * other label.  For label m, k is the first position whose token prefix (tokens
+ * trie_tree scores a label through the last token of the word in which its token
+ * prefix stops being shared with any other label.  For label m, k is the first position whose token prefix (tokens
  * 1..k) no other label shares; the word holding token k goes on while the next
  * token is a word continuation (word_cont[token] != 0), and d_m is the position of
  * its last token.  A label that shares all its prefixes -- it is the start of
@@ -180,8 +180,8 @@ typedef struct {
 
 /*
  * Ancestor-masked tree attention (section 3.2, "Custom attention kernel": all
- * answer nodes of a document in one request, each attending only to the prompt and
- * to the nodes on its own path).
+ * answer nodes of a document in one request; a node's keys are the document's and
+ * those of its ancestors and itself, none from other branches).
  *
  * For document b, query row r (internal node u) and query head h, the keys are
  * the document's keys Kd[doc_offsets[b] .. doc_offsets[b+1]) followed by the node
@@ -218,16 +218,20 @@ int tcs_tree_attn(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, 
  *                 edge (e_tok, e_qrow, e_child = c); lp[b, 0] = 0 for the root.
  *
  *   h_dtype     TCS_F32 or TCS_BF16: storage of h.
- *   w_dtype     h_dtype, or TCS_FP8_E4M3 (with h_dtype TCS_BF16) plus w_scale [V] fp32.
+ *   w_dtype     h_dtype, or (with h_dtype TCS_BF16) TCS_FP8_E4M3 plus w_scale [V] fp32, or
+ *               TCS_FP8_E4M3_A8: the same fp8 weights, and each row of h first quantized to
+ *               E4M3 with its own scale max|h_r|/448 (codes and scales live in ws), the
+ *               logit then being s_r * w_scale[v] * (codes_r . codes_v).
  *   h           [R, d];  W [V, d]
  *   edges       trie->e_tok / e_qrow / e_child, sorted by token
  *   lse         [R] fp32 out;  lp [B, n_nodes] fp32 out
- *   ws          workspace of tcs_lmhead_workspace_bytes(h_dtype, B, n_int, n_nodes, d, V)
- *               bytes (0 for invalid sizes)
- * bf16 heads need d % 64 == 0.
+ *   ws          workspace of tcs_lmhead_workspace_bytes(h_dtype, w_dtype, B, n_int, n_nodes,
+ *               d, V) bytes (0 for invalid sizes or dtype pairs)
+ * bf16 heads need d % 64 == 0.  Errors: TCS_EUNSUPPORTED (dtype pair, d), TCS_EINVAL (sizes,
+ * null pointers, w_scale missing for an fp8 head), TCS_ECAPACITY (short workspace).
  */
-size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
-                                  int32_t d, int32_t V);
+size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                                  int32_t n_nodes, int32_t d, int32_t V);
 int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
                           int32_t n_int, int32_t n_nodes, int32_t d, int32_t V, const void* h,
                           const void* W, const float* w_scale, const int32_t* e_tok,
@@ -308,9 +312,8 @@ int tcs_classify(tcs_stream stream, const tcs_model* model, const tcs_trie_dev* 
 
 /*
  * The same pass split at the label set.  In this single-layer model a trie node's
- * q, k and v come from its token alone and its attention over its own path
- * ("attend only to the prompt and your own path", section 3.2) does not involve
- * the document, so they are computed once per label set; so are the output head's
+ * q, k and v come from its token alone and its attention over its ancestor chain
+ * (section 3.2, custom attention kernel) does not involve the document, so they are computed once per label set; so are the output head's
  * gather lists, which depend only on the trie and the batch size B.  The pages run
  * one label set over a whole table of documents (section 2), so this work is paid
  * once per query rather than once per batch.

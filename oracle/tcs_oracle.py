@@ -8,8 +8,8 @@ Sources (cited by page title and section):
   [CT] "To Classify, Try a Trie Tree" (Quail blog): section 3.1 (the label trie,
        root = the ANSWER: token), section 3.2 (trie_tree: label probability is the
        product of its token probabilities; normalisation over labels; the rule for
-       a label that is a prefix of another; every node attends only to the prompt
-       and to the nodes on its own path), section 4.1 (full-vocabulary output head).
+       a label that is a prefix of another; a node's keys are the document's and
+       its ancestors', no other branch's), section 4.1 (full-vocabulary output head).
   [EX] Quail documentation, "Execution", section "Label scoring" (worked example:
        refund 0.8 x 0.6 = 0.48 against praise 0.3).
   [QI] "Building an Ultra-High Throughput AI-SQL Engine", section 3.2.4 (partial

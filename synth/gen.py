@@ -111,10 +111,10 @@ def word_continuation_flags(cfg: "Config", labels, rng: np.random.Generator):
     """uint8 [V]: 1 where a vocabulary token continues the previous token's word.
 
     Words decide how far a label is scored in the decision-word form of trie_tree
-    ("To Classify, Try a Trie Tree", section 3.2: up to the end of the word where
-    the label leaves all others).  Each token is a continuation with probability
-    WORD_CONT_P; in the running example the label tokens are set by hand so that
-    only "-factor" continues a word.
+    ("To Classify, Try a Trie Tree", section 3.2: a label is scored through the
+    last token of the word in which no other label shares its prefix any more).
+    Each token is a continuation with probability WORD_CONT_P; in the running
+    example the label tokens are set by hand so that only "-factor" continues a word.
     """
     flags = (rng.random(cfg.V) < WORD_CONT_P).astype(np.uint8)
     if cfg.trie[0] == "running":

@@ -1,7 +1,11 @@
 """Helpers for the GPU parity tests (not collected by pytest)."""
+import json
+import os
 import sys
 
 import numpy as np
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 LL_TOL = 2e-2      # label log-likelihood, absolute
 PROB_TOL = 1e-3    # label probability, absolute
@@ -45,3 +49,15 @@ def check_labels(gpu_ll, gpu_prob, gpu_label, o_ll, o_prob, o_label, what=""):
     assert np.all(o_ll.max(axis=1) - o_ll[rows, lab] <= GAP + LL_TOL)
     say(f"{what}: max |dll| {err_ll:.2e}  max |dP| {err_p:.2e}  labels compared {sure.sum()}/{len(sure)}")
     return err_ll, err_p
+
+
+def load_golden(name):
+    """A stored oracle result under tests/golden (JSON)."""
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def golden_fingerprint(inp, docs):
+    """Fingerprint of regenerated inputs, as the golden writer computes it."""
+    from tests.golden.make_full_size_goldens import fingerprint
+    return fingerprint(inp, docs)

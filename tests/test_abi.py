@@ -118,6 +118,35 @@ def test_null_pointer_errors_without_gpu():
     assert lib.tcs_classify(None, None, None, None, None, None, None, None, 0) == tcs.TCS_EINVAL
 
 
+def test_path_sum_rejects_null_qparent_without_gpu():
+    """A trie struct whose qparent is NULL is refused before any launch, also when the
+    optional level-by-level arrays are set (that kernel reads qparent)."""
+    lib = tcs.lib()
+    labels = [[i, i + 1] for i in range(2, 1400, 2)]   # > 512 labels: level-by-level sums
+    t = tcs.trie_build(*labels_to_csr(labels), 0, 2000)
+    fake = 256   # never dereferenced: the call fails before launching
+    dev = tcs.tcs_trie_dev(n_nodes=t.n_nodes, n_int=t.n_int, n_labels=t.n_labels,
+                           max_depth=t.max_depth, **{n: fake for n in tcs.TRIE_DEV_ARRAYS})
+    dev.qparent = None
+    rc = lib.tcs_path_sum_softmax(None, 2, C.byref(dev), fake, fake, fake, fake)
+    assert rc == tcs.TCS_EINVAL and b"null" in lib.tcs_last_error()
+
+
+def test_lmhead_workspace_query_by_dtype_pair():
+    """The head's workspace size depends on the (h, W) dtype pair: a W8A8 head also
+    holds the hidden rows' E4M3 codes (1 byte each) and scales; unsupported pairs give 0."""
+    lib = tcs.lib()
+    B, n_int, n_nodes, d, V = 4, 8, 18, 256, 1000
+    bf = lib.tcs_lmhead_workspace_bytes(tcs.TCS_BF16, tcs.TCS_BF16, B, n_int, n_nodes, d, V)
+    w8 = lib.tcs_lmhead_workspace_bytes(tcs.TCS_BF16, tcs.TCS_FP8_E4M3, B, n_int, n_nodes, d, V)
+    a8 = lib.tcs_lmhead_workspace_bytes(tcs.TCS_BF16, tcs.TCS_FP8_E4M3_A8, B, n_int, n_nodes, d, V)
+    assert bf > 0 and w8 == bf and a8 >= bf + B * n_int * (d + 4)
+    assert lib.tcs_lmhead_workspace_bytes(tcs.TCS_F32, tcs.TCS_FP8_E4M3, B, n_int, n_nodes, d, V) == 0
+    assert lib.tcs_lmhead_workspace_bytes(tcs.TCS_F32, tcs.TCS_FP8_E4M3_A8, B, n_int, n_nodes, d, V) == 0
+    assert lib.tcs_lmhead_lse_gather(None, tcs.TCS_F32, tcs.TCS_FP8_E4M3_A8, 1, 1, 2, 64, 10,
+                                     *([None] * 9), 0) == tcs.TCS_EUNSUPPORTED
+
+
 def test_timing_api_without_launches():
     tcs.timing_enable(True)
     assert tcs.timing_read(tcs.TCS_TIMER_HEAD) == (0.0, 0)

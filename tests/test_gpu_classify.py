@@ -7,7 +7,7 @@ import pytest
 import oracle as O
 import trie_constrained_scoring_amd as tcs
 from synth import config, make_inputs
-from tests.gpu_util import LL_TOL, check_labels, say
+from tests.gpu_util import LL_TOL, check_labels, golden_fingerprint, load_golden, say
 
 pytestmark = pytest.mark.gpu
 
@@ -182,26 +182,37 @@ def test_classify_full_size_sampled_docs(dev, which, request):
     np.testing.assert_allclose(prob.sum(axis=1), 1.0, atol=1e-4)
 
 
+GOLDEN_FULL = {3: "classify_max_label_set_255.json", 4: "classify_large_finite_set_5000.json"}
+
+
 @pytest.mark.parametrize("cid", [3, 4])
-def test_classify_full_size_sampled_labels(dev, cid):
-    """Large tries at full size: sampled (document, label) log-likelihoods from the
-    oracle's path-restricted pass; probabilities and labels by their properties."""
+def test_classify_full_size_every_label_vs_oracle(dev, cid):
+    """Large tries at full size (255 labels, B = 32 x 1,024 tokens; 5,000 labels,
+    B = 8 x 256), in the prepared launch configuration bench.py times: every label's
+    log-likelihood, probability and the chosen label of the stored documents against
+    the whole fp64 oracle pass (tests/golden, written by make_full_size_goldens.py
+    from oracle/ only).  A third document is checked on sampled labels through the
+    oracle's path-restricted pass, and properties that hold at any size on all."""
+    g = load_golden(GOLDEN_FULL[cid])
     cfg = config(cid)
     inp = make_inputs(cfg)
+    assert golden_fingerprint(inp, g["docs"]) == g["fingerprint"], "inputs differ from the golden's"
     label, prob, ll = run_gpu(cfg, inp, prepared=True)
+    docs = g["docs"]
+    o_ll = np.array(g["ll"], dtype=np.float64)
+    o_prob, o_label = O.label_softmax(o_ll)
+    assert o_label.tolist() == g["label"]
+    check_labels(ll[docs], prob[docs], label[docs], o_ll, o_prob, o_label,
+                 f"classify[config {cid} full, every label of docs {docs}]")
+    # another document, sampled labels, through the path-restricted oracle pass
+    b = next(x for x in range(cfg.B // 2, cfg.B) if x not in docs)
     M = len(inp["labels"])
-    rng = np.random.default_rng(cid)
-    model = O.OracleModel(inp)
-    trie = O.build_trie(inp["labels"], inp["root_token"], cfg.V)
-    worst = 0.0
-    for b in (0, cfg.B - 1):
-        ids = sorted(set(rng.choice(M, 6, replace=False).tolist() + [int(label[b])]))
-        o_ll, _ = O.label_ll_on_paths(inp, b, ids, model=model, trie=trie)
-        err = np.abs(ll[b, ids] - o_ll).max()
-        worst = max(worst, err)
-        assert err <= LL_TOL, (b, ids, ll[b, ids], o_ll)
-    say(f"classify[config {cid} full]: sampled max |dll| {worst:.2e}")
-    # properties that hold at any size
+    ids = sorted(set(np.random.default_rng(cid).choice(M, 6, replace=False).tolist() + [int(label[b])]))
+    o_part, _ = O.label_ll_on_paths(inp, b, ids)
+    err = np.abs(ll[b, ids] - o_part).max()
+    assert err <= LL_TOL, (b, ids, ll[b, ids], o_part)
+    say(f"classify[config {cid} full]: doc {b}, {len(ids)} sampled labels, max |dll| {err:.2e}")
+    # properties that hold at any size, on every document
     ll64 = ll.astype(np.float64)
     p_ref = np.exp(ll64 - ll64.max(axis=1, keepdims=True))
     p_ref /= p_ref.sum(axis=1, keepdims=True)

@@ -1,6 +1,6 @@
 """Parity of the decision-word form of trie_tree ("To Classify, Try a Trie Tree",
-section 3.2: each label scored up to the end of the word where it leaves all
-others).  The library cuts the labels on the host (tcs_decision_truncate) and runs
+section 3.2: a label is scored through the last token of the word in which its
+prefix stops being shared).  The library cuts the labels on the host (tcs_decision_truncate) and runs
 the unchanged classify pass on the cut trie; the oracle cuts them from the
 definition and scores the cut trie in fp64."""
 import numpy as np
@@ -9,7 +9,7 @@ import pytest
 import oracle as O
 import trie_constrained_scoring_amd as tcs
 from synth import config, make_inputs
-from tests.gpu_util import LL_TOL, check_labels, say
+from tests.gpu_util import check_labels, golden_fingerprint, load_golden, say
 
 pytestmark = pytest.mark.gpu
 
@@ -85,26 +85,25 @@ def test_decision_word_running_example_full_size(dev):
 
 
 def test_decision_word_max_label_set_full_size(dev):
-    """255-label Zipf trie at full size (B = 32, 1024-token documents): sampled
-    (document, label) scores from the oracle's path-restricted pass on the cut
-    trie; probabilities and labels by their properties."""
+    """255-label Zipf trie at full size (B = 32, 1024-token documents), decision-word
+    form: every label's score, probability and the chosen label of the stored
+    documents against the whole fp64 oracle pass on the oracle's own cut
+    (tests/golden, written from oracle/ only); properties on every document."""
+    g = load_golden("classify_max_label_set_255_decision_words.json")
     cfg = config(3)
     inp = make_inputs(cfg)
+    assert golden_fingerprint(inp, g["docs"]) == g["fingerprint"], "inputs differ from the golden's"
     t, o_trie = cut_both(cfg, inp)
+    assert (t.n_nodes, t.n_int) == (g["n_nodes"], g["n_int"])
     label, prob, ll = run_cut(cfg, inp, t)
-    M = len(inp["labels"])
-    rng = np.random.default_rng(3)
-    model = O.OracleModel(inp)
-    worst = 0.0
-    for b in (0, cfg.B - 1):
-        ids = sorted(set(rng.choice(M, 6, replace=False).tolist() + [int(label[b])]))
-        o_ll, _ = O.label_ll_on_paths(inp, b, ids, model=model, trie=o_trie)
-        err = np.abs(ll[b, ids] - o_ll).max()
-        worst = max(worst, err)
-        assert err <= LL_TOL, (b, ids, ll[b, ids], o_ll)
+    docs = g["docs"]
+    o_ll = np.array(g["ll"], dtype=np.float64)
+    o_prob, o_label = O.label_softmax(o_ll)
+    assert o_label.tolist() == g["label"]
+    check_labels(ll[docs], prob[docs], label[docs], o_ll, o_prob, o_label,
+                 f"decision-word[config 3 full, rows {t.n_int}, every label of docs {docs}]")
     ll64 = ll.astype(np.float64)
     p_ref = np.exp(ll64 - ll64.max(axis=1, keepdims=True))
     p_ref /= p_ref.sum(axis=1, keepdims=True)
     assert np.abs(prob - p_ref).max() < 1e-4
     assert np.array_equal(label, np.argmax(ll, axis=1))
-    say(f"decision-word[config 3 full]: rows {t.n_int}, sampled max |dll| {worst:.2e}")

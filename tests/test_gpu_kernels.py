@@ -191,6 +191,67 @@ def test_lmhead_zero_hidden_gives_log_vocab(dev):
     np.testing.assert_allclose(lp[:, 1:], -np.log(cfg.V), atol=2e-6)
 
 
+# Full-size head (Qwen3-4B shapes: d = 2,560, 40 k-steps of 64 with no padding;
+# V = 151,936, 594 vocabulary tiles over several persistent rounds), element by
+# element against the oracle.  Rows R = 8 B on the running-example trie; the
+# launcher takes 128-row tiles at R = 128 and 256 and 256-row tiles from 512 rows;
+# past 4,096 rows the partials are stored tile-major (sampled documents checked).
+# A dropped 256-entry vocabulary tile would move lse by about 1.7e-3.
+FULL_HEAD = {
+    "bf16-R128": ("bf16", 16, None),
+    "bf16-R256": ("bf16", 32, None),
+    "bf16-R512": ("bf16", 64, None),
+    "fp8-R1024": ("fp8", 128, None),
+    "w8a8-R1024": ("fp8a8", 128, None),
+    "bf16-R4160": ("bf16", 520, [0, 1, 31, 32, 255, 256, 300, 511, 512, 519]),
+}
+
+
+@pytest.fixture(scope="module")
+def full_head_inputs():
+    """Weights of the running-example (bf16 head) and long-document (fp8 head)
+    workloads; a one-token batch, since only the weights are used."""
+    cache = {}
+
+    def get(kind):
+        if kind not in cache:
+            base = 5 if kind in ("fp8", "fp8a8") else 2
+            cfg = config(base, B=1, L=1, head={"fp8": "fp8", "fp8a8": "fp8a8"}.get(kind, "same"))
+            inp = make_inputs(cfg)
+            cache.clear()
+            cache[kind] = (cfg, inp, tcs.Model(cfg, inp), O.OracleModel(inp))
+        return cache[kind]
+    return get
+
+
+@pytest.mark.parametrize("name", list(FULL_HEAD))
+def test_lmhead_full_size_vs_oracle(dev, full_head_inputs, name):
+    torch = _torch()
+    kind, B, docs = FULL_HEAD[name]
+    cfg, inp, model, omodel = full_head_inputs(kind)
+    t = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
+    td = tcs.TrieDevice(t)
+    trie = O.build_trie(inp["labels"], inp["root_token"], cfg.V)
+    R = B * trie.n_int
+    h = O.round_bf16(np.random.default_rng(R).standard_normal((R, cfg.d)))
+    say(f"lmhead-full[{name}]: R={R} d={cfg.d} V={cfg.V}")
+    lse, lp = tcs.lmhead_lse_gather(to_bf16_exact(h).cuda(), model.t["W"], td, B,
+                                    w_scale=model.t["W_scale"], act8=(kind == "fp8a8"))
+    torch.cuda.synchronize()
+    lse = lse.cpu().numpy().reshape(B, trie.n_int)
+    lp = lp.cpu().numpy()
+    docs = list(range(B)) if docs is None else docs
+    hs = h.reshape(B, trie.n_int, cfg.d)[docs]
+    o_lse = O.lm_head_lse(omodel, hs.reshape(-1, cfg.d)).reshape(len(docs), trie.n_int)
+    o_lp = O.edge_logprobs(omodel, trie, hs, o_lse)
+    e1 = np.abs(lse[docs] - o_lse).max()
+    e2 = np.abs(lp[docs] - o_lp).max()
+    say(f"lmhead-full[{name}]: {len(docs)} docs compared, max |dlse| {e1:.2e} max |dlp| {e2:.2e}")
+    assert e1 < 2e-4 and e2 < 2e-4
+    assert np.all(lp[:, 0] == 0)
+    assert np.all(np.isfinite(lse)) and np.all(np.isfinite(lp))
+
+
 # ------------------------------------------------------------------ tree attention
 
 ATTN_CASES = {

@@ -94,7 +94,7 @@ def lib():
         L.tcs_tree_attn.argtypes = [vp, C.c_int, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                     C.c_float, vp, vp, sz]
         L.tcs_lmhead_workspace_bytes.restype = sz
-        L.tcs_lmhead_workspace_bytes.argtypes = [C.c_int, i32, i32, i32, i32, i32]
+        L.tcs_lmhead_workspace_bytes.argtypes = [C.c_int, C.c_int, i32, i32, i32, i32, i32]
         L.tcs_lmhead_lse_gather.argtypes = [vp, C.c_int, C.c_int, i32, i32, i32, i32, i32, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, sz]
         L.tcs_path_sum_softmax.argtypes = [vp, i32, C.POINTER(tcs_trie_dev), vp, vp, vp, vp]
@@ -321,18 +321,20 @@ def tree_attn(Qn, Kn, Vn, Kd, Vd, doc_offsets, qparent, scale, O=None, ws=None, 
     return O
 
 
-def lmhead_workspace_bytes(B, n_int, n_nodes, d, V, h_dtype=TCS_BF16) -> int:
-    n = int(lib().tcs_lmhead_workspace_bytes(h_dtype, B, n_int, n_nodes, d, V))
+def lmhead_workspace_bytes(B, n_int, n_nodes, d, V, h_dtype=TCS_BF16, w_dtype=None) -> int:
+    w_dtype = h_dtype if w_dtype is None else w_dtype
+    n = int(lib().tcs_lmhead_workspace_bytes(h_dtype, w_dtype, B, n_int, n_nodes, d, V))
     if n == 0:
         _check(TCS_EINVAL)
     return n
 
 
 def lmhead_lse_gather(h, W, trie_dev: TrieDevice, B, w_scale=None, lse=None, lp=None, ws=None,
-                      stream=None):
+                      stream=None, act8=False):
     """Output head with fused log-sum-exp and child gather (tcs_lmhead_lse_gather).
 
-    h [B * n_int, d]; W [V, d] (bf16/f32, or uint8 E4M3 codes with w_scale [V]).
+    h [B * n_int, d]; W [V, d] (bf16/f32, or uint8 E4M3 codes with w_scale [V]);
+    act8 (fp8 W only): quantize each row of h to E4M3 first (the W8A8 head).
     Returns (lse [B * n_int], lp [B, n_nodes]).
     """
     torch = _torch()
@@ -345,12 +347,17 @@ def lmhead_lse_gather(h, W, trie_dev: TrieDevice, B, w_scale=None, lse=None, lp=
         lse = torch.empty(R, dtype=torch.float32, device=h.device)
     if lp is None:
         lp = torch.empty((B, t.n_nodes), dtype=torch.float32, device=h.device)
-    need = lmhead_workspace_bytes(B, t.n_int, t.n_nodes, d, V, _dtype_code(h))
+    w_code = _dtype_code(W)
+    if act8:
+        if w_code != TCS_FP8_E4M3:
+            raise ValueError("act8 needs E4M3 weights")
+        w_code = TCS_FP8_E4M3_A8
+    need = lmhead_workspace_bytes(B, t.n_int, t.n_nodes, d, V, _dtype_code(h), w_code)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     _need_cuda(h, W, w_scale, lse, lp, ws)
     _check(lib().tcs_lmhead_lse_gather(
-        _stream(stream), _dtype_code(h), _dtype_code(W), B, t.n_int, t.n_nodes, d, V, _ptr(h),
+        _stream(stream), _dtype_code(h), w_code, B, t.n_int, t.n_nodes, d, V, _ptr(h),
         _ptr(W), _ptr(w_scale), _ptr(trie_dev["e_tok"]), _ptr(trie_dev["e_qrow"]),
         _ptr(trie_dev["e_child"]), _ptr(lse), _ptr(lp), _ptr(ws), ws.numel()))
     return lse, lp

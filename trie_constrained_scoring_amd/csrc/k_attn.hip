@@ -1,9 +1,9 @@
 // Ancestor-masked tree attention.
 //
-// "To Classify, Try a Trie Tree", section 3.2 ("Custom attention kernel"): all
-// answer nodes of a document go in one request and each node attends only to the
-// prompt and to the nodes on its own path.  The scores of a node against its own
-// path do not depend on the document, so they are reduced once per trie to a
+// "To Classify, Try a Trie Tree", section 3.2 ("Custom attention kernel"): one
+// request carries every answer node of a document, and a node's keys are the
+// document's plus those of its ancestors and itself, never a sibling branch's.  The
+// scores of a node against its ancestor chain do not depend on the document, so they are reduced once per trie to a
 // softmax partial (max, sum, weighted value sum) per (node, head).  The document
 // part is a dense attention of every node query against the document's keys; its
 // online-softmax state is merged with the path partial by log-sum-exp at the end,

@@ -955,9 +955,10 @@ size_t lmhead_part_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t V)
   return align_up(parts * size_t(B) * n_int * 8);
 }
 
-size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
-                       int32_t V) {
-  return lmhead_prep_bytes(h_dtype, B, n_int, n_nodes, d, V) + lmhead_part_bytes(h_dtype, B, n_int, V);
+size_t lmhead_ws_bytes(tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                       int32_t n_nodes, int32_t d, int32_t V) {
+  return lmhead_prep_bytes(h_dtype, B, n_int, n_nodes, d, V) + lmhead_part_bytes(h_dtype, B, n_int, V) +
+         lmhead_act8_bytes(w_dtype, B * n_int, d);
 }
 
 int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
@@ -1135,12 +1136,15 @@ int launch_lmhead(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
                   int32_t n_nodes, int32_t d, int32_t V, const void* h, const void* W,
                   const float* w_scale, const int32_t* e_tok, const int32_t* e_qrow,
                   const int32_t* e_child, int32_t n_edges, float* lse, float* lp, void* ws) {
+  // workspace: [prepared gather lists | partials | fp8 codes and scales of h (W8A8)]
   const size_t pb = lmhead_prep_bytes(h_dtype, B, n_int, n_nodes, d, V);
+  const size_t qb = lmhead_part_bytes(h_dtype, B, n_int, V);
   if (int rc = launch_lmhead_prep(stream, h_dtype, B, n_int, n_nodes, d, V, e_tok, e_qrow, e_child,
                                   n_edges, ws))
     return rc;
+  void* act8 = w_dtype == TCS_FP8_E4M3_A8 ? static_cast<char*>(ws) + pb + qb : nullptr;
   return launch_lmhead_run(stream, h_dtype, w_dtype, B, n_int, n_nodes, d, V, h, W, w_scale, e_tok,
-                           e_qrow, e_child, lse, lp, ws, static_cast<char*>(ws) + pb);
+                           e_qrow, e_child, lse, lp, ws, static_cast<char*>(ws) + pb, true, act8);
 }
 
 }  // namespace tcs

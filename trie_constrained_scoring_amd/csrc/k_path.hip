@@ -400,7 +400,8 @@ __global__ __launch_bounds__(PATH_THREADS) void path_levels_kernel(
 }
 
 static bool path_levels_ok(const tcs_trie_dev* trie) {
-  return trie->qrow && trie->row_level_offsets && trie->label_row && trie->n_int <= PATH_MAX_ROWS &&
+  return trie->qrow && trie->qparent && trie->row_level_offsets && trie->label_row &&
+         trie->n_int <= PATH_MAX_ROWS &&
          trie->max_depth + 2 <= PATH_MAX_LEVELS && trie->n_labels <= PATH_LREG * PATH_THREADS &&
          trie->n_nodes <= 32768;
 }

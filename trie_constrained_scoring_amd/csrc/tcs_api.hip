@@ -85,10 +85,17 @@ int tcs_tree_attn(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, 
                         qparent, scale, O, ws);
 }
 
-size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
-                                  int32_t d, int32_t V) {
+static bool head_dtypes_ok(tcs_dtype h_dtype, tcs_dtype w_dtype) {
+  if (h_dtype != TCS_F32 && h_dtype != TCS_BF16) return false;
+  return w_dtype == h_dtype ||
+         (h_dtype == TCS_BF16 && (w_dtype == TCS_FP8_E4M3 || w_dtype == TCS_FP8_E4M3_A8));
+}
+
+size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                                  int32_t n_nodes, int32_t d, int32_t V) {
+  if (!head_dtypes_ok(h_dtype, w_dtype)) return 0;
   if (B < 0 || n_int < 1 || n_nodes < 2 || d < 1 || V < 1 || int64_t(B) * n_int > INT32_MAX) return 0;
-  return lmhead_ws_bytes(h_dtype, B, n_int, n_nodes, d, V);
+  return lmhead_ws_bytes(h_dtype, w_dtype, B, n_int, n_nodes, d, V);
 }
 
 int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B,
@@ -97,20 +104,19 @@ int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtyp
                           const int32_t* e_qrow, const int32_t* e_child, float* lse, float* lp,
                           void* ws, size_t ws_bytes) {
   clear_error();
-  if (h_dtype != TCS_F32 && h_dtype != TCS_BF16)
-    return fail(TCS_EUNSUPPORTED, "lmhead: h dtype %d", int(h_dtype));
-  if (!(w_dtype == h_dtype || (h_dtype == TCS_BF16 && w_dtype == TCS_FP8_E4M3)))
+  if (!head_dtypes_ok(h_dtype, w_dtype))
     return fail(TCS_EUNSUPPORTED, "lmhead: weight dtype %d with h dtype %d", int(w_dtype), int(h_dtype));
   if (B < 0 || n_int < 1 || n_nodes < 2 || d < 1 || V < 1)
     return fail(TCS_EINVAL, "lmhead: B=%d n_int=%d n_nodes=%d d=%d V=%d", B, n_int, n_nodes, d, V);
   if (h_dtype == TCS_BF16 && d % 64 != 0)
     return fail(TCS_EUNSUPPORTED, "lmhead: bf16 head needs d %% 64 == 0 (d=%d)", d);
   if (B == 0) return TCS_OK;
-  if (!h || !W || !e_tok || !e_qrow || !e_child || !lse || !lp || (w_dtype == TCS_FP8_E4M3 && !w_scale))
+  const bool fp8_w = w_dtype == TCS_FP8_E4M3 || w_dtype == TCS_FP8_E4M3_A8;
+  if (!h || !W || !e_tok || !e_qrow || !e_child || !lse || !lp || (fp8_w && !w_scale))
     return fail(TCS_EINVAL, "lmhead: null pointer");
   const int64_t rows = int64_t(B) * n_int;
   if (rows > INT32_MAX) return fail(TCS_EINVAL, "lmhead: %lld rows", (long long)rows);
-  const size_t need = lmhead_ws_bytes(h_dtype, B, n_int, n_nodes, d, V);
+  const size_t need = lmhead_ws_bytes(h_dtype, w_dtype, B, n_int, n_nodes, d, V);
   if (!ws || ws_bytes < need) return fail(TCS_ECAPACITY, "lmhead: workspace %zu < %zu bytes", ws_bytes, need);
   return launch_lmhead(stream, h_dtype, w_dtype, B, n_int, n_nodes, d, V, h, W, w_scale, e_tok,
                        e_qrow, e_child, n_nodes - 1, lse, lp, ws);
@@ -124,7 +130,7 @@ int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie,
     return fail(TCS_EINVAL, "path_sum: B=%d M=%d n_nodes=%d", B, trie->n_labels, trie->n_nodes);
   if (B == 0) return TCS_OK;
   if (!lp || !ll || !label || !trie->parent || !trie->child_begin || !trie->child_count ||
-      !trie->label_node)
+      !trie->label_node || !trie->qparent)
     return fail(TCS_EINVAL, "path_sum: null pointer");
   return launch_path_sum(stream, B, trie, lp, ll, prob, label);
 }

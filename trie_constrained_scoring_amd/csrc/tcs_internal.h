@@ -80,13 +80,14 @@ int launch_zero_fill(void* stream, void* p, size_t bytes);
 // Output head, see tcs_lmhead_lse_gather.  Its workspace is a per-label-set part
 // (lmhead_prep_bytes: edge segments, zero block, gather lists for batches of B
 // documents; written by launch_lmhead_prep) followed by the per-batch (max, sum exp)
-// partials (lmhead_part_bytes).  launch_lmhead does both on one workspace.
+// partials (lmhead_part_bytes), then for a W8A8 head the hidden rows' codes and
+// scales (lmhead_act8_bytes).  launch_lmhead does all of it on one workspace.
 int lmhead_n_tiles(tcs_dtype h_dtype, int32_t V);
 size_t lmhead_prep_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
                          int32_t V);
 size_t lmhead_part_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t V);
-size_t lmhead_ws_bytes(tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes, int32_t d,
-                       int32_t V);
+size_t lmhead_ws_bytes(tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
+                       int32_t n_nodes, int32_t d, int32_t V);
 int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int, int32_t n_nodes,
                        int32_t d, int32_t V, const int32_t* e_tok, const int32_t* e_qrow,
                        const int32_t* e_child, int32_t n_edges, void* prep);

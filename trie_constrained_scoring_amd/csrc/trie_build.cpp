@@ -236,8 +236,8 @@ extern "C" int tcs_trie_build(const int32_t* label_offsets, const int32_t* label
 
 // Decision-word cut of every label ("To Classify, Try a Trie Tree", section 3.2).
 // One pass inserts the labels into a (node, token) map and counts, per node, the
-// labels that pass through it; label m leaves all others at the first node on its
-// path that it alone passes, and its word then runs on over the continuation tokens.
+// labels that pass through it; label m separates from the rest at the first node
+// on its path that no other label passes, and its word then runs on over the continuation tokens.
 extern "C" int tcs_decision_truncate(const int32_t* label_offsets, const int32_t* label_tokens,
                                      int32_t M, int32_t V, const uint8_t* word_cont,
                                      int32_t* out_offsets, int32_t* out_tokens, int32_t* depth) {
