@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--extra 3,4]
                     [--no-cpu-baseline] [--no-path-stress] [--no-decision-word] [--no-letters]
-                    [--no-decode] [--no-shard] [--no-w8a8]
+                    [--no-decode] [--no-long-document] [--no-shard] [--no-w8a8]
     python bench.py --copy-calibration     # plain copy of known size, for HBM counters
     python bench.py --head-probe --config 3 [--power]  # head alone: workload-like vs constant
                                                        # operands (+ socket power and clocks)
@@ -29,6 +29,9 @@ of trie_tree: fewer query rows, same kernels); the headline scores every label o
 its full root-to-leaf path.  ``letters`` runs them under the letters method (one
 answer position per document, only the letter rows of the head), ``trie_decode`` under
 greedy decoding in the trie (one answer position per undecided document per step).
+``long_document`` runs the long-document workload as stated (B = 128 documents of 4,096
+tokens, fp8 head weights with bf16 activations), where the document attention streams
+2.1 GB of keys and values per batch.
 ``w8a8`` runs the long-document workload with the hidden rows quantized to E4M3 before
 the head (fp8 x fp8 matrix cores; roofline against the 5.0 PFLOP/s fp8 peak).
 ``shard_of_8`` runs the long-document workload at one GPU's share of an 8-GPU run
@@ -95,14 +98,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup(cid: int, streams: int = 1, **overrides):
+def setup(cid: int, streams: int = 1, inp=None, **overrides):
+    """Inputs (generated, or `inp` when given: arrays drawn for this workload), the
+    trie, device weights and documents, the prepared state and run buffers."""
     import torch
     import trie_constrained_scoring_amd as tcs
     from synth import config, make_inputs
     cfg = config(cid, **overrides)
-    t0 = time.time()
-    inp = make_inputs(cfg)
-    log(f"[bench] config {cid} inputs generated in {time.time() - t0:.1f}s")
+    if inp is None:
+        t0 = time.time()
+        inp = make_inputs(cfg)
+        log(f"[bench] config {cid} inputs generated in {time.time() - t0:.1f}s")
+    else:
+        inp = dict(inp, cfg=cfg)
     t0 = time.perf_counter()
     trie = tcs.trie_build(inp["label_offsets"], inp["label_tokens"], inp["root_token"], cfg.V)
     trie_ms = (time.perf_counter() - t0) * 1e3
@@ -338,6 +346,24 @@ def decode_measure(S, steps, warmup, streams):
     return e
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def first_docs(inp, n):
+    """The first n documents of a key/value batch (a view of the same arrays)."""
+    offs = inp["doc_offsets"][:n + 1]
+    return dict(inp, doc_offsets=offs, Kd=inp["Kd"][:offs[-1]], Vd=inp["Vd"][:offs[-1]])
+
+
 def cpu_baseline(S, budget_s=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of documents."""
     import oracle as O
@@ -354,7 +380,8 @@ def cpu_baseline(S, budget_s=15.0):
     t0 = time.perf_counter()
     O.classify(inp, docs=list(range(n)), model=model, trie=trie)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "docs/s", "cores": cores, "kind": "oracle",
+    return {"value": n / dt, "unit": "docs/s", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{n} of {S['docs'].B} documents of the same batch, every label, fp64 numpy "
                       f"(BLAS threads = visible cores), {dt:.1f}s"}
 
@@ -502,6 +529,8 @@ def main():
                     help="output-head kind for the primary workload (default: the workload's own)")
     ap.add_argument("--no-w8a8", action="store_true",
                     help="leave out the long-document workload with the W8A8 head (fp8 activations)")
+    ap.add_argument("--no-long-document", action="store_true",
+                    help="leave out the long-document workload (B = 128 x 4096, W8A16 head)")
     ap.add_argument("--no-shard", action="store_true",
                     help="leave out the long-document workload at one GPU's share of 8 (B = 16)")
     ap.add_argument("--no-decode", action="store_true",
@@ -612,12 +641,43 @@ def main():
         S = S2
     if extra:
         res["at_labels"] = extra
+    # the long-document workload (B = 128 x 4,096 tokens) as stated: bf16 activations,
+    # fp8 head weights (W8A16); its inputs are drawn once and serve the W8A8 and
+    # one-GPU-share passes below as well
+    inp5 = None
+    if args.config != 5 and not (args.no_long_document and args.no_w8a8 and args.no_shard):
+        from synth import config as _config, make_inputs
+        del S
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        inp5 = make_inputs(_config(5))
+        log(f"[bench] config 5 inputs generated in {time.time() - t0:.1f}s")
+        S = None
+    if inp5 is not None and not args.no_long_document:
+        del S
+        torch.cuda.empty_cache()
+        S = setup(5, args.streams, inp=inp5)
+        sl, kl = run_steps(S, *long_enough(S, few, 10))
+        fl, Rl = head_flops(S)
+        tf = fl / (kl["head"] * 1e-3) / 1e12
+        t5 = S["trie"]
+        res["long_document"] = {
+            "config": 5, "workload": f"long-document-kv: B={S['docs'].B} docs x {S['cfg'].L} tokens, "
+                                     f"{t5.n_labels} labels, fp8 e4m3 head weights + fp32 row scales, "
+                                     "bf16 activations (W8A16)",
+            "docs_per_s": round(S["docs"].B / sl, 2), "ms_per_step": round(sl * 1e3, 4),
+            "trie_nodes_per_s": round(S["docs"].B * t5.n_nodes / sl, 1),
+            "head_ms": round(kl["head"], 4), "head_rows": Rl, "head_tflops": round(tf, 2),
+            "head_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "head_share_of_step": round(kl["head"] / (sl * 1e3), 4)}
+        if kl["doc_attn"]:
+            res["long_document"]["doc_attn_roofline"] = doc_attn_roofline(S, kl["doc_attn"])
     if not args.no_w8a8 and cfg.head != "fp8a8":
         # the long-document workload with its hidden rows quantized to E4M3 before
         # the head (fp8 x fp8 matrix cores); a precision change, so reported apart
         del S
         torch.cuda.empty_cache()
-        S = setup(5, args.streams, head="fp8a8")
+        S = setup(5, args.streams, inp=inp5, head="fp8a8")
         s8, k8 = run_steps(S, *long_enough(S, few, 10))
         f8, R8 = head_flops(S)
         tf = f8 / (k8["head"] * 1e-3) / 1e12
@@ -632,7 +692,7 @@ def main():
         # 128-document long-document batch over 8 GPUs is 16 documents
         del S
         torch.cuda.empty_cache()
-        S = setup(5, args.streams, B=16)
+        S = setup(5, args.streams, inp=first_docs(inp5, 16) if inp5 is not None else None, B=16)
         s5, k5 = run_steps(S, *long_enough(S, few, 10))
         f5, _ = head_flops(S)
         tf = f5 / (k5["head"] * 1e-3) / 1e12
@@ -642,6 +702,7 @@ def main():
                              "head_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         if k5["doc_attn"]:
             res["shard_of_8"]["doc_attn_roofline"] = doc_attn_roofline(S, k5["doc_attn"])
+    del inp5
     if decision:
         res["decision_word"] = decision
     if letters:

@@ -56,8 +56,11 @@ reason in the design notes):
       activations): each stored hidden row h (bf16 values) is quantized before the
       head with s = fl32(max|h| / 448) and codes = E4M3(fl32(h / s)), nearest value,
       ties to the even code, saturating at 448 (an all-zero row keeps s = 0); the
-      logit is s * s_w * sum(codes_h * codes_w).  The scale and the quotients are
-      fp32, as the kernel computes them, because they decide integer codes.
+      logit is s * s_w * sum(codes_h * codes_w).  The scales are fp32 numbers, as
+      the pages' per-row scales are, and the quotient h / s that the rounding to a
+      code decides on is taken in that same fp32 precision (correctly rounded):
+      where floating point decides an integer code, both sides take the decision in
+      the precision the format fixes.
 
 Parity status: every function below is pinned by the non-GPU oracle tests
 (library routines, closed forms, the worked example, brute-force scoring).

@@ -214,11 +214,15 @@ def full_head_inputs():
     cache = {}
 
     def get(kind):
-        if kind not in cache:
-            base = 5 if kind in ("fp8", "fp8a8") else 2
-            cfg = config(base, B=1, L=1, head={"fp8": "fp8", "fp8a8": "fp8a8"}.get(kind, "same"))
-            inp = make_inputs(cfg)
+        base = 5 if kind in ("fp8", "fp8a8") else 2
+        if cache.get("base") != base:
             cache.clear()
+            cache["base"] = base
+            cache["inp"] = make_inputs(config(base, B=1, L=1))
+        if kind not in cache:
+            # the W8A8 head reads the same E4M3 weights; only the activations differ
+            cfg = config(base, B=1, L=1, head={"fp8": "fp8", "fp8a8": "fp8a8"}.get(kind, "same"))
+            inp = dict(cache["inp"], cfg=cfg)
             cache[kind] = (cfg, inp, tcs.Model(cfg, inp), O.OracleModel(inp))
         return cache[kind]
     return get

@@ -3,8 +3,9 @@
 // "To Classify, Try a Trie Tree", section 3.2 ("Custom attention kernel"): one
 // request carries every answer node of a document, and a node's keys are the
 // document's plus those of its ancestors and itself, never a sibling branch's.  The
-// scores of a node against its ancestor chain do not depend on the document, so they are reduced once per trie to a
-// softmax partial (max, sum, weighted value sum) per (node, head).  The document
+// scores of a node against its ancestor chain do not depend on the document, so
+// they are reduced once per trie to a softmax partial (max, sum, weighted value
+// sum) per (node, head).  The document
 // part is a dense attention of every node query against the document's keys; its
 // online-softmax state is merged with the path partial by log-sum-exp at the end,
 // the same combine that "Building an Ultra-High Throughput AI-SQL Engine"

@@ -1054,7 +1054,6 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
   Carve cv(const_cast<void*>(prep));
   const HeadPrep P = head_prep_layout(cv, h_dtype, B, n_int, n_nodes, d, V);
   float2* p = static_cast<float2*>(part);
-  const int n_rt = (R + 255) / 256;
   int n_parts = n_tiles;
   timer_begin(TCS_TIMER_HEAD, stream);
   if (h_dtype == TCS_BF16) {

@@ -1,7 +1,6 @@
 // C-ABI entry points of libtcs: argument checks, workspace layout, and the
 // classify chain on one stream.
 #include <cmath>
-#include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
@@ -10,17 +9,6 @@
 #include "tcs_internal.h"
 
 namespace tcs {
-
-static thread_local char g_err[512] = "";
-
-int fail(int code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof(g_err), fmt, ap);
-  va_end(ap);
-  return code;
-}
-void clear_error() { g_err[0] = 0; }
 
 int launch_attn_simt(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_t Hq, int32_t Hkv,
                      int32_t hd, const void* Qn, const void* Kn, const void* Vn, const void* Kd,
@@ -61,9 +49,6 @@ static int tree_attn_impl(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, 
 using namespace tcs;
 
 extern "C" {
-
-const char* tcs_last_error(void) { return g_err; }
-const char* tcs_version(void) { return "libtcs 0.1 (gfx950)"; }
 
 size_t tcs_tree_attn_workspace_bytes(int32_t n_int, int32_t Hq, int32_t hd) {
   return anc_bytes(n_int, Hq, hd);
