@@ -204,6 +204,32 @@ int tcs_tree_attn(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, 
                   const void* Kd, const void* Vd, const int32_t* doc_offsets,
                   const int32_t* qparent, float scale, void* O, void* ws, size_t ws_bytes);
 
+/*
+ * tcs_tree_attn without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  Arguments, layouts and results are those of
+ * tcs_tree_attn (same kernels, bit-identical output).  The scratch that
+ * tcs_tree_attn takes from `ws` (tcs_tree_attn_workspace_bytes(n_int, Hq, hd)
+ * bytes: the per-(row, head) path partials) lives instead in a device array inside
+ * the library of TCS_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the
+ * process ends; its address is looked up once per device on the first call with
+ * that device current.  No memory is allocated or freed by the call.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other host threads) race and give undefined results; calls in
+ * order on one stream are safe.  Each call rewrites every scratch entry it reads,
+ * so nothing needs clearing between calls.
+ * Errors: as tcs_tree_attn, and TCS_ECAPACITY when the scratch needed exceeds
+ * TCS_NOALLOC_SCRATCH_BYTES (about 32,000 (row, head) pairs at head_dim 128, e.g.
+ * 1,008 query rows with 32 heads), TCS_EHIP if the array's address cannot be found.
+ */
+#define TCS_NOALLOC_SCRATCH_BYTES (16u << 20)
+int tcs_tree_attn_noalloc(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int,
+                          int32_t Hq, int32_t Hkv, int32_t hd, const void* Qn, const void* Kn,
+                          const void* Vn, const void* Kd, const void* Vd,
+                          const int32_t* doc_offsets, const int32_t* qparent, float scale,
+                          void* O);
+
 /* ------------------------------------------------------------- LM head ---- */
 
 /*

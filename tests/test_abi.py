@@ -147,6 +147,23 @@ def test_lmhead_workspace_query_by_dtype_pair():
                                      *([None] * 9), 0) == tcs.TCS_EUNSUPPORTED
 
 
+def test_tree_attn_noalloc_refuses_oversize_without_gpu():
+    """tcs_tree_attn_noalloc checks its sizes before any HIP call: scratch beyond the
+    built-in array is refused with TCS_ECAPACITY (pointers are never dereferenced)."""
+    lib = tcs.lib()
+    fake = C.c_void_p(256)
+    n_ok = 1
+    while tcs.tree_attn_workspace_bytes(n_ok + 1, 32, 128) <= tcs.NOALLOC_SCRATCH_BYTES:
+        n_ok += 1
+    assert n_ok >= 1000
+    rc = lib.tcs_tree_attn_noalloc(None, tcs.TCS_BF16, 1, n_ok + 1, 32, 8, 128, *([fake] * 7), 1.0, fake)
+    assert rc == tcs.TCS_ECAPACITY and b"scratch" in lib.tcs_last_error()
+    assert lib.tcs_tree_attn_noalloc(None, tcs.TCS_BF16, 1, 4, 4, 2, 96, *([fake] * 7), 1.0, fake) == \
+        tcs.TCS_EUNSUPPORTED
+    assert lib.tcs_tree_attn_noalloc(None, tcs.TCS_BF16, 1, 4, 4, 2, 128, *([None] * 7), 1.0, None) == \
+        tcs.TCS_EINVAL
+
+
 def test_timing_api_without_launches():
     tcs.timing_enable(True)
     assert tcs.timing_read(tcs.TCS_TIMER_HEAD) == (0.0, 0)

@@ -93,6 +93,8 @@ def lib():
         L.tcs_tree_attn_workspace_bytes.argtypes = [i32, i32, i32]
         L.tcs_tree_attn.argtypes = [vp, C.c_int, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                     C.c_float, vp, vp, sz]
+        L.tcs_tree_attn_noalloc.argtypes = [vp, C.c_int, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                            vp, vp, C.c_float, vp]
         L.tcs_lmhead_workspace_bytes.restype = sz
         L.tcs_lmhead_workspace_bytes.argtypes = [C.c_int, C.c_int, i32, i32, i32, i32, i32]
         L.tcs_lmhead_lse_gather.argtypes = [vp, C.c_int, C.c_int, i32, i32, i32, i32, i32, vp, vp,
@@ -318,6 +320,26 @@ def tree_attn(Qn, Kn, Vn, Kd, Vd, doc_offsets, qparent, scale, O=None, ws=None, 
     _check(lib().tcs_tree_attn(_stream(stream), _dtype_code(Qn), B, n_int, Hq, Hkv, hd, _ptr(Qn),
                                _ptr(Kn), _ptr(Vn), _ptr(Kd), _ptr(Vd), _ptr(doc_offsets),
                                _ptr(qparent), float(scale), _ptr(O), _ptr(ws), ws.numel()))
+    return O
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # TCS_NOALLOC_SCRATCH_BYTES in include/tcs.h
+
+
+def tree_attn_noalloc(Qn, Kn, Vn, Kd, Vd, doc_offsets, qparent, scale, O=None, stream=None):
+    """tcs_tree_attn_noalloc: tcs_tree_attn with its scratch in the library's own
+    per-GPU device array (no workspace argument, nothing allocated by the call).
+    Calls that overlap on one GPU race on that array."""
+    torch = _torch()
+    n_int, Hq, hd = Qn.shape
+    Hkv = Kn.shape[1]
+    B = doc_offsets.shape[0] - 1
+    if O is None:
+        O = torch.empty((B, n_int, Hq, hd), dtype=Qn.dtype, device=Qn.device)
+    _need_cuda(Qn, Kn, Vn, Kd, Vd, doc_offsets, qparent, O)
+    _check(lib().tcs_tree_attn_noalloc(_stream(stream), _dtype_code(Qn), B, n_int, Hq, Hkv, hd,
+                                       _ptr(Qn), _ptr(Kn), _ptr(Vn), _ptr(Kd), _ptr(Vd),
+                                       _ptr(doc_offsets), _ptr(qparent), float(scale), _ptr(O)))
     return O
 
 

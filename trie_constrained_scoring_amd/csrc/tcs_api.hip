@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -44,6 +45,36 @@ static int tree_attn_impl(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, 
 }
 
 
+// Scratch of tcs_tree_attn_noalloc: the path partials live in this file-scope
+// device array instead of a caller workspace.  Every GPU the library runs on holds
+// its own copy until the process ends.  In host code the array's name is only a
+// stand-in: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[TCS_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first call
+// for that device, with the device current).
+static int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TCS_EHIP, "tree_attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TCS_EUNSUPPORTED, "tree_attn_noalloc: device %d (at most %d devices)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(TCS_EHIP, "tree_attn_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TCS_OK;
+}
+
 }  // namespace tcs
 
 using namespace tcs;
@@ -74,6 +105,29 @@ static bool head_dtypes_ok(tcs_dtype h_dtype, tcs_dtype w_dtype) {
   if (h_dtype != TCS_F32 && h_dtype != TCS_BF16) return false;
   return w_dtype == h_dtype ||
          (h_dtype == TCS_BF16 && (w_dtype == TCS_FP8_E4M3 || w_dtype == TCS_FP8_E4M3_A8));
+}
+
+int tcs_tree_attn_noalloc(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t n_int, int32_t Hq,
+                          int32_t Hkv, int32_t hd, const void* Qn, const void* Kn, const void* Vn,
+                          const void* Kd, const void* Vd, const int32_t* doc_offsets,
+                          const int32_t* qparent, float scale, void* O) {
+  clear_error();
+  if (int rc = check_attn_dims(dtype, Hq, Hkv, hd)) return rc;
+  if (B < 0 || n_int < 0) return fail(TCS_EINVAL, "tree_attn_noalloc: B=%d n_int=%d", B, n_int);
+  if (B == 0 || n_int == 0) return TCS_OK;
+  if (!Qn || !Kn || !Vn || !Kd || !Vd || !doc_offsets || !qparent || !O)
+    return fail(TCS_EINVAL, "tree_attn_noalloc: null pointer");
+  const size_t need = dtype == TCS_BF16 ? anc_bytes(n_int, Hq, hd) : 0;
+  if (need > TCS_NOALLOC_SCRATCH_BYTES)
+    return fail(TCS_ECAPACITY,
+                "tree_attn_noalloc: %d rows x %d heads need %zu bytes of scratch, more than the "
+                "built-in %zu (use tcs_tree_attn with a workspace)",
+                n_int, Hq, need, size_t(TCS_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0)
+    if (int rc = noalloc_scratch(&ws)) return rc;
+  return tree_attn_impl(stream, dtype, B, n_int, Hq, Hkv, hd, Qn, Kn, Vn, Kd, Vd, doc_offsets,
+                        qparent, scale, O, ws);
 }
 
 size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
