@@ -11,6 +11,7 @@
 // the same combine that "Building an Ultra-High Throughput AI-SQL Engine"
 // (section 3.2.4) applies to its two attention calls for joins.
 #include <algorithm>
+#include <type_traits>
 #include <cstdio>
 
 #include "tcs_device.h"
@@ -1091,6 +1092,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
 // lane merges its row with the row's path partial and writes its half of the row
 // straight from the accumulators, so the ring keeps loading meanwhile.  Two
 // workgroups fit on a CU (64 KB of LDS each).
+constexpr int ROWS_DMA_MAX_DPW = 64;  // documents per workgroup of the kernel below, at most
 __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
     int B, int dpw, int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn,
     const uint16_t* __restrict__ Kd, const uint16_t* __restrict__ Vd,
@@ -1102,7 +1104,16 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
   constexpr int OPB = KT * ROW;          // bytes per operand per stage (16 KB)
   constexpr int SLOT = 2 * OPB;          // K then V
   constexpr int NBLK = HD / 32, KSTEPS = HD / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SLOT];
+  // the two ring slots are distinct arrays, and every stage below is compiled for
+  // one slot parity, so the compiler can tell that a stage's fragment reads and the
+  // next stage's buffer-to-LDS loads touch different memory (with one array and a
+  // computed slot offset it must wait for those loads before the first read)
+  __shared__ __attribute__((aligned(16))) uint8_t slot0[SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t slot1[SLOT];
+  // offsets of the workgroup's documents: the prefetch cursor reads them from LDS,
+  // so stepping into the next document waits on no vector-memory load (a global
+  // read there would also wait for the stage loads just issued)
+  __shared__ int s_doc[ROWS_DMA_MAX_DPW + 1];
 
   const int G = Hq / Hkv;
   const int rows_total = n_int * G;
@@ -1112,6 +1123,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
   const int b_lo = blockIdx.x / (n_rb * Hkv) * dpw;
   const int b_hi = min(B, b_lo + dpw);
   const int tid = threadIdx.x, lane = tid & 63;
+  if (tid <= b_hi - b_lo) s_doc[tid] = doc_offsets[b_lo + tid];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = rb * 128 + wave * 32;   // this wave's first row
   const int RS = Hkv * HD * 2;           // bytes between consecutive keys of one head
@@ -1119,8 +1131,10 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
   // slots start as zeros, so a key past a document's end that no load writes
   // still holds finite values (its weight is 0)
 #pragma unroll
-  for (int i = 0; i < 2 * SLOT / (256 * 16); ++i)
-    *reinterpret_cast<uint4*>(lds + (i * 256 + tid) * 16) = uint4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < SLOT / (256 * 16); ++i) {
+    *reinterpret_cast<uint4*>(slot0 + (i * 256 + tid) * 16) = uint4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(slot1 + (i * 256 + tid) * 16) = uint4{0u, 0u, 0u, 0u};
+  }
   __syncthreads();  // every wave's zeros are in place before any load can land
 
   // Q^T fragments: lane holds row l%32, hd 16 ks + 8 (l/32) ..
@@ -1147,14 +1161,19 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
     const int row = 4 * (4 * wave + jj) + (lane >> 4);
     vo[jj] = row * RS + (((lane & 15) ^ kv_swz(row & 15)) << 4);
   }
-  auto n_stages = [&](int b) { return (doc_offsets[b + 1] - doc_offsets[b] + KT - 1) / KT; };
-  // stage t of document b into slot sl
-  auto issue = [&](int b, int t, int sl) __attribute__((always_inline)) {
-    const int doc0 = doc_offsets[b], L = doc_offsets[b + 1] - doc0;
+  auto doc_at = [&](int b) { return __builtin_amdgcn_readfirstlane(s_doc[b - b_lo]); };
+  auto n_stages = [&](int b) { return (doc_at(b + 1) - doc_at(b) + KT - 1) / KT; };
+  // stage t of document b into ring slot `slot`; past the last document (b = b_hi)
+  // the loads go through a zero-range buffer resource and touch no memory, so every
+  // stage issues the same loads and no branch decides whether a slot is being filled
+  auto issue = [&](int b, int t, uint8_t* slot) __attribute__((always_inline)) {
+    const bool ok = b < b_hi;
+    const int bb = ok ? b : b_lo;
+    const int doc0 = doc_at(bb), L = doc_at(bb + 1) - doc0;
     const int nkeys = min(KT, L - t * KT);
-    const int bytes = (nkeys - 1) * RS + ROW;
+    const int bytes = ok ? (nkeys - 1) * RS + ROW : 0;
     const size_t off = ((size_t)(doc0 + t * KT) * Hkv + g) * HD;
-    uint8_t* dst = lds + sl * SLOT + wave * 4 * 1024;
+    uint8_t* dst = slot + wave * 4 * 1024;
     kv_issue<4>(Kd + off, bytes, dst, vo);
     kv_issue<4>(Vd + off, bytes, dst + OPB, vo);
   };
@@ -1184,7 +1203,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
   int pb = b_lo, pt = 0;
   while (pb < b_hi && n_stages(pb) == 0) ++pb;
   int kc = 0;  // stages computed so far (slot kc & 1)
-  if (pb < b_hi) issue(pb, 0, 0);
+  if (pb < b_hi) issue(pb, 0, slot0);
   auto advance = [&]() __attribute__((always_inline)) {
     if (++pt >= n_stages(pb)) {
       pt = 0;
@@ -1194,7 +1213,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
   advance();
 
   for (int b = b_lo; b < b_hi; ++b) {
-    const int L = doc_offsets[b + 1] - doc_offsets[b];
+    const int L = doc_at(b + 1) - doc_at(b);
     const int nst = (L + KT - 1) / KT;
     f32x16 acc[NBLK];
 #pragma unroll
@@ -1202,16 +1221,18 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
     float m = -INFINITY, lsum = 0.f;  // base-2 running max; this lane's share of the sum
-    for (int t = 0; t < nst; ++t, ++kc) {
+    // one stage; Par = kc & 1 picks the slot it reads and the slot it refills
+    auto stage = [&](auto Par, int t) __attribute__((always_inline)) {
+      constexpr int P = decltype(Par)::value;
+      uint8_t* const cur = P ? slot1 : slot0;
+      uint8_t* const nxt = P ? slot0 : slot1;
       wait_vmcnt<0>();       // this wave's part of stage kc has landed
       wait_lgkmcnt0();       // and its reads of stage kc - 1 are done
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (pb < b_hi) {       // stage kc + 1 into the slot stage kc - 1 used
-        issue(pb, pt, (kc + 1) & 1);
-        advance();
-      }
-      const uint8_t* sl = lds + (kc & 1) * SLOT;
+      issue(pb, pt, nxt);    // stage kc + 1 into the slot stage kc - 1 used
+      if (pb < b_hi) advance();
+      const uint8_t* sl = cur;
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -1275,6 +1296,10 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
             acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[st], acc[blk], 0, 0, 0);
           }
       }
+    };
+    for (int t = 0; t < nst; ++t, ++kc) {
+      if (kc & 1) stage(std::integral_constant<int, 1>{}, t);
+      else stage(std::integral_constant<int, 0>{}, t);
     }
     // merge with the row's path partial; lane writes hd blk*32 + 8 e4 + 4 c + 0..3
     lsum += __shfl_xor(lsum, 32, 64);
@@ -1346,7 +1371,7 @@ int launch_doc_attn(void* stream, tcs_dtype dt, int32_t B, int32_t n_int, int32_
     // are then read once per dpw documents
     const long blocks = long(Hkv) * ((rows + 127) / 128);
     const long chunks = std::min(long(B), (4096 + blocks - 1) / blocks);
-    const int dpw = int(std::max(1L, B / chunks));
+    const int dpw = int(std::min(long(ROWS_DMA_MAX_DPW), std::max(1L, B / chunks)));
     const long grid = blocks * ((B + dpw - 1) / dpw);
     if (hd == 128)
       doc_attn_rows_dma_kernel<<<grid, 256, 0, s>>>(B, dpw, n_int, Hq, Hkv, q, kd, vd, doc_offsets, ml, anc_o, scale, o);
