@@ -1212,23 +1212,67 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
   };
   advance();
 
+  // P^T fragments of one 32-key block, built one pair of keys at a time: pair q
+  // (keys 2q, 2q+1 of the lane's 16) gives word q % 4 of fragment q / 4, as the
+  // weights exp2(s - m) split into a bf16 high part and the bf16 remainder; the
+  // pair's weights are added to ls.
+  auto weight_pair = [&](const f32x16& scb, float mrow, float& ls, int q, uint32_t (&wh)[2][4],
+                         uint32_t (&wl)[2][4]) __attribute__((always_inline)) {
+    const float a = __builtin_amdgcn_exp2f(fmaf(scb[2 * q], qk, -mrow));
+    const float a2 = __builtin_amdgcn_exp2f(fmaf(scb[2 * q + 1], qk, -mrow));
+    ls += a;
+    ls += a2;
+    const uint32_t h2 = pack_bf16(a, a2);
+    wh[q >> 2][q & 3] = h2;
+    wl[q >> 2][q & 3] = pack_bf16(a - __uint_as_float(h2 << 16), a2 - __uint_as_float(h2 & 0xFFFF0000u));
+  };
+  auto frags = [&](const uint32_t (&w)[2][4], int st) __attribute__((always_inline)) {
+    uint4 u{w[st][0], w[st][1], w[st][2], w[st][3]};
+    return *reinterpret_cast<bf16x8*>(&u);
+  };
+
   for (int b = b_lo; b < b_hi; ++b) {
     const int L = doc_at(b + 1) - doc_at(b);
     const int nst = (L + KT - 1) / KT;
+    // The row's softmax state starts from its path partial (the keys of its own
+    // ancestors and itself): acc = their unnormalised value sum, m = their maximum
+    // score (base 2), and lsum = their weight sum, held by one lane of the row's two.
+    // The document's keys then extend the same online softmax, and the end of the
+    // document only normalises.  The partial is loaded at the document's first stage,
+    // before that stage's buffer-to-LDS loads are issued, so its first use waits for
+    // these loads alone while the stage's QK products run.
     f32x16 acc[NBLK];
+    float m = 0.f, lsum = 0.f;  // base-2 running max; this lane's share of the sum
+    auto seed = [&]() __attribute__((always_inline)) {
+      const float* ao = anc_o + ((size_t)r * Hq + h) * HD + 4 * c;
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i)
+      for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
-    float m = -INFINITY, lsum = 0.f;  // base-2 running max; this lane's share of the sum
-    // one stage; Par = kc & 1 picks the slot it reads and the slot it refills
-    auto stage = [&](auto Par, int t) __attribute__((always_inline)) {
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const float4 v = *reinterpret_cast<const float4*>(ao + blk * 32 + 8 * e4);
+          acc[blk][4 * e4 + 0] = v.x;
+          acc[blk][4 * e4 + 1] = v.y;
+          acc[blk][4 * e4 + 2] = v.z;
+          acc[blk][4 * e4 + 3] = v.w;
+        }
+      const float2 a = anc_ml[(size_t)r * Hq + h];
+      m = a.x * LOG2E;
+      lsum = c == 0 ? a.y : 0.f;
+    };
+    // (an empty document's row is its path partial alone)
+    if (nst == 0) seed();
+    // one stage; Par = kc & 1 picks the slot it reads and the slot it refills, and
+    // First (the document's first stage) loads the path partial; both are compile-time
+    // so the loads and the slots need no branch
+    auto stage = [&](auto Par, auto First, int t) __attribute__((always_inline)) {
       constexpr int P = decltype(Par)::value;
       uint8_t* const cur = P ? slot1 : slot0;
       uint8_t* const nxt = P ? slot0 : slot1;
       wait_vmcnt<0>();       // this wave's part of stage kc has landed
       wait_lgkmcnt0();       // and its reads of stage kc - 1 are done
       __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(First)::value) seed();
       __builtin_amdgcn_sched_barrier(0);
       issue(pb, pt, nxt);    // stage kc + 1 into the slot stage kc - 1 used
       if (pb < b_hi) advance();
@@ -1262,71 +1306,67 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sc[kb][e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk;  // finite: every stage has a valid key
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk;
       lazy_rescale(m, tmax, lsum, acc);
+      // weights of block 0; then block 0's PV products, each pair of matrix ops
+      // followed by one pair of block 1's weights (the matrix cores and the vector
+      // ALU work at once); then block 1's products
+      uint32_t w0h[2][4], w0l[2][4], w1h[2][4], w1l[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], qk, -m));
-          lsum += p[e];
-        }
-        bf16x8 ph[2], pl[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          uint32_t wh[4], wl[4];
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            const float a = p[8 * st + 2 * q2], a2 = p[8 * st + 2 * q2 + 1];
-            wh[q2] = pack_bf16(a, a2);
-            wl[q2] = pack_bf16(a - __uint_as_float(wh[q2] << 16), a2 - __uint_as_float(wh[q2] & 0xFFFF0000u));
-          }
-          uint4 uh{wh[0], wh[1], wh[2], wh[3]}, ul{wl[0], wl[1], wl[2], wl[3]};
-          ph[st] = *reinterpret_cast<bf16x8*>(&uh);
-          pl[st] = *reinterpret_cast<bf16x8*>(&ul);
-        }
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const bf16x8 vf = lds_read_tr_x2(sl + kb * 32 * ROW + vof[st][0][blk],
-                                             sl + kb * 32 * ROW + vof[st][1][blk]);
-            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[st], acc[blk], 0, 0, 0);
-            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[st], acc[blk], 0, 0, 0);
-          }
-      }
-    };
-    for (int t = 0; t < nst; ++t, ++kc) {
-      if (kc & 1) stage(std::integral_constant<int, 1>{}, t);
-      else stage(std::integral_constant<int, 0>{}, t);
-    }
-    // merge with the row's path partial; lane writes hd blk*32 + 8 e4 + 4 c + 0..3
-    lsum += __shfl_xor(lsum, 32, 64);
-    if (row_ok) {
-      const float* ao = anc_o + ((size_t)r * Hq + h) * HD + 4 * c;
-      float4 av[NBLK][4];
+      for (int q = 0; q < 8; ++q) weight_pair(sc[0], m, lsum, q, w0h, w0l);
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) av[blk][e4] = *reinterpret_cast<const float4*>(ao + blk * 32 + 8 * e4);
-      const float2 a = anc_ml[(size_t)r * Hq + h];
-      const float ma = a.x * LOG2E;
-      const float Mt = fmaxf(m, ma);
-      const float fd = m == -INFINITY ? 0.f : exp2f(m - Mt);
-      const float fa = exp2f(ma - Mt);
-      const float inv = 1.0f / (lsum * fd + a.y * fa);
-      const float sd = fd * inv, sa = fa * inv;
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 vf = lds_read_tr_x2(sl + vof[st][0][blk], sl + vof[st][1][blk]);
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, frags(w0h, st), acc[blk], 0, 0, 0);
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, frags(w0l, st), acc[blk], 0, 0, 0);
+          weight_pair(sc[1], m, lsum, 2 * blk + st, w1h, w1l);
+        }
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 vf = lds_read_tr_x2(sl + 32 * ROW + vof[st][0][blk], sl + 32 * ROW + vof[st][1][blk]);
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, frags(w1h, st), acc[blk], 0, 0, 0);
+          acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, frags(w1l, st), acc[blk], 0, 0, 0);
+        }
+      // the schedule of that block (after lazy_rescale's branch): block 0's weights
+      // (12 vector instructions per pair of keys), then per V^T fragment two DS reads,
+      // a matrix op, six vector instructions, a matrix op, six more
+      __builtin_amdgcn_sched_group_barrier(0x002, 96, 0);  // VALU: block 0's weights
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (V^T)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+    };
+    using Odd = std::integral_constant<int, 1>;
+    using Even = std::integral_constant<int, 0>;
+    if (nst > 0) {
+      if (kc & 1) stage(Odd{}, std::true_type{}, 0);
+      else stage(Even{}, std::true_type{}, 0);
+      ++kc;
+    }
+    for (int t = 1; t < nst; ++t, ++kc) {
+      if (kc & 1) stage(Odd{}, std::false_type{}, t);
+      else stage(Even{}, std::false_type{}, t);
+    }
+    // normalise; lane writes hd blk*32 + 8 e4 + 4 c + 0..3
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (row_ok) {
+      const float inv = 1.0f / lsum;
       uint16_t* op = O + (((size_t)b * n_int + r) * Hq + h) * HD + 4 * c;
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const float4 an = av[blk][e4];
+        for (int e4 = 0; e4 < 4; ++e4)
           *reinterpret_cast<uint2*>(op + blk * 32 + 8 * e4) =
-              uint2{pack_bf16(acc[blk][4 * e4] * sd + an.x * sa, acc[blk][4 * e4 + 1] * sd + an.y * sa),
-                    pack_bf16(acc[blk][4 * e4 + 2] * sd + an.z * sa, acc[blk][4 * e4 + 3] * sd + an.w * sa)};
-        }
+              uint2{pack_bf16(acc[blk][4 * e4] * inv, acc[blk][4 * e4 + 1] * inv),
+                    pack_bf16(acc[blk][4 * e4 + 2] * inv, acc[blk][4 * e4 + 3] * inv)};
     }
   }
   wait_vmcnt<0>();  // nothing may still target LDS at exit
