@@ -253,7 +253,8 @@ int tcs_tree_attn_noalloc(tcs_stream stream, tcs_dtype dtype, int32_t B, int32_t
  *   lse         [R] fp32 out;  lp [B, n_nodes] fp32 out
  *   ws          workspace of tcs_lmhead_workspace_bytes(h_dtype, w_dtype, B, n_int, n_nodes,
  *               d, V) bytes (0 for invalid sizes or dtype pairs)
- * bf16 heads need d % 64 == 0.  Errors: TCS_EUNSUPPORTED (dtype pair, d), TCS_EINVAL (sizes,
+ * bf16 heads need d % 64 == 0, the W8A8 head d % 128 == 0.  Errors: TCS_EUNSUPPORTED (dtype
+ * pair, d), TCS_EINVAL (sizes,
  * null pointers, w_scale missing for an fp8 head), TCS_ECAPACITY (short workspace).
  */
 size_t tcs_lmhead_workspace_bytes(tcs_dtype h_dtype, tcs_dtype w_dtype, int32_t B, int32_t n_int,
@@ -295,8 +296,8 @@ int tcs_path_sum_softmax(tcs_stream stream, int32_t B, const tcs_trie_dev* trie,
 typedef struct {
   tcs_dtype dtype;       /* TCS_F32 or TCS_BF16: E, Wq, Wk, Wv, Wo and activations */
   tcs_dtype head_dtype;  /* dtype, or for bf16 models TCS_FP8_E4M3 (W8A16) or TCS_FP8_E4M3_A8
-                            (W8A8: tcs_classify / tcs_classify_run only; tcs_letters_run and
-                            tcs_decode_run answer TCS_EUNSUPPORTED) */
+                            (W8A8, d % 128 == 0: tcs_classify / tcs_classify_run only;
+                            tcs_letters_run and tcs_decode_run answer TCS_EUNSUPPORTED) */
   int32_t d, Hq, Hkv, hd, V;
   float eps;
   const void* E;         /* [V, d] token embeddings */

@@ -145,6 +145,11 @@ def test_lmhead_workspace_query_by_dtype_pair():
     assert lib.tcs_lmhead_workspace_bytes(tcs.TCS_F32, tcs.TCS_FP8_E4M3_A8, B, n_int, n_nodes, d, V) == 0
     assert lib.tcs_lmhead_lse_gather(None, tcs.TCS_F32, tcs.TCS_FP8_E4M3_A8, 1, 1, 2, 64, 10,
                                      *([None] * 9), 0) == tcs.TCS_EUNSUPPORTED
+    # the W8A8 head steps over 128 codes of d at a time: d = 192 is refused before any
+    # pointer is touched
+    assert lib.tcs_lmhead_lse_gather(None, tcs.TCS_BF16, tcs.TCS_FP8_E4M3_A8, 1, 1, 2, 192, 10,
+                                     *([None] * 9), 0) == tcs.TCS_EUNSUPPORTED
+    assert b"128" in lib.tcs_last_error()
 
 
 def test_tree_attn_noalloc_refuses_oversize_without_gpu():

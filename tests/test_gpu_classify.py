@@ -45,7 +45,7 @@ SMALL = {
     "fp8-small": config(5, V=2500, d=192, Hq=4, Hkv=1, B=4, L=300),
     # W8A8 head: hidden rows quantized to E4M3 per row; the second case has 320
     # rows, a full and a ragged row tile
-    "fp8a8-small": config(5, V=2500, d=192, Hq=4, Hkv=1, B=4, L=300, head="fp8a8"),
+    "fp8a8-small": config(5, V=2500, d=384, Hq=4, Hkv=1, B=4, L=300, head="fp8a8"),
     "fp8a8-rows": config(5, V=3000, d=256, Hq=4, Hkv=1, B=40, L=50, head="fp8a8"),
     # one label (probability 1, always chosen); a 40-token chain beside short labels
     "single-label-bf16": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=64, B=3, L=20,

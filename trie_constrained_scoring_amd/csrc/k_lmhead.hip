@@ -103,6 +103,11 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
 // the fp32 logits in the epilogue.  The k order inside a pair of k-steps is
 // permuted the same way on both operands (lane half c supplies k 32m + 16c + 8s +
 // 0..7 in step 2m+s), which leaves the dot products unchanged.
+//
+// With fp8 hidden states too (W8A8) both operands are E4M3 codes in 128-byte slot
+// rows, 128 codes per k-step (the bf16 slot layout), and each 32x32 block takes two
+// fp8 matrix ops per step: the steps, and so the barriers, are half as many as with
+// 64-code steps, and each DMA stream has as much time to land as in the bf16 head.
 
 // The ring kernel runs 8 waves (two per SIMD); each owns 128 vocabulary entries x
 // 64 rows of the 256 x 256 tile and loads 1/8 of every operand k-tile.
@@ -285,7 +290,9 @@ __device__ __forceinline__ void ring_body(
   const int all_rounds = GEMM ? (n_rt * n_vt + HEAD_WGS - 1) / HEAD_WGS : head_grid(n_rt, n_vt) / HEAD_WGS;
   const int rounds = min(all_rounds, w_lo + rounds_per_wg);
   const int bslot = int(blockIdx.x) % HEAD_WGS;
-  const int nk = d / DMA_BK;
+  // k-step: 64 elements (128-byte bf16 rows, 64-byte fp8 W rows), or 128 fp8
+  // elements (128-byte rows) when both operands are fp8
+  const int nk = A8 ? d / (2 * DMA_BK) : d / DMA_BK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wr = wave >> 1;  // vocabulary half, row quarter
@@ -319,37 +326,31 @@ __device__ __forceinline__ void ring_body(
     return Span{W, hbytes, 0, 0};
   };
 
-  // Load j (0..3) of this wave fills slot rows wave*32 + 8j .. +7 (1 KB): lane i
-  // writes row i/8, position i%8, which holds global chunk (i%8) ^ swz(row % 16);
-  // row % 16 = 8*(j&1) + i/8.  The k offset goes in the scalar offset.
+  // 128-byte slot rows (bf16 operands; both fp8 operands with A8).  Load j (0..3)
+  // of this wave fills slot rows wave*32 + 8j .. +7 (1 KB): lane i writes row i/8,
+  // position i%8, which holds global chunk (i%8) ^ swz(row % 16); row % 16 =
+  // 8*(j&1) + i/8.  The k offset goes in the scalar offset.
   const int lr = lane >> 3, lp = lane & 7;
   int vo[RING_LOADS];
 #pragma unroll
   for (int j = 0; j < RING_LOADS; ++j)
-    vo[j] = ((wave * 32 + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
-  // bf16 h k-tile (TR rows): the wave's TR/64 loads fill rows wave*TR/8 + 8j + i/8
+    vo[j] = (wave * 32 + j * 8 + lr) * (d * WRB) + (lp ^ dma_swz(lr + 8 * (j & 1))) * 16;
+  // h k-tile (TR rows): the wave's TR/64 loads fill rows wave*TR/8 + 8j + i/8
   int voh[TR / 64];
 #pragma unroll
   for (int j = 0; j < TR / 64; ++j)
-    voh[j] = ((wave * (TR / 8) + j * 8 + lr) * d + (lp ^ dma_swz(lr + 8 * (j & 1))) * 8) * 2;
-  // fp8 W: load j (0..1) fills rows wave*32 + 16j + i/4, position i%4, which holds
-  // chunk (i%4) ^ dma8_swz(row % 16)
+    voh[j] = (wave * (TR / 8) + j * 8 + lr) * (d * HRB) + (lp ^ dma_swz(lr + 8 * (j & 1))) * 16;
+  // fp8 W with bf16 h: load j (0..1) fills rows wave*32 + 16j + i/4, position i%4,
+  // which holds chunk (i%4) ^ dma8_swz(row % 16)
+  constexpr bool W8H16 = W8 && !A8;
   int vo8[RING_LOADS8];
 #pragma unroll
   for (int j = 0; j < RING_LOADS8; ++j) {
     const int row = wave * 32 + j * 16 + (lane >> 2);
     vo8[j] = row * d + (((lane & 3) ^ dma8_swz(row & 15)) << 4);
   }
-  constexpr int W_LOADS = W8 ? RING_LOADS8 : RING_LOADS;
-  constexpr int H_LOADS = A8 ? TR / 128 : TR / 64;
-  // A8 h k-tile (TR rows x 64 bytes): load j of a wave fills rows wave*TR/8 + 16j ..
-  // +15, lane i writing 16 bytes at row i/4, position i%4 (chunk (i%4) ^ dma8_swz(row % 16))
-  int vo8h[TR / 128];
-#pragma unroll
-  for (int j = 0; j < TR / 128; ++j) {
-    const int row = wave * (TR / 8) + 16 * j + (lane >> 2);
-    vo8h[j] = row * d + (((lane & 3) ^ dma8_swz(row & 15)) << 4);
-  }
+  constexpr int W_LOADS = W8H16 ? RING_LOADS8 : RING_LOADS;
+  constexpr int H_LOADS = TR / 64;
   int w = next_valid(w_lo);
   if (w >= rounds) return;
   // A tile runs nk5 = nk rounded up to a multiple of 5 steps, so every tile starts
@@ -372,7 +373,7 @@ __device__ __forceinline__ void ring_body(
     const bool pad = k >= nk;
     const uint8_t* b = s0.wb + (nxt ? dwb : 0);
     const int n = s0.wn + (nxt ? dwn : 0);
-    if constexpr (W8)
+    if constexpr (W8H16)
       head_issue8(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl, wave, vo8);
     else
       head_issue<RING_LOADS>(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl,
@@ -384,18 +385,8 @@ __device__ __forceinline__ void ring_body(
     const bool pad = k >= nk;
     const uint8_t* b = s0.hb + (nxt ? dhb : 0);
     const int n = s0.hn + (nxt ? dhn : 0);
-    if constexpr (A8) {
-      const void* base = pad ? static_cast<const void*>(zero) : static_cast<const void*>(b);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, pad ? zbytes : n, 0x00020000);
-#pragma unroll
-      for (int j = 0; j < TR / 128; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, TCS_LDS(sl + (wave * (TR / 8) + 16 * j) * 64), 16,
-                                                 vo8h[j], (pad ? 0 : k) * DMA_BK, 0, 0);
-    }
-    else
-      head_issue<TR / 64>(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl,
-                           wave * (TR / 8), voh);
+    head_issue<TR / 64>(pad ? static_cast<const void*>(zero) : b, pad ? zbytes : n, pad ? 0 : k, sl,
+                        wave * (TR / 8), voh);
   };
 
   // h fragment of k-step ks: row base + lane%32, chunk 2 ks + lane/32 (bf16 W) or
@@ -509,62 +500,79 @@ __device__ __forceinline__ void ring_body(
     if constexpr (!LAST) interleave_ds();
   };
 
-  // fp8 x fp8 (A8): one v_mfma_scale_f32_32x32x64_f8f6f4 per 32x32 block and k-step.
-  // Lane l supplies k 32 (l/32) .. +31 of its row on both operands (16-byte chunks
-  // 2 (l/32) and 2 (l/32) + 1 of the 64-byte slot row); any k order shared by the
-  // two operands gives the same dot products.
-  int fq[2];
+  // fp8 x fp8 (A8): a k-step is 128 codes (one 128-byte slot row per operand row),
+  // two v_mfma_scale_f32_32x32x64_f8f6f4 per 32x32 block: in half s lane l supplies
+  // k 64 s + 32 (l/32) .. +31 of its row on both operands (16-byte chunks
+  // 4 s + 2 (l/32) and + 1); any k order shared by the two operands gives the same
+  // dot products.
+  int fq[2][2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) fq[t] = (lane & 31) * 64 + (((2 * (lane >> 5) + t) ^ dma8_swz(lane & 15)) << 4);
-  v8i_t wf[4], hf[JN];  // W fragments (vocabulary blocks) and the h fragments of this step
-  auto frag8 = [&](const uint8_t* base) __attribute__((always_inline)) {
-    const uint4 x = *reinterpret_cast<const uint4*>(base + fq[0]);
-    const uint4 y = *reinterpret_cast<const uint4*>(base + fq[1]);
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      fq[hs][t] = (lane & 31) * 128 + (((4 * hs + 2 * (lane >> 5) + t) ^ dma_swz(lane & 15)) << 4);
+  // W fragments (vocabulary blocks) of the current half; h fragments of both halves
+  v8i_t wf[4], hf0[JN], hf1[JN];
+  auto frag8 = [&](const uint8_t* base, int hs) __attribute__((always_inline)) {
+    const uint4 x = *reinterpret_cast<const uint4*>(base + fq[hs][0]);
+    const uint4 y = *reinterpret_cast<const uint4*>(base + fq[hs][1]);
     return v8i_t{int(x.x), int(x.y), int(x.z), int(x.w), int(y.x), int(y.y), int(y.z), int(y.w)};
   };
-  auto mfma8 = [&](int i) __attribute__((always_inline)) {
+  auto mfma8 = [&](int i, const v8i_t (&hf)[JN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < JN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], hf[j], acc[i][j], 0, 0, 0, 127,
                                                                  0, 127);
   };
-  // one k-step g: W(g) blocks 2-3 are read while blocks 0-1 are multiplied (their
-  // fragments and h(g)'s were read in the previous step); after the barrier the
-  // next step's W blocks 0-1 are read while blocks 2-3 are multiplied, then h(g+1).
-  auto step8 = [&](auto Uc, int kt, auto Lc) __attribute__((always_inline)) {
+  auto wfrag = [&](const uint8_t* sl, int i, int hs) __attribute__((always_inline)) {
+    wf[i] = frag8(sl + (wm * 128 + 32 * i) * 128, hs);
+  };
+  auto hfrag = [&](const uint8_t* sl, v8i_t (&hf)[JN], int hs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < JN; ++j) hf[j] = frag8(sl + (wr * 32 * JN + 32 * j) * 128, hs);
+  };
+  // one k-step g (fragments of W blocks 0-1 and h of half 0 were read in the
+  // previous step).  Each group of fragment reads is followed by four matrix ops
+  // that do not need it: half 0 reads W blocks 2-3, multiplies blocks 0-1, reads
+  // half 1's W blocks 0-1 and h, multiplies blocks 2-3; half 1 does the same around
+  // the step's barrier, reading the next step's half-0 fragments after it.
+  auto step8 = [&](auto Uc, int kt) __attribute__((always_inline)) {
     constexpr int U = decltype(Uc)::value;
-    constexpr bool LAST = decltype(Lc)::value;
-    constexpr int sA = (2 * U) % 5;
+    constexpr int sA = (2 * U) % 5, sB = (2 * U + 1) % 5;
     constexpr int sB1 = (2 * U + 3) % 5, sA1 = (2 * U + 2) % 5, sA2 = (2 * U + 4) % 5;
     issue_h(kt + 1, slot[sB1]);  // h(g+1)
     issue_w(kt + 2, slot[sA2]);  // W(g+2)
-    wf[2] = frag8(slot[sA] + (wm * 128 + 64) * 64);
-    wf[3] = frag8(slot[sA] + (wm * 128 + 96) * 64);
-    mfma8(0);
-    mfma8(1);
+    wfrag(slot[sA], 2, 0);
+    wfrag(slot[sA], 3, 0);
+    mfma8(0, hf0);
+    mfma8(1, hf0);
+    __builtin_amdgcn_sched_barrier(0);
+    wfrag(slot[sA], 0, 1);
+    wfrag(slot[sA], 1, 1);
+    hfrag(slot[sB], hf1, 1);
+    mfma8(2, hf0);
+    mfma8(3, hf0);
+    __builtin_amdgcn_sched_barrier(0);
+    wfrag(slot[sA], 2, 1);
+    wfrag(slot[sA], 3, 1);
+    mfma8(0, hf1);
+    mfma8(1, hf1);
     wait_vmcnt<W_LOADS>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!LAST) {
-      wf[0] = frag8(slot[sA1] + (wm * 128 + 0) * 64);
-      wf[1] = frag8(slot[sA1] + (wm * 128 + 32) * 64);
-    }
-    mfma8(2);
-    mfma8(3);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!LAST) {  // after blocks 2-3 issued
-#pragma unroll
-      for (int j = 0; j < JN; ++j) hf[j] = frag8(slot[sB1] + (wr * 32 * JN + 32 * j) * 64);
-    }
+    wfrag(slot[sA1], 0, 0);
+    wfrag(slot[sA1], 1, 0);
+    hfrag(slot[sB1], hf0, 0);
+    mfma8(2, hf1);
+    mfma8(3, hf1);
     __builtin_amdgcn_sched_barrier(0);
   };
   // fragments of a tile's first step: W(0) blocks 0-1 in slot 0, h(0) in slot 1
   auto first_frags8 = [&]() __attribute__((always_inline)) {
-    wf[0] = frag8(slot[0] + (wm * 128) * 64);
-    wf[1] = frag8(slot[0] + (wm * 128 + 32) * 64);
-#pragma unroll
-    for (int j = 0; j < JN; ++j) hf[j] = frag8(slot[1] + (wr * 32 * JN + 32 * j) * 64);
+    wfrag(slot[0], 0, 0);
+    wfrag(slot[0], 1, 0);
+    hfrag(slot[1], hf0, 0);
   };
 
   // prologue: W(0), h(0), W(1)
@@ -588,19 +596,18 @@ __device__ __forceinline__ void ring_body(
     using F = std::false_type;
     int kt = 0;
     if constexpr (A8) {
+      // The whole tile is one branch-free loop: its final step already reads the
+      // next tile's first fragments (slots 0 and 1), which stay live across the
+      // epilogue.  A straight-line final group of steps would let the compiler move
+      // its matrix ops past the step barriers.
 #pragma unroll 1
-      for (; kt + 5 < nk5; kt += 5) {
-        step8(std::integral_constant<int, 0>{}, kt, F{});
-        step8(std::integral_constant<int, 1>{}, kt + 1, F{});
-        step8(std::integral_constant<int, 2>{}, kt + 2, F{});
-        step8(std::integral_constant<int, 3>{}, kt + 3, F{});
-        step8(std::integral_constant<int, 4>{}, kt + 4, F{});
+      for (; kt < nk5; kt += 5) {
+        step8(std::integral_constant<int, 0>{}, kt);
+        step8(std::integral_constant<int, 1>{}, kt + 1);
+        step8(std::integral_constant<int, 2>{}, kt + 2);
+        step8(std::integral_constant<int, 3>{}, kt + 3);
+        step8(std::integral_constant<int, 4>{}, kt + 4);
       }
-      step8(std::integral_constant<int, 0>{}, kt, F{});
-      step8(std::integral_constant<int, 1>{}, kt + 1, F{});
-      step8(std::integral_constant<int, 2>{}, kt + 2, F{});
-      step8(std::integral_constant<int, 3>{}, kt + 3, F{});
-      step8(std::integral_constant<int, 4>{}, kt + 4, std::true_type{});
     } else {
       for (; kt + 5 < nk5; kt += 5) {
         step(std::integral_constant<int, 0>{}, kt, F{});
@@ -653,8 +660,7 @@ __device__ __forceinline__ void ring_body(
     if constexpr (A8) {  // each hidden row's own activation scale
 #pragma unroll
       for (int jn = 0; jn < JN; ++jn) {
-        const int r = r0 + rloc + 32 * jn;
-        const float hs = r < R ? h_scale[r] : 0.f;
+        const float hs = h_scale[min(r0 + rloc + 32 * jn, R - 1)];
 #pragma unroll
         for (int im = 0; im < 4; ++im)
 #pragma unroll
@@ -694,12 +700,9 @@ __device__ __forceinline__ void ring_body(
       if (lane < 32 && r < R) part[pi] = ms[jn];
     }
     }
-    // the next tile's W(0) and h(0) are in slots 0 and 1 (landed at the last barrier)
-    if constexpr (A8) {
-      __builtin_amdgcn_sched_barrier(0);  // the epilogue's registers are free first
-      first_frags8();
-    }
-    else read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
+    // the next tile's W(0) and h(0) are in slots 0 and 1 (landed at the last
+    // barrier; the fp8 x fp8 loop has read its fragments already)
+    if constexpr (!A8) read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
     w = w1;
     w1 = next_valid(w1 + 1);
     s0 = s1;
@@ -889,7 +892,8 @@ int lmhead_n_tiles(tcs_dtype /*h_dtype*/, int32_t V) { return (V + HEAD_BN - 1) 
 static int head_rounds_per_wg(int /*rounds*/) { return 8; }
 
 // 256 x d zeros for the padding steps of the bf16 head when d / 64 is not a
-// multiple of 5 (else none).
+// multiple of 5 (else none).  The W8A8 head's steps are 128 codes: when d / 128
+// is not a multiple of 5, d / 64 = 2 d / 128 is not either, so the zeros exist.
 static size_t head_zero_bytes(int32_t d) {
   const int nk = d / DMA_BK;
   return nk % 5 == 0 ? 0 : size_t(256) * d * 2;
@@ -1068,6 +1072,7 @@ int launch_lmhead_run(void* stream, tcs_dtype h_dtype, tcs_dtype w_dtype, int32_
     auto zp = reinterpret_cast<const uint16_t*>(P.zero);
     if (w_dtype == TCS_FP8_E4M3_A8) {
       if (!act8) return fail(TCS_EINVAL, "lmhead: W8A8 head without its activation buffer");
+      if (d % 128 != 0) return fail(TCS_EUNSUPPORTED, "lmhead: W8A8 head needs d %% 128 == 0 (d=%d)", d);
       auto codes = static_cast<uint32_t*>(act8);
       auto hs = reinterpret_cast<float*>(static_cast<char*>(act8) + align_up(size_t(R) * d));
       quant_rows_e4m3_kernel<<<(R + 3) / 4, 256, 0, s>>>(R, d, hp, codes, hs);

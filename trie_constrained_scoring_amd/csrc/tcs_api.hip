@@ -149,6 +149,8 @@ int tcs_lmhead_lse_gather(tcs_stream stream, tcs_dtype h_dtype, tcs_dtype w_dtyp
     return fail(TCS_EINVAL, "lmhead: B=%d n_int=%d n_nodes=%d d=%d V=%d", B, n_int, n_nodes, d, V);
   if (h_dtype == TCS_BF16 && d % 64 != 0)
     return fail(TCS_EUNSUPPORTED, "lmhead: bf16 head needs d %% 64 == 0 (d=%d)", d);
+  if (w_dtype == TCS_FP8_E4M3_A8 && d % 128 != 0)
+    return fail(TCS_EUNSUPPORTED, "lmhead: W8A8 head needs d %% 128 == 0 (d=%d)", d);
   if (B == 0) return TCS_OK;
   const bool fp8_w = w_dtype == TCS_FP8_E4M3 || w_dtype == TCS_FP8_E4M3_A8;
   if (!h || !W || !e_tok || !e_qrow || !e_child || !lse || !lp || (fp8_w && !w_scale))
@@ -249,6 +251,8 @@ static int check_classify(const tcs_model* m, const tcs_trie_dev* t, const tcs_d
   if (m->d < 1 || m->V < 1) return fail(TCS_EINVAL, "classify: d=%d V=%d", m->d, m->V);
   if (m->dtype == TCS_BF16 && m->d % 64 != 0)
     return fail(TCS_EUNSUPPORTED, "classify: bf16 model needs d %% 64 == 0 (d=%d)", m->d);
+  if (m->head_dtype == TCS_FP8_E4M3_A8 && m->d % 128 != 0)
+    return fail(TCS_EUNSUPPORTED, "classify: W8A8 head needs d %% 128 == 0 (d=%d)", m->d);
   if (!m->E || !m->Wq || !m->Wk || !m->Wv || !m->Wo || !m->W ||
       ((m->head_dtype == TCS_FP8_E4M3 || m->head_dtype == TCS_FP8_E4M3_A8) && !m->W_scale))
     return fail(TCS_EINVAL, "classify: null weight pointer");
