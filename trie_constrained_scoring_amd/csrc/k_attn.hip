@@ -1278,16 +1278,23 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
       if (pb < b_hi) advance();
       const uint8_t* sl = cur;
       f32x16 sc[2];
+      // the matrix ops of this stage's scores run at raised wave priority, so the
+      // SIMD's other wave (another workgroup, in its vector phase) yields to them
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+      // the two key blocks' products alternate, so consecutive matrix ops do not
+      // depend on each other
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
+      for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + kb * 32 * ROW + ko[ks]);
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
         }
-      }
+      __builtin_amdgcn_s_setprio(0);
       // online softmax (base 2) over the 64 keys; only a document's last stage has
       // keys past its end, which are masked (the empty asm keeps this a branch
       // rather than selects on every stage)
@@ -1314,6 +1321,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
       uint32_t w0h[2][4], w0l[2][4], w1h[2][4], w1l[2][4];
 #pragma unroll
       for (int q = 0; q < 8; ++q) weight_pair(sc[0], m, lsum, q, w0h, w0l);
+      __builtin_amdgcn_s_setprio(1);  // the PV matrix ops, as the scores'
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
@@ -1331,6 +1339,7 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
           acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, frags(w1h, st), acc[blk], 0, 0, 0);
           acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, frags(w1l, st), acc[blk], 0, 0, 0);
         }
+      __builtin_amdgcn_s_setprio(0);
       // the schedule of that block (after lazy_rescale's branch): block 0's weights
       // (12 vector instructions per pair of keys), then per V^T fragment two DS reads,
       // a matrix op, six vector instructions, a matrix op, six more
