@@ -596,10 +596,10 @@ __device__ __forceinline__ void ring_body(
     using F = std::false_type;
     int kt = 0;
     if constexpr (A8) {
-      // The whole tile is one branch-free loop: its final step already reads the
-      // next tile's first fragments (slots 0 and 1), which stay live across the
-      // epilogue.  A straight-line final group of steps would let the compiler move
-      // its matrix ops past the step barriers.
+      // The whole tile is one branch-free loop (its final step also reads the next
+      // tile's first fragments, which are read again after the epilogue).  A
+      // straight-line final group of steps would let the compiler move its matrix
+      // ops past the step barriers.
 #pragma unroll 1
       for (; kt < nk5; kt += 5) {
         step8(std::integral_constant<int, 0>{}, kt);
@@ -701,8 +701,11 @@ __device__ __forceinline__ void ring_body(
     }
     }
     // the next tile's W(0) and h(0) are in slots 0 and 1 (landed at the last
-    // barrier; the fp8 x fp8 loop has read its fragments already)
-    if constexpr (!A8) read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
+    // barrier, and no load targets those slots until its first step).  The fp8 x fp8
+    // loop's final step read them too, but those values are not kept across the
+    // epilogue: reading them again here leaves the epilogue 32 more registers.
+    if constexpr (A8) first_frags8();
+    else read_frags(slot[0], slot[1], 0, fa[0], fb[0]);
     w = w1;
     w1 = next_valid(w1 + 1);
     s0 = s1;
