@@ -377,13 +377,20 @@ def cpu_baseline(S, budget_s=15.0):
     O.classify(inp, docs=[0], model=model, trie=trie)
     one = time.perf_counter() - t0
     n = int(max(1, min(S["docs"].B, budget_s // max(one, 1e-3))))
+    # a whole batch that takes well under the budget is scored again, so that the
+    # timed sample is ~10 s or more of CPU work
+    reps = 0
     t0 = time.perf_counter()
-    O.classify(inp, docs=list(range(n)), model=model, trie=trie)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "docs/s", "cores": cores, "cpu_model": cpu_model(),
+    while True:
+        O.classify(inp, docs=list(range(n)), model=model, trie=trie)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if n < S["docs"].B or dt >= 0.6 * budget_s:
+            break
+    return {"value": n * reps / dt, "unit": "docs/s", "cores": cores, "cpu_model": cpu_model(),
             "kind": "oracle",
-            "sample": f"{n} of {S['docs'].B} documents of the same batch, every label, fp64 numpy "
-                      f"(BLAS threads = visible cores), {dt:.1f}s"}
+            "sample": f"{n} of {S['docs'].B} documents of the same batch x {reps} passes, every label, "
+                      f"fp64 numpy (BLAS threads = visible cores), {dt:.1f}s"}
 
 
 def path_stress(cid: int = 4, B: int = 4096, reps: int = 10):
