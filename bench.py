@@ -287,6 +287,37 @@ def doc_attn_roofline(S, ms):
             "ms_per_launch": round(ms, 4)}
 
 
+def classify_roofline(S, step_ms):
+    """Roofline of the whole classify step: the sum over its kernels of each one's
+    bound, max(algorithmic FLOP / matrix-core peak, algorithmic bytes / HBM peak),
+    against the measured time per batch.  Kernels: document attention, output
+    projection (+ residual), RMSNorm, output head (bf16 matrix cores for bf16 and
+    fp8 weights, fp8 ones for W8A8, after the rows' quantization), log-sum-exp merge
+    of its partials, path sums."""
+    cfg, td = S["cfg"], S["td"]
+    B, n_int, N, M = S["docs"].B, td.trie.n_int, td.trie.n_nodes, td.trie.n_labels
+    R, qd, d, V = B * n_int, cfg.Hq * cfg.hd, cfg.d, cfg.V
+    hbm = PEAK_HBM_GBS * 1e9
+    def bound_us(flops, nbytes, peak_tflops=PEAK_BF16_TFLOPS):
+        return max(flops / (peak_tflops * 1e12), nbytes / hbm) * 1e6
+    wbytes = 1 if cfg.head in ("fp8", "fp8a8") else 2
+    parts = {
+        "doc_attn": bound_us(doc_attn_flops(S), doc_attn_bytes(S)),
+        "o_proj": bound_us(2.0 * R * qd * d, R * qd * 2 + d * qd * 2 + R * d * 4),
+        "rownorm": bound_us(0, R * d * 4 + R * d * 2),
+        "head": bound_us(2.0 * R * d * V, V * d * wbytes + R * d * 2,
+                         PEAK_FP8_TFLOPS if cfg.head == "fp8a8" else PEAK_BF16_TFLOPS),
+        "lse_merge": bound_us(0, R * 2 * ((V + 255) // 256) * 8 + R * 4),
+        "path_sums": bound_us(0, B * (4 * N + 8 * M)),
+    }
+    if cfg.head == "fp8a8":  # the hidden rows' E4M3 quantization before the head
+        parts["quant_rows"] = bound_us(0, R * d * 2 + R * d + R * 4)
+    total = sum(parts.values())
+    return {"bound_ms": round(total / 1e3, 4), "ms_per_step": round(step_ms, 4),
+            "frac": round(total / 1e3 / step_ms, 4),
+            "parts_us": {k: round(v, 2) for k, v in parts.items()}}
+
+
 def letters_measure(S, steps, warmup, streams):
     """The same documents and weights under the letters method (tcs_letters_run): one
     answer position per document and the M letter rows of the head; the document
@@ -613,6 +644,7 @@ def main():
     res["head_share_of_step"] = round(kern["head"] / (sec * 1e3), 4)
     if kern["doc_attn"]:
         res["doc_attn_roofline"] = doc_attn_roofline(S, kern["doc_attn"])
+    res["classify_roofline"] = classify_roofline(S, sec * 1e3)
     decision, letters, decode = {}, {}, {}
     if not args.no_decision_word:
         decision[cfg.name] = decision_word(S, args.steps, args.warmup, args.streams)
@@ -638,6 +670,7 @@ def main():
         if k2["doc_attn"]:
             e["doc_attn_ms"] = round(k2["doc_attn"], 4)
             e["doc_attn_roofline"] = doc_attn_roofline(S2, k2["doc_attn"])
+        e["classify_roofline"] = classify_roofline(S2, s2 * 1e3)
         extra[str(S2["trie"].n_labels)] = e
         if not args.no_decision_word:
             decision[S2["cfg"].name] = decision_word(S2, few, 2, args.streams)
@@ -679,6 +712,7 @@ def main():
             "head_share_of_step": round(kl["head"] / (sl * 1e3), 4)}
         if kl["doc_attn"]:
             res["long_document"]["doc_attn_roofline"] = doc_attn_roofline(S, kl["doc_attn"])
+        res["long_document"]["classify_roofline"] = classify_roofline(S, sl * 1e3)
     if not args.no_w8a8 and cfg.head != "fp8a8":
         # the long-document workload with its hidden rows quantized to E4M3 before
         # the head (fp8 x fp8 matrix cores); a precision change, so reported apart
@@ -693,7 +727,8 @@ def main():
                        "head_ms": round(k8["head"], 4), "rows": R8,
                        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                                    "kernel": "quant_rows_e4m3_kernel + lmhead_ring_kernel<fp8 W, fp8 h>"}}
+                                    "kernel": "quant_rows_e4m3_kernel + lmhead_ring_kernel<fp8 W, fp8 h>"},
+                       "classify_roofline": classify_roofline(S, s8 * 1e3)}
     if not args.no_shard:
         # documents shard over GPUs with no collective: one GPU's share of the
         # 128-document long-document batch over 8 GPUs is 16 documents
