@@ -1360,9 +1360,23 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
       else stage(Even{}, std::true_type{}, 0);
       ++kc;
     }
-    for (int t = 1; t < nst; ++t, ++kc) {
-      if (kc & 1) stage(Odd{}, std::false_type{}, t);
-      else stage(Even{}, std::false_type{}, t);
+    // the rest in (even slot, odd slot) pairs, so that the loop body is straight-line
+    // code and the accumulators stay in the same registers from stage to stage (a
+    // branch on the parity at every stage made the compiler copy them out and back)
+    using F = std::false_type;
+    int t = 1;
+    if (t < nst && (kc & 1)) {
+      stage(Odd{}, F{}, t);
+      ++t;
+      ++kc;
+    }
+    for (; t + 1 < nst; t += 2, kc += 2) {
+      stage(Even{}, F{}, t);
+      stage(Odd{}, F{}, t + 1);
+    }
+    if (t < nst) {
+      stage(Even{}, F{}, t);
+      ++kc;
     }
     // normalise; lane writes hd blk*32 + 8 e4 + 4 c + 0..3
     lsum += __shfl_xor(lsum, 32, 64);
