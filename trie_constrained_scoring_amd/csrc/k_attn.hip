@@ -1286,14 +1286,29 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
       // the two key blocks' products alternate, so consecutive matrix ops do not
-      // depend on each other
+      // depend on each other; K fragments are read four matrix ops ahead, so their
+      // LDS latency is not waited out one fragment at a time
+      {
+        constexpr int NF = 2 * KSTEPS, AHEAD = 4;
+        auto kfrag = [&](int i) __attribute__((always_inline)) {
+          return *reinterpret_cast<const bf16x8*>(sl + (i & 1) * 32 * ROW + ko[i >> 1]);
+        };
+        bf16x8 kq[AHEAD];
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
+        for (int i = 0; i < AHEAD; ++i) kq[i] = kfrag(i);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + kb * 32 * ROW + ko[ks]);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
+        for (int i = 0; i < NF; ++i) {
+          sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i % AHEAD], qf[i >> 1], sc[i & 1], 0, 0, 0);
+          if (i + AHEAD < NF) kq[i % AHEAD] = kfrag(i + AHEAD);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < NF - AHEAD; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);  // MFMA
+      }
       __builtin_amdgcn_s_setprio(0);
       // online softmax (base 2) over the 64 keys; only a document's last stage has
       // keys past its end, which are masked (the empty asm keeps this a branch
