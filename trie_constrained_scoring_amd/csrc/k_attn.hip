@@ -1088,10 +1088,12 @@ __global__ __launch_bounds__(256, 2) void doc_attn_rows_kernel(
 // like the key-streaming kernel), shared by the four waves; the ring runs on
 // across documents.  Per stage each wave computes S^T = K Q^T for two 32-key
 // blocks, one online-softmax update, and O^T += V^T P^T with V^T from transposing
-// LDS reads and P split into bf16 high and low parts.  At a document's end each
-// lane merges its row with the row's path partial and writes its half of the row
-// straight from the accumulators, so the ring keeps loading meanwhile.  Two
-// workgroups fit on a CU (64 KB of LDS each).
+// LDS reads and P split into bf16 high and low parts.  Each row's softmax state
+// starts from its path partial at the document's first stage; at the document's
+// end each lane normalises its half of the row and writes it straight from the
+// accumulators, so the ring keeps loading meanwhile.  Two workgroups fit on a CU
+// (64 KB of LDS each), and each wave raises its priority over its matrix ops, so
+// the SIMD's other wave (of the other workgroup) runs its softmax under them.
 constexpr int ROWS_DMA_MAX_DPW = 64;  // documents per workgroup of the kernel below, at most
 __global__ __launch_bounds__(256, 2) void doc_attn_rows_dma_kernel(
     int B, int dpw, int n_int, int Hq, int Hkv, const uint16_t* __restrict__ Qn,
