@@ -460,12 +460,19 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   constexpr int ROW = HD * 2;            // bytes per key row
   constexpr int OPB = KB * ROW;          // bytes per operand per stage (8 KB)
   constexpr int NLD = OPB / 1024;        // 1 KB loads per operand per stage
-  constexpr int WAVE_BYTES = NS * 2 * OPB;
   constexpr int NBLK = HD / 32, KSTEPS = HD / 16;
-  constexpr int OUT_LD = HD + 1;
-  constexpr int EPI_BYTES = 4 * 32 * OUT_LD * 4 + 4 * 32 * 2 * 4;
-  constexpr int LDS_BYTES = 4 * WAVE_BYTES > EPI_BYTES ? 4 * WAVE_BYTES : EPI_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  // K and V stages live in two distinct arrays, so the compiler can tell that a
+  // buffer-to-LDS load into one does not write what is being read from the other
+  // (with one array it waits for every such load before the next LDS read).  The
+  // merge at the end reuses them: hd 0..63 of the 4 x 32 rows in the K array and hd
+  // 64..127 in the V array ([4][32][65] fp32 each), then each (wave, row)'s max
+  // and sum after them.
+  constexpr int HALF = HD / 2, OUT_LD2 = HALF + 1;
+  constexpr int EPI_HALF = 4 * 32 * OUT_LD2 * 4, SML_BYTES = 4 * 32 * 4;
+  constexpr int OPS_BYTES = 4 * NS * OPB;
+  constexpr int ARR_BYTES = OPS_BYTES > EPI_HALF + SML_BYTES ? OPS_BYTES : EPI_HALF + SML_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t sk_arr[ARR_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sv_arr[ARR_BYTES];
 
   const int G = Hq / Hkv;
   const int rows_total = n_int * G;
@@ -493,13 +500,16 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   const int doc0 = doc_offsets[doc];
   const int L = doc_offsets[doc + 1] - doc0;
   const int RS = Hkv * HD * 2;           // bytes between consecutive keys of one head
-  uint8_t* const ring = lds + wave * WAVE_BYTES;
+  uint8_t* const kring = sk_arr + wave * NS * OPB;  // this wave's K slots
+  uint8_t* const vring = sv_arr + wave * NS * OPB;  // and V slots
 
   // this wave's slots start as zeros, so a key past the document end that no load
   // writes still holds finite values (its weight is 0)
 #pragma unroll
-  for (int i = 0; i < WAVE_BYTES / (64 * 16); ++i)
-    *reinterpret_cast<uint4*>(ring + (i * 64 + lane) * 16) = uint4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < NS * OPB / (64 * 16); ++i) {
+    *reinterpret_cast<uint4*>(kring + (i * 64 + lane) * 16) = uint4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(vring + (i * 64 + lane) * 16) = uint4{0u, 0u, 0u, 0u};
+  }
 
   // Q^T fragments: lane holds row l%32, hd 16 ks + 8 (l/32) ..
   bf16x8 qf[KSTEPS];
@@ -527,13 +537,17 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   const uint16_t* const vbase = Vd + ((size_t)doc0 * Hkv + g) * HD;
   // Stage t into slot s: one buffer resource per stage over its valid keys, so keys
   // past the document end fall outside the range and read nothing.
-  auto issue = [&](int t, int s) __attribute__((always_inline)) {
+  // (operand 0: K, 1: V)
+  auto issue_op = [&](int t, int s, int op) __attribute__((always_inline)) {
     const int nkeys = min(KB, L - t * KB);
     const int bytes = (nkeys - 1) * RS + ROW;
     const size_t off = (size_t)t * KB * Hkv * HD;
-    uint8_t* sk = ring + s * 2 * OPB;
-    kv_issue<NLD>(kbase + off, bytes, sk, vo);
-    kv_issue<NLD>(vbase + off, bytes, sk + OPB, vo);
+    if (op) kv_issue<NLD>(vbase + off, bytes, vring + s * OPB, vo);
+    else kv_issue<NLD>(kbase + off, bytes, kring + s * OPB, vo);
+  };
+  auto issue = [&](int t, int s) __attribute__((always_inline)) {
+    issue_op(t, s, 0);
+    issue_op(t, s, 1);
   };
 
   // fragment offsets inside a slot
@@ -555,7 +569,7 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk) {
           const int chunk = 4 * blk + 2 * hsel + ((s & 3) >> 1);
-          vof[st][q][blk] = OPB + key * ROW + ((chunk ^ kv_swz(key & 15)) << 4) + 8 * (s & 1);
+          vof[st][q][blk] = key * ROW + ((chunk ^ kv_swz(key & 15)) << 4) + 8 * (s & 1);
         }
       }
   }
@@ -568,7 +582,9 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
   float m = -INFINITY, lsum = 0.f;  // base-2 running max; this lane's share of the sum
   const float qk = scale * LOG2E;
 
-  auto compute = [&](const uint8_t* sl, int t) __attribute__((always_inline)) {
+  // after_s runs once the stage's K fragments have all been read (the one-slot
+  // loop refills the K half there)
+  auto compute = [&](const uint8_t* sl, const uint8_t* vl, int t, auto&& after_s) __attribute__((always_inline)) {
     f32x16 sc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sc[e] = 0.f;
@@ -577,6 +593,7 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + ko[ks]);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
     }
+    after_s();
     // online softmax (base 2); only the document's last stage has keys past its
     // end, which are masked (the empty asm keeps this a branch)
     if (t * KB + KB > L) {
@@ -617,7 +634,7 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 vf = lds_read_tr_x2(sl + vof[st][0][blk], sl + vof[st][1][blk]);
+        const bf16x8 vf = lds_read_tr_x2(vl + vof[st][0][blk], vl + vof[st][1][blk]);
         acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[st], acc[blk], 0, 0, 0);
         acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[st], acc[blk], 0, 0, 0);
       }
@@ -633,41 +650,56 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     for (int i = 0; i < cnt; ++i) {
       if (i + 1 < cnt) wait_vmcnt<2 * NLD>(); else wait_vmcnt<0>();
       __builtin_amdgcn_sched_barrier(0);
-      compute(ring + (i & 1) * 2 * OPB, vw + NW * i);
+      compute(kring + (i & 1) * OPB, vring + (i & 1) * OPB, vw + NW * i, [] {});
       if (i + 2 < cnt) {
         wait_lgkmcnt0();  // this slot's reads are done before it is refilled
         __builtin_amdgcn_sched_barrier(0);
         issue(vw + NW * (i + 2), i & 1);
       }
     }
-  } else {  // one slot: the other workgroup on the CU covers each wave's load wait
+  } else {
+    // one slot: the other workgroup on the CU covers each wave's load wait.  The
+    // next stage's K goes into the slot as soon as this stage's scores have read
+    // it, so it is in flight during the softmax and PV; its V once PV is done.
+    if (cnt > 0) issue(vw, 0);
     for (int i = 0; i < cnt; ++i) {
-      issue(vw + NW * i, 0);
+      const bool more = i + 1 < cnt;
+      const int tn = vw + NW * (i + 1);
       wait_vmcnt<0>();
       __builtin_amdgcn_sched_barrier(0);
-      compute(ring, vw + NW * i);
-      wait_lgkmcnt0();  // the slot's reads are done before it is refilled
+      compute(kring, vring, vw + NW * i, [&]() __attribute__((always_inline)) {
+        if (more) {
+          wait_lgkmcnt0();  // K's reads are done before it is refilled
+          __builtin_amdgcn_sched_barrier(0);
+          issue_op(tn, 0, 0);
+        }
+      });
+      wait_lgkmcnt0();  // V's reads are done before it is refilled
       __builtin_amdgcn_sched_barrier(0);
+      if (more) issue_op(tn, 0, 1);
     }
   }
   __syncthreads();
 
   // merge the four key slices of each row and the row's path partial
-  float* so = reinterpret_cast<float*>(lds);          // [4][32][HD+1]
-  float* sml = so + 4 * 32 * OUT_LD;                  // [4][32][2]
+  float* const so_lo = reinterpret_cast<float*>(sk_arr);  // [4][32][65]: hd 0..63
+  float* const so_hi = reinterpret_cast<float*>(sv_arr);  // hd 64..127
+  float* const sm = reinterpret_cast<float*>(sk_arr + EPI_HALF);  // [4][32] max
+  float* const ss = reinterpret_cast<float*>(sv_arr + EPI_HALF);  // [4][32] sum
   lsum += __shfl_xor(lsum, 32, 64);
   {
-    float* base = so + (size_t)wave * 32 * OUT_LD;
+    const int wr = (wave * 32 + kr) * OUT_LD2;
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int hd = blk * 32 + 8 * (e >> 2) + 4 * c + (e & 3);
-        base[kr * OUT_LD + hd] = acc[blk][e];
+        if (blk < NBLK / 2) so_lo[wr + hd] = acc[blk][e];
+        else so_hi[wr + hd - HALF] = acc[blk][e];
       }
     if (lane < 32) {
-      sml[(wave * 32 + kr) * 2 + 0] = m;
-      sml[(wave * 32 + kr) * 2 + 1] = lsum;
+      sm[wave * 32 + kr] = m;
+      ss[wave * 32 + kr] = lsum;
     }
   }
   __syncthreads();
@@ -676,18 +708,20 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
     // issued before any is used
     constexpr int SEG = HD / 8;
     const int row = tid >> 3, h0 = (tid & 7) * SEG;
+    // this thread's 16 hd of the merge tile
+    const float* const so = (h0 < HALF ? so_lo : so_hi) + (h0 < HALF ? h0 : h0 - HALF);
     const int j = j0 + row;
     if (j < rows_total) {
       const int r = j / G, h = g * G + j % G;
       if (S > 1) {  // this workgroup's share of the keys: (max, sum, unnormalised output)
         float M = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) M = fmaxf(M, sml[(k * 32 + row) * 2]);
+        for (int k = 0; k < 4; ++k) M = fmaxf(M, sm[k * 32 + row]);
         float f[4], Ls = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          f[k] = M == -INFINITY ? 0.f : exp2f(sml[(k * 32 + row) * 2] - M);
-          Ls += f[k] * sml[(k * 32 + row) * 2 + 1];
+          f[k] = M == -INFINITY ? 0.f : exp2f(sm[k * 32 + row] - M);
+          Ls += f[k] * ss[k * 32 + row];
         }
         const size_t pi = (size_t)z * Bn * n_int * Hq + ((size_t)b * n_int + r) * Hq + h;
         if ((tid & 7) == 0) pml[pi] = float2{M, Ls};
@@ -699,7 +733,7 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
           for (int e = 0; e < 4; ++e) {
             w[e] = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) w[e] += f[k] * so[((size_t)k * 32 + row) * OUT_LD + h0 + 4 * i + e];
+            for (int k = 0; k < 4; ++k) w[e] += f[k] * so[(k * 32 + row) * OUT_LD2 + 4 * i + e];
           }
           pp[i] = float4{w[0], w[1], w[2], w[3]};
         }
@@ -712,12 +746,12 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
       const float2 a = anc_ml[(size_t)(rq + r) * Hq + h];
       float M = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) M = fmaxf(M, sml[(k * 32 + row) * 2]);
+      for (int k = 0; k < 4; ++k) M = fmaxf(M, sm[k * 32 + row]);
       float f[4], Ls = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        f[k] = M == -INFINITY ? 0.f : exp2f(sml[(k * 32 + row) * 2] - M);
-        Ls += f[k] * sml[(k * 32 + row) * 2 + 1];
+        f[k] = M == -INFINITY ? 0.f : exp2f(sm[k * 32 + row] - M);
+        Ls += f[k] * ss[k * 32 + row];
       }
       const float ma = a.x * LOG2E;
       const float Mt = fmaxf(M, ma);
@@ -729,7 +763,7 @@ __global__ __launch_bounds__(256, 3 - NS) void doc_attn_stream_kernel(
       for (int e = 0; e < SEG; ++e) {
         float Os = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) Os += f[k] * so[((size_t)k * 32 + row) * OUT_LD + h0 + e];
+        for (int k = 0; k < 4; ++k) Os += f[k] * so[(k * 32 + row) * OUT_LD2 + e];
         const float an = (&av[e / 4].x)[e % 4];
         v[e] = (Os * fd + an * fa) * inv;
       }
