@@ -385,7 +385,8 @@ __global__ __launch_bounds__(256) void doc_attn_mfma_kernel(
 // buffer-to-LDS loads, so the key loop has no workgroup barrier.  With NS = 1 two
 // workgroups share a CU and each covers the other's load waits (measured on MI355X:
 // 12% faster than NS = 2 with one workgroup per CU on 512-key documents, equal on
-// 4096-key ones).
+// 4096-key ones); the next stage's K is loaded as soon as the scores have read the
+// current one, so it is in flight during the softmax and PV.
 //
 // K and V stay in their natural [key][hd] layout.  In a slot, the 16-byte chunk c
 // of key row r sits at position c ^ kv_swz(r mod 16), which puts both the K
