@@ -19,6 +19,7 @@ namespace tcs {
 constexpr int HEAD_BN = 256;   // vocabulary entries per tile
 constexpr int HEAD_SEG = 128;  // vocabulary entries per edge segment (and bf16 partial)
 constexpr int HEAD_WGS = 256;  // persistent bf16 head: one workgroup per CU
+constexpr int HEAD_LIST_ROWS = 64;  // rows per gather list (per vocabulary half-tile)
 // below this many rows the matrix-core head stores its (max, sum) partials row-major
 constexpr int LSE_ROWMAJOR_MAX_ROWS = 4096;
 
@@ -45,14 +46,16 @@ __global__ void head_prep_kernel(int n_seg, const int32_t* __restrict__ e_tok, i
 // Gather lists of the bf16 head.  The logit of child c of query row q in document
 // b sits in tile (vocabulary half-tile tok/128, row tile r/256), r = b n_int + q,
 // in accumulator element t = 16 im + e of the lane whose half is hh and whose row
-// is r % 256.  Each (edge, document) pair is pushed on its tile half's list:
-// rec = {next, output index b*n_nodes + c, t | hh << 6 | (r % 256) << 7, 0}.
+// is r % 256.  Each (edge, document) pair is pushed on the list of its vocabulary
+// half-tile and 64-row block (the rows one wave of a 256-row tile holds), so a
+// wave walks only its own rows' records: rec = {next, output index b*n_nodes + c,
+// t | hh << 6 | (r % 256) << 7, 0}.
 __global__ void head_list_init_kernel(int n_keys, int32_t* __restrict__ list_head) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t < n_keys) list_head[t] = -1;
 }
 
-__global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
+__global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rb,
                                       const int32_t* __restrict__ e_tok,
                                       const int32_t* __restrict__ e_qrow,
                                       const int32_t* __restrict__ e_child, int n_edges,
@@ -65,7 +68,7 @@ __global__ void head_list_link_kernel(int B, int n_int, int n_nodes, int n_rt,
   const int off = tok & (HEAD_SEG - 1);  // 32 im + 8 (e>>2) + 4 hh + (e&3)
   const int t = (off >> 5) * 16 + (((off >> 3) & 3) << 2) + (off & 3);
   const int hh = (off >> 2) & 1;
-  const int key = (tok / HEAD_SEG) * n_rt + r / 256;
+  const int key = (tok / HEAD_SEG) * n_rb + r / HEAD_LIST_ROWS;
   const int next = atomicExch(&list_head[key], int(i));
   rec[i] = int4{next, b * n_nodes + e_child[e], t | (hh << 6) | ((r & 255) << 7), 0};
 }
@@ -282,7 +285,7 @@ __device__ __forceinline__ void ring_body(
   constexpr int HRB = A8 ? 1 : 2;  // bytes per hidden-state element
   constexpr int JN = TR / 128;  // 32-row blocks per wave
   const int n_rt = (R + TR - 1) / TR, n_vt = (V + HEAD_BN - 1) / HEAD_BN;
-  const int n_rt256 = (R + 255) / 256;  // row tiles of the gather lists
+  const int n_rbl = (R + HEAD_LIST_ROWS - 1) / HEAD_LIST_ROWS;  // row blocks of the gather lists
   // workgroup g takes rounds [w_lo, rounds) of slot g % 256: a bounded run of
   // consecutive rounds, so the workgroups that share operand tiles in an XCD's L2
   // stay within a few rounds of each other
@@ -670,9 +673,13 @@ __device__ __forceinline__ void ring_body(
     // entries at or past V (last vocabulary tile) drop out of the row sums; the
     // accumulators are only read from here on
     const int vlim = V - v0 - vhalf;  // entry (im, e) is valid iff 32 im + 8 (e>>2) + (e&3) < vlim
-    // child-token gather: walk this half-tile's list for this row tile (scalar)
-    // (the lists are per 256-row tile: rit is the row within it)
-    for (int k = list_head[(2 * vt + wm) * n_rt256 + (TR == 128 ? rt >> 1 : rt)]; k >= 0;) {
+    // child-token gather: walk the list of this half-tile and this wave's 64-row block
+    // (scalar; rit is the row within the 256-row tile).  The wave's rows are block
+    // 4 rt + wr of a 256-row tile; rows 32 wr .. of a 128-row tile fall in block
+    // 2 rt + wr / 2, whose other half the filter below skips.  A block past the
+    // last row has no list.
+    const int lblk = TR == 128 ? 2 * rt + (wr >> 1) : 4 * rt + wr;
+    for (int k = lblk < n_rbl ? list_head[(2 * vt + wm) * n_rbl + lblk] : -1; k >= 0;) {
       const int4 q = rec[k];
       const int t = q.z & 63, hh = (q.z >> 6) & 1, rit = q.z >> 7;
       // row r0 + (rit mod TR) is in this wave's share of the tile's rows
@@ -915,11 +922,11 @@ static HeadPrep head_prep_layout(Carve& cv, tcs_dtype h_dtype, int32_t B, int32_
   const size_t R = size_t(B) * n_int;
   const size_t n_tiles = size_t(lmhead_n_tiles(h_dtype, V));
   const bool mfma_head = h_dtype == TCS_BF16;
-  const size_t n_rt = (R + 255) / 256;
+  const size_t n_rbl = (R + HEAD_LIST_ROWS - 1) / HEAD_LIST_ROWS;
   HeadPrep P;
   P.seg = cv.take<int32_t>(2 * n_tiles + 1);
   P.zero = cv.take<uint4>(mfma_head ? head_zero_bytes(d) / 16 : 0);
-  P.list_head = cv.take<int32_t>(mfma_head ? 2 * n_tiles * n_rt : 0);
+  P.list_head = cv.take<int32_t>(mfma_head ? 2 * n_tiles * n_rbl : 0);
   P.rec = cv.take<int4>(mfma_head ? size_t(n_nodes - 1) * B : 0);
   return P;
 }
@@ -979,8 +986,8 @@ int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int
   const HeadPrep P = head_prep_layout(cv, h_dtype, B, n_int, n_nodes, d, V);
   const bool mfma_head = h_dtype == TCS_BF16;
   const size_t zbytes = mfma_head ? head_zero_bytes(d) : 0;
-  const int n_rt = (R + 255) / 256;
-  const int n_keys = mfma_head ? 2 * n_tiles * n_rt : 0;
+  const int n_rbl = (R + HEAD_LIST_ROWS - 1) / HEAD_LIST_ROWS;
+  const int n_keys = mfma_head ? 2 * n_tiles * n_rbl : 0;
   const long n_pairs = mfma_head ? long(n_edges) * B : 0;
   const int n_prep = max(2 * n_tiles + 1, int(zbytes / 16));
   head_prep_kernel<<<(n_prep + 255) / 256, 256, 0, s>>>(2 * n_tiles, e_tok, n_edges, P.seg, P.zero,
@@ -989,7 +996,7 @@ int launch_lmhead_prep(void* stream, tcs_dtype h_dtype, int32_t B, int32_t n_int
     head_list_init_kernel<<<(n_keys + 255) / 256, 256, 0, s>>>(n_keys, P.list_head);
     if (n_pairs > 0)
       head_list_link_kernel<<<int((n_pairs + 255) / 256), 256, 0, s>>>(
-          B, n_int, n_nodes, n_rt, e_tok, e_qrow, e_child, n_edges, P.list_head, P.rec);
+          B, n_int, n_nodes, n_rbl, e_tok, e_qrow, e_child, n_edges, P.list_head, P.rec);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "lmhead prep: %s", hipGetErrorString(e));
