@@ -61,6 +61,10 @@ PATH_CASES = {
     "zipf255": ("cfg", 3),
     "zipf5000": ("cfg", 4),
     "prefix": ("labels", [[3], [3, 4], [3, 4, 5], [3, 6], [9, 9, 9], [9, 9], [1]]),
+    # depth 12 with prefix labels: the walk with the parent arrays staged in LDS
+    "prefix-deep": ("labels", [[5, 1, 2, 3, 4, 5, 6, 7, 8], [5, 1, 2, 3, 4, 5, 6, 7],
+                               [5, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11], [5, 1, 2, 3, 9], [2],
+                               [3] * 10, [3] * 12, [3] * 11 + [4]]),
     "single": ("labels", [[4, 2, 7]]),
 }
 

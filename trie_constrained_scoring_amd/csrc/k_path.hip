@@ -26,10 +26,34 @@ __global__ void node_qrow_kernel(int n_edges, const int32_t* __restrict__ e_chil
   if (e < n_edges) node_qrow[e_child[e]] = e_qrow[e];
 }
 
+// Entry i of an fp32 array of n entries, 0 when i is outside [0, n) (the buffer
+// unit drops the load), with no branch around it.
+__device__ __forceinline__ float gather_load(const float* base, int n, int i) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, n * 4, 0x00020000);
+  const uint32_t off = uint32_t(i) < uint32_t(n) ? uint32_t(i) * 4u : 0x80000000u;
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+__device__ __forceinline__ int gather_load_i32(const int32_t* base, int n, int i) {
+  return int(__float_as_uint(gather_load(reinterpret_cast<const float*>(base), n, i)));
+}
+
+// Deep tries (depth >= PATH_STAGE_DEPTH, up to PATH_STAGE_NODES nodes) take the
+// staged walk below; shallow ones walk the global arrays directly.
+constexpr int PATH_STAGE_DEPTH = 8;
+constexpr int PATH_STAGE_NODES = 8192;  // 4 bytes of LDS each
+constexpr int PATH_WALK_BATCH = 8;      // path nodes whose log-probs are requested together
+
 // One workgroup per document; each thread walks the paths of its labels from the
-// label node up to the root (depths are small), accumulating in fp64.  With `lse`
-// set, lp holds the raw child logits and the edge log-prob of node v is
-// lp[v] - lse[b n_int + node_qrow[v]] (the head's finalisation folded in).
+// label node up to the root, accumulating in fp64.  With `lse` set, lp holds the
+// raw child logits and the edge log-prob of node v is lp[v] - lse[b n_int +
+// node_qrow[v]] (the head's finalisation folded in).
+// STAGED: the parent and parent-row arrays are first copied to LDS (uint16), so
+// the chain of parent reads runs in LDS, and the log-probs of PATH_WALK_BATCH path
+// nodes at a time are requested together: a depth-40 path costs five rounds of
+// global loads instead of forty dependent ones.  The sum runs in the same order
+// either way, so both forms give the same bits.
+template <bool STAGED>
 __global__ __launch_bounds__(256) void path_sum_kernel(
     int n_nodes, int M, const float* __restrict__ lp, const float* __restrict__ lse,
     const int32_t* __restrict__ node_qrow, int n_int, const int32_t* __restrict__ parent,
@@ -39,6 +63,7 @@ __global__ __launch_bounds__(256) void path_sum_kernel(
   __shared__ double rv[4];
   __shared__ int ri[4];
   __shared__ double rs[4];
+  extern __shared__ uint16_t walk_lds[];  // STAGED: parent [n_nodes] | parent's row [n_nodes]
   const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float* lpb = lp + (size_t)b * n_nodes;
   const float* lseb = lse ? lse + (size_t)b * n_int : nullptr;
@@ -46,13 +71,72 @@ __global__ __launch_bounds__(256) void path_sum_kernel(
     const double x = double(lpb[v]);
     return lseb ? x - double(lseb[node_qrow[v]]) : x;
   };
+  uint16_t* const spn = walk_lds;
+  uint16_t* const sqr = walk_lds + n_nodes;
+  if constexpr (STAGED) {
+    constexpr int CH = 8;  // loads in flight per thread and array
+    for (int v0 = 0; v0 < n_nodes; v0 += CH * 256) {
+      int pv[CH], qv[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) pv[i] = gather_load_i32(parent, n_nodes, v0 + t + 256 * i);
+      if (lseb) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) qv[i] = gather_load_i32(node_qrow, n_nodes, v0 + t + 256 * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) qv[i] = 0;
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int v = v0 + t + 256 * i;
+        if (v < n_nodes) {
+          spn[v] = uint16_t(v == 0 ? 0 : pv[i]);
+          sqr[v] = uint16_t(v == 0 ? 0 : qv[i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
   float* llb = ll + (size_t)b * M;
   double best = -HUGE_VAL;
   int best_i = INT_MAX;
   for (int m = t; m < M; m += 256) {
     const int u = label_node[m];
     double acc = 0.0;
-    for (int v = u, steps = 0; v > 0 && steps < u; v = parent[v], ++steps) acc += edge_lp(v);
+    if constexpr (STAGED) {
+      int v = u, steps = 0;
+      while (v > 0 && steps < u) {
+        // the next nodes of the path and their parents' rows (-1 past the root)
+        int vs[PATH_WALK_BATCH], qs[PATH_WALK_BATCH];
+#pragma unroll
+        for (int i = 0; i < PATH_WALK_BATCH; ++i) {
+          const bool on = v > 0 && steps < u;
+          vs[i] = on ? v : -1;
+          qs[i] = -1;
+          if (on) {
+            qs[i] = sqr[v];
+            v = spn[v];
+            ++steps;
+          }
+        }
+        float x[PATH_WALK_BATCH], ls[PATH_WALK_BATCH];
+#pragma unroll
+        for (int i = 0; i < PATH_WALK_BATCH; ++i) x[i] = gather_load(lpb, n_nodes, vs[i]);
+        if (lseb) {
+#pragma unroll
+          for (int i = 0; i < PATH_WALK_BATCH; ++i) ls[i] = gather_load(lseb, n_int, qs[i]);
+#pragma unroll
+          for (int i = 0; i < PATH_WALK_BATCH; ++i)
+            if (vs[i] >= 0) acc += double(x[i]) - double(ls[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < PATH_WALK_BATCH; ++i)
+            if (vs[i] >= 0) acc += double(x[i]);
+        }
+      }
+    } else {
+      for (int v = u, steps = 0; v > 0 && steps < u; v = parent[v], ++steps) acc += edge_lp(v);
+    }
     const int cc = child_count[u];
     if (cc > 0) {
       const int cb = child_begin[u];
@@ -125,9 +209,12 @@ constexpr int PATH_KREG = 48;         // lp entries per thread held in registers
 constexpr int PATH_LREG = 16;         // labels per thread (so at most 8192 labels)
 constexpr int PATH_MAX_ROWS = 19968;  // 8 bytes each
 constexpr int PATH_MAX_LEVELS = 256;
-// Up to this many labels the per-label walk is faster (measured on MI355X: 10
-// labels 7 us vs 20 us, 255 labels 22 us vs 36 us per launch; 5,000 labels 151 us
-// vs 50 us): it has no level barriers, and each thread walks about one label.
+constexpr int PATH_PCH = 16;          // parent-row loads in flight per thread (LDS set-up)
+// Up to this many labels the per-label walk is faster (measured on MI355X per
+// launch, walk vs levels: 10 labels 7 vs 20 us, 255 labels 22 vs 36 us, 5,000
+// labels 151 vs 50 us; since then the staged walk takes 13 us at 255 labels and
+// the batched parent-row loads bring the levels kernel to 41 us at 5,000): it has
+// no level barriers, and each thread walks about one label.
 constexpr int PATH_WALK_MAX_LABELS = 512;
 
 // A sum held as an unevaluated pair hi + lo of fp32 values (lo stored as bf16),
@@ -161,15 +248,6 @@ __device__ __forceinline__ uint32_t row_load(const void* base, int n, int t, int
   return __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, k * PATH_THREADS * 4, 0);
 }
 
-// Entry i of an fp32 array of n entries, 0 when i is outside [0, n) (the buffer
-// unit drops the load), with no branch around it.
-__device__ __forceinline__ float gather_load(const float* base, int n, int i) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, n * 4, 0x00020000);
-  const uint32_t off = uint32_t(i) < uint32_t(n) ? uint32_t(i) * 4u : 0x80000000u;
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-}
-
 // LDS writes before, LDS reads after; outstanding global loads stay in flight
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -193,7 +271,19 @@ __global__ __launch_bounds__(PATH_THREADS) void path_levels_kernel(
   __shared__ double rs[PATH_THREADS / 64];
   __shared__ int ri[PATH_THREADS / 64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int r = t; r < n_int; r += PATH_THREADS) spar[r] = uint16_t(r == 0 ? 0 : qparent[r]);
+  // parent rows into LDS, PATH_PCH loads in flight per thread before their writes
+  // (one load and one write per row in a loop waits for every load in turn: ~40
+  // load latencies on a 17k-row trie)
+  for (int r0 = 0; r0 < n_int; r0 += PATH_PCH * PATH_THREADS) {
+    int pv[PATH_PCH];
+#pragma unroll
+    for (int i = 0; i < PATH_PCH; ++i) pv[i] = gather_load_i32(qparent, n_int, r0 + t + i * PATH_THREADS);
+#pragma unroll
+    for (int i = 0; i < PATH_PCH; ++i) {
+      const int r = r0 + t + i * PATH_THREADS;
+      if (r < n_int) spar[r] = uint16_t(r == 0 ? 0 : pv[i]);
+    }
+  }
   for (int d = t; d < max_depth + 2; d += PATH_THREADS) slev[d] = row_level_offsets[d];
   // what every document needs from the trie, in registers: the rows of this
   // thread's nodes t + 512 k (0 past the end), and for its labels t + 512 j the
@@ -449,9 +539,14 @@ int launch_path_sum(void* stream, int32_t B, const tcs_trie_dev* trie, const flo
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (trie->n_labels > PATH_WALK_MAX_LABELS && path_levels_ok(trie))
     return launch_path_levels(s, B, trie, lp, ll, prob, label, lse);
-  path_sum_kernel<<<B, 256, 0, s>>>(trie->n_nodes, trie->n_labels, lp, lse, node_qrow, trie->n_int,
-                                    trie->parent, trie->child_begin, trie->child_count,
-                                    trie->label_node, ll, prob, label);
+  if (trie->max_depth >= PATH_STAGE_DEPTH && trie->n_nodes <= PATH_STAGE_NODES)
+    path_sum_kernel<true><<<B, 256, size_t(trie->n_nodes) * 4, s>>>(
+        trie->n_nodes, trie->n_labels, lp, lse, node_qrow, trie->n_int, trie->parent,
+        trie->child_begin, trie->child_count, trie->label_node, ll, prob, label);
+  else
+    path_sum_kernel<false><<<B, 256, 0, s>>>(trie->n_nodes, trie->n_labels, lp, lse, node_qrow,
+                                             trie->n_int, trie->parent, trie->child_begin,
+                                             trie->child_count, trie->label_node, ll, prob, label);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TCS_EHIP, "path_sum: %s", hipGetErrorString(e));
   return TCS_OK;
