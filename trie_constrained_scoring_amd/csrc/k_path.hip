@@ -209,11 +209,11 @@ constexpr int PATH_KREG = 48;         // lp entries per thread held in registers
 constexpr int PATH_LREG = 16;         // labels per thread (so at most 8192 labels)
 constexpr int PATH_MAX_ROWS = 19968;  // 8 bytes each
 constexpr int PATH_MAX_LEVELS = 256;
-constexpr int PATH_PCH = 16;          // parent-row loads in flight per thread (LDS set-up)
+constexpr int PATH_PROWS = (PATH_MAX_ROWS + PATH_THREADS - 1) / PATH_THREADS;  // parent rows per thread
 // Up to this many labels the per-label walk is faster (measured on MI355X per
 // launch, walk vs levels: 10 labels 7 vs 20 us, 255 labels 22 vs 36 us, 5,000
 // labels 151 vs 50 us; since then the staged walk takes 13 us at 255 labels and
-// the batched parent-row loads bring the levels kernel to 41 us at 5,000): it has
+// the batched set-up loads bring the levels kernel to 35 us at 5,000): it has
 // no level barriers, and each thread walks about one label.
 constexpr int PATH_WALK_MAX_LABELS = 512;
 
@@ -271,37 +271,44 @@ __global__ __launch_bounds__(PATH_THREADS) void path_levels_kernel(
   __shared__ double rs[PATH_THREADS / 64];
   __shared__ int ri[PATH_THREADS / 64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // parent rows into LDS, PATH_PCH loads in flight per thread before their writes
-  // (one load and one write per row in a loop waits for every load in turn: ~40
-  // load latencies on a 17k-row trie)
-  for (int r0 = 0; r0 < n_int; r0 += PATH_PCH * PATH_THREADS) {
-    int pv[PATH_PCH];
+  // Set-up.  Every load that does not depend on another is requested before any
+  // is used (a loop of one load and one LDS write per row waits for each load in
+  // turn): the parent rows (into LDS), the level offsets, this thread's node rows
+  // t + 512 k (0 past the end) and label nodes and rows t + 512 j; then, with the
+  // nodes, whether each label node is a leaf.  Node rows are packed two to a
+  // register (0xFFFF for a leaf), a label as node | row << 16 | leaf << 31 (nodes
+  // and rows are below 2^15 here).
+  int pv[PATH_PROWS];
 #pragma unroll
-    for (int i = 0; i < PATH_PCH; ++i) pv[i] = gather_load_i32(qparent, n_int, r0 + t + i * PATH_THREADS);
-#pragma unroll
-    for (int i = 0; i < PATH_PCH; ++i) {
-      const int r = r0 + t + i * PATH_THREADS;
-      if (r < n_int) spar[r] = uint16_t(r == 0 ? 0 : pv[i]);
-    }
-  }
-  for (int d = t; d < max_depth + 2; d += PATH_THREADS) slev[d] = row_level_offsets[d];
-  // what every document needs from the trie, in registers: the rows of this
-  // thread's nodes t + 512 k (0 past the end), and for its labels t + 512 j the
-  // label node, the row its score starts from, and whether the node is a leaf
-  // (packed: node rows two to a register, 0xFFFF for a leaf; label node | row << 16
-  // | leaf << 31 -- nodes and rows are below 2^15 here)
+  for (int i = 0; i < PATH_PROWS; ++i) pv[i] = gather_load_i32(qparent, n_int, t + i * PATH_THREADS);
+  const int lvo = gather_load_i32(row_level_offsets, max_depth + 2, t);
   uint32_t qr2[PATH_KREG / 2];
 #pragma unroll
   for (int k = 0; k < PATH_KREG; k += 2)
     qr2[k / 2] = (row_load(qrow, n_nodes, t, k) & 0xFFFFu) | (row_load(qrow, n_nodes, t, k + 1) << 16);
-  uint32_t lab[PATH_LREG];
+  int lnode[PATH_LREG], lrow[PATH_LREG];
 #pragma unroll
   for (int j = 0; j < PATH_LREG; ++j) {
-    const int m = t + PATH_THREADS * j;
-    const int u = m < M ? label_node[m] : 0;
-    const int r = m < M ? label_row[m] : 0;
-    const bool lf = m >= M || child_count[u] == 0;
-    lab[j] = uint32_t(u) | (uint32_t(r) << 16) | (lf ? 0x80000000u : 0u);
+    lnode[j] = gather_load_i32(label_node, M, t + PATH_THREADS * j);
+    lrow[j] = gather_load_i32(label_row, M, t + PATH_THREADS * j);
+  }
+#pragma unroll
+  for (int i = 0; i < PATH_PROWS; ++i) {
+    const int r = t + i * PATH_THREADS;
+    if (r < n_int) spar[r] = uint16_t(r == 0 ? 0 : pv[i]);
+  }
+  if (t < max_depth + 2) slev[t] = lvo;
+  uint32_t lab[PATH_LREG];
+  {
+    int cc[PATH_LREG];
+#pragma unroll
+    for (int j = 0; j < PATH_LREG; ++j)
+      cc[j] = gather_load_i32(child_count, n_nodes, t + PATH_THREADS * j < M ? lnode[j] : -1);
+#pragma unroll
+    for (int j = 0; j < PATH_LREG; ++j) {
+      const bool lf = t + PATH_THREADS * j >= M || cc[j] == 0;
+      lab[j] = uint32_t(lnode[j]) | (uint32_t(lrow[j]) << 16) | (lf ? 0x80000000u : 0u);
+    }
   }
   const bool any_internal = __syncthreads_or(int(
       [&] {
