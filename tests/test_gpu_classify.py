@@ -52,6 +52,11 @@ SMALL = {
                                 trie=("explicit", [[4, 2, 7]])),
     "deep-chain-bf16": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=128, B=3, L=30,
                               trie=("explicit", [list(range(100, 140)), [5], [100, 101, 7]])),
+    # 12 deep with a label that is a prefix of another: the per-label walk over parent
+    # arrays staged in LDS, with the head's log-sum-exp folded in and the prefix term
+    "deep-prefix-bf16": config(2, V=2000, d=128, Hq=4, Hkv=2, hd=128, B=4, L=30,
+                               trie=("explicit", [list(range(100, 112)), list(range(100, 110)), [5],
+                                                  [100, 101, 7]])),
     # few-row output projection on the K-split kernel: ragged row and column tiles,
     # 128- and 256-row tiles, even and uneven K splits (R = B x 8 internal nodes)
     "proj-split-bm128": config(2, V=2000, d=320, Hq=4, Hkv=2, hd=128, B=25, L=24),
